@@ -1,0 +1,149 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module holds no arithmetic of the method itself: only random draws and the
+input recipe (value distributions, shapes, seeds).  Both the GPU path and the CPU
+oracle consume what it returns, and it imports neither of them.
+
+Recipe (same for every workload):
+  * q, k ~ N(0, 1), then scaled to unit L2 norm per token and head (in fp32),
+    then cast to the io dtype (bf16 with round-to-nearest-even, or kept fp32);
+  * v ~ N(0, 1), cast to the io dtype;
+  * b = sigmoid(N(0, 1));  a = exp(-softplus(N(0, 1)) * 0.1)   (fp32, per value head);
+  * conv weights ~ 0.5 * N(0, 1);  conv inputs ~ N(0, 1);
+  * states entering decode / flush ~ 0.1 * N(0, 1) (fp32).
+Large tensors are drawn in token blocks, each block from its own generator seeded
+from (seed, block index), so any block can be re-drawn alone and memory stays bounded.
+
+Workload shapes (a "27B-shaped" layer is 48 value heads of 128 x 128 fp32 state; a
+"4B-shaped" layer is 32 heads), following "Prefix caching on Gated DeltaNet hybrids"
+("Why hits were wrong": 48 heads x 128 x 128 fp32, blocks of 896 tokens) and
+"Caching less to serve more requests" ("What we changed": 2 MiB of fp32 state per
+layer, a 32-slot input buffer, 16-row flush blocks).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+TOKEN_BLOCK = 8192
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seqlens: tuple
+    n_qk_heads: int
+    n_v_heads: int
+    head_dim: int
+    io_dtype: torch.dtype
+    block: int
+    seed: int
+
+    @property
+    def conv_channels(self) -> int:
+        return (2 * self.n_qk_heads + self.n_v_heads) * self.head_dim
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seqlens))
+
+
+# The parity / bench workloads.
+TINY = Workload("tiny_fp32_T64_H2_d16_block16", (64,), 2, 2, 16, torch.float32, 16, 1000)
+PREFILL_27B = Workload("prefill_27b_T8192_H48_d128_block896", (8192,), 48, 48, 128,
+                       torch.bfloat16, 896, 1001)
+VARLEN_27B = Workload("varlen_27b_4seq_block896", (2688, 5000, 6272, 12000), 48, 48, 128,
+                      torch.bfloat16, 896, 1002)
+LONG_27B = Workload("long_27b_T229376_H48_d128_block896", (229376,), 48, 48, 128,
+                    torch.bfloat16, 896, 1004)
+
+FLUSH_4B = dict(name="flush_4b_16req_H32_d128_32slots", n_req=16, n_heads=32, head_dim=128,
+                buf_rows=32, seed=1003)
+DECODE_27B = dict(name="decode_27b_256req_H48_d128", n_req=256, n_heads=48, head_dim=128,
+                  seed=1005)
+
+
+def _gen(seed: int, block_index: int = 0) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) * 1_000_003 + int(block_index))
+    return g
+
+
+def _unit_rows(x: torch.Tensor) -> torch.Tensor:
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def qkvab(T: int, n_qk: int, n_v: int, d: int, io_dtype=torch.bfloat16, seed: int = 0,
+          token_offset: int = 0, heads=None):
+    """Draw q, k [T, n_qk, d], v [T, n_v, d] (io dtype) and a, b [T, n_v] (fp32).
+
+    Tokens are drawn in blocks of TOKEN_BLOCK absolute token indices (token_offset is
+    the absolute index of the first token), so a slice of a long sequence can be drawn
+    without the rest.  `heads` optionally selects value heads (their query/key heads
+    follow) after drawing, for oracle checks on a subset of heads.
+    """
+    qs, ks, vs, as_, bs = [], [], [], [], []
+    t = token_offset
+    end = token_offset + T
+    while t < end:
+        blk = t // TOKEN_BLOCK
+        b0 = blk * TOKEN_BLOCK
+        lo, hi = t - b0, min(end, b0 + TOKEN_BLOCK) - b0
+        g = _gen(seed, blk)
+        n = TOKEN_BLOCK
+        q = torch.randn(n, n_qk, d, generator=g)[lo:hi]
+        k = torch.randn(n, n_qk, d, generator=g)[lo:hi]
+        v = torch.randn(n, n_v, d, generator=g)[lo:hi]
+        b = torch.sigmoid(torch.randn(n, n_v, generator=g))[lo:hi]
+        a = torch.exp(-torch.nn.functional.softplus(torch.randn(n, n_v, generator=g)) * 0.1)[lo:hi]
+        qs.append(_unit_rows(q).to(io_dtype))
+        ks.append(_unit_rows(k).to(io_dtype))
+        vs.append(v.to(io_dtype))
+        as_.append(a.contiguous())
+        bs.append(b.contiguous())
+        t = b0 + hi
+    q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
+    a, b = torch.cat(as_), torch.cat(bs)
+    if heads is not None:
+        group = n_v // n_qk
+        heads = list(heads)
+        qk_heads = sorted({h // group for h in heads})
+        q, k = q[:, qk_heads].contiguous(), k[:, qk_heads].contiguous()
+        v, a, b = v[:, heads].contiguous(), a[:, heads].contiguous(), b[:, heads].contiguous()
+    return q, k, v, a, b
+
+
+def conv_inputs(T: int, channels: int, width: int = 4, io_dtype=torch.bfloat16, seed: int = 0):
+    """Draw conv inputs x [T, C] and weights w [C, width] in the io dtype."""
+    g = _gen(seed, 10_000)
+    w = (0.5 * torch.randn(channels, width, generator=g)).to(io_dtype)
+    xs = []
+    for blk in range((T + TOKEN_BLOCK - 1) // TOKEN_BLOCK):
+        n = min(TOKEN_BLOCK, T - blk * TOKEN_BLOCK)
+        xs.append(torch.randn(n, channels, generator=_gen(seed, 20_000 + blk)).to(io_dtype))
+    x = torch.cat(xs) if xs else torch.zeros(0, channels, dtype=io_dtype)
+    return x, w
+
+
+def conv_tail(n: int, channels: int, width: int = 4, io_dtype=torch.bfloat16, seed: int = 0):
+    """Draw n conv tails [n, width - 1, C]."""
+    g = _gen(seed, 30_000)
+    return torch.randn(n, width - 1, channels, generator=g).to(io_dtype)
+
+
+def states(n: int, n_v: int, d: int, seed: int = 0, std: float = 0.1):
+    """Draw n fp32 states [n, n_v, d, d] ~ std * N(0, 1)."""
+    g = _gen(seed, 40_000)
+    return std * torch.randn(n, n_v, d, d, generator=g)
+
+
+def accepted_counts(n_req: int, seed: int, max_rows: int = 16):
+    """Accepted rows per request: uniform in 0..max_rows-1 plus the bonus token."""
+    g = _gen(seed, 50_000)
+    return torch.randint(0, max_rows, (n_req,), generator=g, dtype=torch.int32) + 1
+
+
+def permutation(n: int, seed: int):
+    g = _gen(seed, 60_000)
+    return torch.randperm(n, generator=g)
