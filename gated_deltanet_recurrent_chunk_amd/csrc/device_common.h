@@ -1,0 +1,140 @@
+// device_common.h -- gfx950 device helpers shared by the libgdn kernels.
+//
+// Matrix products run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16: 16x16 fp32
+// accumulator, contraction 32, one 64-lane wave).  The state and every intermediate
+// of the chunk transform are fp32; a product with an fp32 operand splits it into a sum
+// of bf16 terms (x = t0 + t1 [+ t2], each term the bf16 rounding of what the earlier
+// terms left) and accumulates the cross products whose combined order is small
+// enough.  With bf16 inputs: two terms, products of order <= 1 (error ~2^-16
+// relative per product); with fp32 inputs: three terms, order <= 2 (~2^-24).  bf16
+// input values are exact in one term.
+//
+// Register layout of the 16x16x32 bf16 MFMA (lane l, g = l / 16):
+//   A (16 x 32): row l % 16, contraction elements 8g .. 8g+7
+//   B (32 x 16): column l % 16, contraction elements 8g .. 8g+7
+//   C (16 x 16): column l % 16, rows 4g .. 4g+3
+// The contraction index is a dummy, so any permutation applied to both operands
+// gives the same sum.  All products here use the permutation
+//   kappa(s, g, e) = 32 s + 16 (e / 4) + 4 g + (e % 4)      (k-step s, element e),
+// under which the C layout of one product (rows 16 m + 4 g + r of tile m) is directly
+// the B operand of the next one (tiles 2s and 2s+1 give elements 0..3 and 4..7).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint16_t bf16_bits;
+
+// Precision policy per io type: terms of an input operand, terms of an fp32 operand,
+// highest product order kept.
+template <typename IO>
+struct Prec;
+template <>
+struct Prec<bf16_bits> {
+  static constexpr int NTI = 1, NTF = 2, ORD = 1;
+};
+template <>
+struct Prec<float> {
+  static constexpr int NTI = 3, NTF = 3, ORD = 2;
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// Round to nearest even (the conversion instruction of gfx950).
+__device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_bits, h);
+}
+__device__ __forceinline__ float to_f32(bf16_bits x) { return bf16_to_f32(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename IO>
+__device__ __forceinline__ IO from_f32(float x);
+template <>
+__device__ __forceinline__ bf16_bits from_f32<bf16_bits>(float x) { return f32_to_bf16(x); }
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Split x into NT bf16 terms; returns their bit patterns.
+template <int NT>
+__device__ __forceinline__ void split_terms(float x, bf16_bits (&t)[NT]) {
+  float r = x;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    t[i] = f32_to_bf16(r);
+    if (i + 1 < NT) r = r - bf16_to_f32(t[i]);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += sum over term pairs (i, j) with i + j <= ORD of A_i * B_j; the smallest
+// orders are accumulated first.
+template <int NA, int NB, int ORD>
+__device__ __forceinline__ void mma_terms(f32x4& acc, const bf16x8 (&a)[NA], const bf16x8 (&b)[NB]) {
+#pragma unroll
+  for (int o = ORD; o >= 0; --o) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int j = o - i;
+      if (j >= 0 && j < NB) acc = mfma(a[i], b[j], acc);
+    }
+  }
+}
+
+// Pack 8 bf16 bit patterns into an MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const bf16_bits (&v)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = __builtin_bit_cast(__bf16, v[e]);
+  return r;
+}
+
+// Operand from two runs of 4 bf16 in LDS (elements 0..3 at p0, 4..7 at p1).
+__device__ __forceinline__ bf16x8 lds_operand(const bf16_bits* p0, const bf16_bits* p1) {
+  uint2 lo = *reinterpret_cast<const uint2*>(p0);
+  uint2 hi = *reinterpret_cast<const uint2*>(p1);
+  typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+  u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Operand terms from fp32 register values laid out as the C tiles 2s and 2s+1:
+// v0 = tile 2s rows 0..3, v1 = tile 2s+1 rows 0..3 (pass zeros for a missing tile).
+template <int NT>
+__device__ __forceinline__ void reg_operand(const f32x4& v0, const f32x4& v1, bf16x8 (&out)[NT]) {
+  bf16_bits t[8][NT];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    split_terms<NT>(v0[r], t[r]);
+    split_terms<NT>(v1[r], t[4 + r]);
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    bf16_bits p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = t[e][i];
+    out[i] = pack8(p);
+  }
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Wave-wide inclusive prefix sum (64 lanes), fixed combination order.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (lane >= off) x = x + y;
+  }
+  return x;
+}
+
+}  // namespace gdn

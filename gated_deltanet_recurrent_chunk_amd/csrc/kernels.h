@@ -1,0 +1,115 @@
+// kernels.h -- kernel argument blocks and launchers of libgdn (host and device view).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace gdn {
+
+typedef uint16_t bf16_bits;
+
+// Workgroup shape of the scan: up to four 16-row waves per (sequence, head) group.
+template <int D>
+struct ScanShape {
+  static constexpr int NW = D >= 64 ? 4 : D / 16;
+};
+
+template <typename IO>
+struct FactorizeArgs {
+  const ChunkDesc* chunks;
+  const IO* k;
+  int64_t qk_stride;  // elements per token row of q and k
+  const float* a;
+  const float* b;
+  uint8_t* factors;
+  size_t factor_stride;
+  int32_t n_chunks;
+  int32_t Hv;
+  int32_t group;  // value heads per query/key head
+};
+
+template <typename IO>
+struct ScanArgs {
+  const ChunkDesc* chunks;
+  const ScanSeq* seqs;
+  const IO* q;
+  const IO* k;
+  const IO* v;
+  int64_t qk_stride;
+  int64_t v_stride;
+  const uint8_t* factors;
+  size_t factor_stride;
+  int32_t n_chunks;
+  int32_t Hv;
+  int32_t group;
+  float scale;
+  float* o;
+  uint8_t* ckpt_pool;
+  size_t page_bytes;
+};
+
+template <typename IO>
+struct FlushArgs {
+  float* state_pool;
+  const int32_t* slot_ids;
+  const int32_t* n_accepted;
+  const IO* buf_k;
+  const IO* buf_v;
+  const float* buf_a;
+  const float* buf_b;
+  int32_t* status;
+  int64_t n_slots;
+  int32_t buf_rows;
+  int32_t Hqk;
+  int32_t Hv;
+  int32_t group;
+};
+
+template <typename IO>
+struct DecodeArgs {
+  const IO* q;
+  const IO* k;
+  const IO* v;
+  const float* a;
+  const float* b;
+  float* state_pool;
+  const int32_t* slot_ids;
+  float* o;
+  int32_t* status;
+  int64_t n_slots;
+  int32_t Hqk;
+  int32_t Hv;
+  int32_t group;
+  float scale;
+};
+
+template <typename IO>
+struct ConvArgs {
+  const ConvSeq* seqs;
+  const ConvTile* tiles;
+  const int32_t* pages;
+  const IO* x;
+  const IO* w;
+  IO* y;
+  uint8_t* ckpt_pool;
+  size_t page_bytes;
+  size_t tail_offset;  // byte offset of the conv tail inside a page
+  int64_t channels;
+  int32_t block;
+  int32_t act;
+};
+
+hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, int n_chunks, hipStream_t st);
+hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, int n_chunks, hipStream_t st);
+hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, int n_seqs, hipStream_t st);
+hipError_t launch_scan(const ScanArgs<float>& a, int D, int n_seqs, hipStream_t st);
+hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st);
+hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, int ct, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs<bf16_bits>& a, int D, int n_req, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs<float>& a, int D, int n_req, hipStream_t st);
+hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st);
+hipError_t launch_conv(const ConvArgs<float>& a, int n_tiles, hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,273 @@
+// stream_kernels.hip -- the bandwidth-bound kernels of libgdn: decode step and conv update.
+//
+// Both read every byte once and write every byte once; the work is spread so that
+// consecutive lanes touch consecutive 16-byte pieces of a row.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace gdn {
+
+namespace {
+
+template <typename IO, int N>
+__device__ __forceinline__ void load_vec(const IO* p, float (&out)[N]) {
+  if constexpr (sizeof(IO) == 2) {
+    static_assert(N % 8 == 0, "bf16 vectors of 8");
+#pragma unroll
+    for (int u = 0; u < N / 8; ++u) {
+      uint4 v = reinterpret_cast<const uint4*>(p)[u];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        out[8 * u + e] = bf16_to_f32((bf16_bits)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu)));
+    }
+  } else {
+    static_assert(N % 4 == 0, "fp32 vectors of 4");
+#pragma unroll
+    for (int u = 0; u < N / 4; ++u) {
+      float4 v = reinterpret_cast<const float4*>(p)[u];
+      out[4 * u] = v.x;
+      out[4 * u + 1] = v.y;
+      out[4 * u + 2] = v.z;
+      out[4 * u + 3] = v.w;
+    }
+  }
+}
+
+template <typename IO, int N>
+__device__ __forceinline__ void store_vec(IO* p, const float (&in)[N]) {
+  if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+    for (int u = 0; u < N / 8; ++u) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)f32_to_bf16(in[8 * u + 2 * e]) | ((uint32_t)f32_to_bf16(in[8 * u + 2 * e + 1]) << 16);
+      reinterpret_cast<uint4*>(p)[u] = uint4{w[0], w[1], w[2], w[3]};
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < N / 4; ++u)
+      reinterpret_cast<float4*>(p)[u] = float4{in[4 * u], in[4 * u + 1], in[4 * u + 2], in[4 * u + 3]};
+  }
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace
+
+// ==================================================================================
+// Decode: one workgroup per (request, value head).  A state row is covered by D/8
+// lanes holding 8 consecutive floats each; one pass computes, per row i,
+//   r_k = s_i . k,  r_q = s_i . q,  delta_i = b (v_i - a r_k),
+//   s_i <- a s_i + delta_i k,  o_i = scale (a r_q + delta_i (k . q)),
+// which is S_t = a S (I - b k k^T) + b v k^T and o = S_t q expanded, with the state
+// read and written exactly once.
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
+  constexpr int LPR = D / 8;
+  constexpr int NTH = (D * LPR < 256) ? D * LPR : 256;
+  constexpr int RPP = NTH / LPR;
+  constexpr int NP = D / RPP;
+  const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int slot = p.slot_ids[r];
+  if (slot < -1 || slot >= p.n_slots) {
+    if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
+    return;
+  }
+  if (slot < 0) return;  // padding: nothing read, nothing written
+  const int sub = tid % LPR, rowi = tid / LPR;
+  const int j0 = sub * 8;
+  const int hk = h / p.group;
+  float* st = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
+
+  f32x4 s[NP][2];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const int i = pp * RPP + rowi;
+    s[pp][0] = *reinterpret_cast<const f32x4*>(st + (size_t)i * D + j0);
+    s[pp][1] = *reinterpret_cast<const f32x4*>(st + (size_t)i * D + j0 + 4);
+  }
+  float k[8], q[8];
+  load_vec<IO, 8>(p.k + ((size_t)r * p.Hqk + hk) * D + j0, k);
+  load_vec<IO, 8>(p.q + ((size_t)r * p.Hqk + hk) * D + j0, q);
+  const float a = p.a[(size_t)r * p.Hv + h];
+  const float b = p.b[(size_t)r * p.Hv + h];
+  const IO* vrow = p.v + ((size_t)r * p.Hv + h) * D;
+  float vi[NP];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) vi[pp] = to_f32(vrow[pp * RPP + rowi]);
+
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kq = fmaf(k[e], q[e], kq);
+  kq = group_sum<LPR>(kq);
+
+  float* orow = p.o + ((size_t)r * p.Hv + h) * D;
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const int i = pp * RPP + rowi;
+    float rk = 0.f, rq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rk = fmaf(s[pp][0][e], k[e], rk);
+      rq = fmaf(s[pp][0][e], q[e], rq);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rk = fmaf(s[pp][1][e], k[4 + e], rk);
+      rq = fmaf(s[pp][1][e], q[4 + e], rq);
+    }
+    rk = group_sum<LPR>(rk);
+    rq = group_sum<LPR>(rq);
+    const float delta = b * (vi[pp] - a * rk);
+    f32x4 n0, n1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      n0[e] = fmaf(a, s[pp][0][e], delta * k[e]);
+      n1[e] = fmaf(a, s[pp][1][e], delta * k[4 + e]);
+    }
+    *reinterpret_cast<f32x4*>(st + (size_t)i * D + j0) = n0;
+    *reinterpret_cast<f32x4*>(st + (size_t)i * D + j0 + 4) = n1;
+    if (sub == 0) orow[i] = p.scale * fmaf(a, rq, delta * kq);
+  }
+}
+
+// ==================================================================================
+// Conv: thread = VEC consecutive channels x one tile of up to kConvTile rows of one
+// sequence.  The three previous raw rows travel in registers; the rows before a
+// sequence's first token come from its tail source (or are zero, never read).
+//   y[t][c] = act(w[c][0] x[t-3][c] + w[c][1] x[t-2][c] + w[c][2] x[t-1][c] + w[c][3] x[t][c])
+// At an absolute block boundary the three raw rows before it go to that page's tail
+// region.  The first tile of each sequence also writes the sequence's new tail; it is
+// the only tile that reads the old one, so an in-place tail update is safe.
+template <typename IO>
+__global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
+  constexpr int VEC = 16 / sizeof(IO);
+  const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * VEC;
+  if (c0 >= p.channels) return;
+  const ConvTile tile = p.tiles[blockIdx.x];
+  const ConvSeq sq = p.seqs[tile.seq];
+  const int64_t C = p.channels;
+  const int64_t rel0 = tile.row - sq.row0;
+
+  float w[4][VEC];
+  {
+    float wr[4 * VEC];
+    load_vec<IO, 4 * VEC>(p.w + c0 * 4, wr);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j][e] = wr[4 * e + j];
+  }
+  const IO* src = reinterpret_cast<const IO*>(sq.src_tail);
+  auto load_row = [&](int64_t rel, float (&out)[VEC]) {
+    if (rel >= 0) {
+      load_vec<IO, VEC>(p.x + (sq.row0 + rel) * C + c0, out);
+    } else if (src) {
+      load_vec<IO, VEC>(src + (3 + rel) * C + c0, out);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) out[e] = 0.f;
+    }
+  };
+  float h0[VEC], h1[VEC], h2[VEC];
+  load_row(rel0 - 3, h0);
+  load_row(rel0 - 2, h1);
+  load_row(rel0 - 1, h2);
+  const int64_t pblk = p.block > 0 ? sq.p0 / p.block : 0;
+  for (int t = 0; t < tile.len; ++t) {
+    float xt[VEC], yv[VEC];
+    load_row(rel0 + t, xt);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float acc = w[0][e] * h0[e];
+      acc = fmaf(w[1][e], h1[e], acc);
+      acc = fmaf(w[2][e], h2[e], acc);
+      acc = fmaf(w[3][e], xt[e], acc);
+      if (p.act == GDN_ACT_SILU) acc = acc / (1.f + expf(-acc));
+      yv[e] = acc;
+      h0[e] = h1[e];
+      h1[e] = h2[e];
+      h2[e] = xt[e];
+    }
+    store_vec<IO, VEC>(p.y + (tile.row + t) * C + c0, yv);
+    if (p.block > 0) {
+      const int64_t pos = sq.p0 + rel0 + t + 1;
+      if (pos % p.block == 0) {
+        const int32_t pid = p.pages[sq.page_begin + (pos / p.block - pblk - 1)];
+        if (pid >= 0) {
+          IO* dst = reinterpret_cast<IO*>(p.ckpt_pool + (size_t)pid * p.page_bytes + p.tail_offset);
+          store_vec<IO, VEC>(dst + c0, h0);
+          store_vec<IO, VEC>(dst + C + c0, h1);
+          store_vec<IO, VEC>(dst + 2 * C + c0, h2);
+        }
+      }
+    }
+  }
+  if (rel0 == 0) {
+    float t0[VEC], t1[VEC], t2[VEC];
+    load_row(sq.len - 3, t0);
+    load_row(sq.len - 2, t1);
+    load_row(sq.len - 1, t2);
+    IO* dst = reinterpret_cast<IO*>(sq.dst_tail);
+    store_vec<IO, VEC>(dst + c0, t0);
+    store_vec<IO, VEC>(dst + C + c0, t1);
+    store_vec<IO, VEC>(dst + 2 * C + c0, t2);
+  }
+}
+
+// ==================================================================================
+template <typename IO, int D>
+static hipError_t launch_decode_t(const DecodeArgs<IO>& a, int n_req, hipStream_t st) {
+  if (n_req == 0) return hipSuccess;
+  constexpr int LPR = D / 8;
+  constexpr int NTH = (D * LPR < 256) ? D * LPR : 256;
+  hipLaunchKernelGGL((decode_kernel<IO, D>), dim3(n_req, a.Hv), dim3(NTH), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs<bf16_bits>& a, int D, int n_req, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_decode_t<bf16_bits, 16>(a, n_req, st);
+    case 32: return launch_decode_t<bf16_bits, 32>(a, n_req, st);
+    case 64: return launch_decode_t<bf16_bits, 64>(a, n_req, st);
+    case 128: return launch_decode_t<bf16_bits, 128>(a, n_req, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+hipError_t launch_decode(const DecodeArgs<float>& a, int D, int n_req, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_decode_t<float, 16>(a, n_req, st);
+    case 32: return launch_decode_t<float, 32>(a, n_req, st);
+    case 64: return launch_decode_t<float, 64>(a, n_req, st);
+    case 128: return launch_decode_t<float, 128>(a, n_req, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename IO>
+static hipError_t launch_conv_t(const ConvArgs<IO>& a, int n_tiles, hipStream_t st) {
+  if (n_tiles == 0) return hipSuccess;
+  constexpr int VEC = 16 / sizeof(IO);
+  const int64_t groups = a.channels / VEC;
+  dim3 grid((unsigned)n_tiles, (unsigned)((groups + 255) / 256));
+  hipLaunchKernelGGL((conv_kernel<IO>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st) {
+  return launch_conv_t<bf16_bits>(a, n_tiles, st);
+}
+hipError_t launch_conv(const ConvArgs<float>& a, int n_tiles, hipStream_t st) {
+  return launch_conv_t<float>(a, n_tiles, st);
+}
+
+}  // namespace gdn

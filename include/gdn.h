@@ -1,0 +1,277 @@
+/*
+ * gdn.h -- C ABI of libgdn, the Gated DeltaNet recurrent-state update for AMD MI355X (gfx950).
+ *
+ * The operation.  Per value head, a state S of d x d fp32 (row i = value channel,
+ * column j = key channel) follows the gated delta rule (Yang, Kautz & Hatamizadeh,
+ * "Gated Delta Networks: Improving Mamba2 with Delta Rule", ICLR 2025):
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,     o_t = scale * S_t q_t
+ *
+ * with a_t in (0, 1] (the decay gate) and b_t in [0, 1] (the write strength).  A
+ * layer holds one such state per value head plus a short causal conv window over
+ * the packed q|k|v channels.  The state shape (48 heads x 128 x 128 fp32 per layer
+ * on the 27B models, 32 heads on the 4B ones) and the conv window being part of the
+ * state come from "Prefix caching on Gated DeltaNet hybrids" (section "Why hits were
+ * wrong") and "Hybrid linear attention (gated DeltaNet)" (section "Why this family is
+ * different").
+ *
+ * Conventions for every call:
+ *   - Pointers marked [host] are host memory read before the call returns; all other
+ *     pointers are device memory of the current HIP device.  The caller owns all
+ *     memory; libgdn allocates and frees nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` and runs asynchronously.  Argument validation is
+ *     synchronous and happens before anything is enqueued: on any error the call
+ *     returns a non-zero gdn_status, enqueues nothing and modifies no memory (fail
+ *     closed, as "Prefix caching on Gated DeltaNet hybrids", section "The in-page
+ *     layout", requires of a partial-block copy or an off-boundary resume).
+ *   - Token-major packed layouts: q, k are [tokens][n_qk_heads][d]; v and o are
+ *     [tokens][n_v_heads][d]; a, b are [tokens][n_v_heads] fp32.  Value head h reads
+ *     query/key head h / (n_v_heads / n_qk_heads).
+ *   - A state is fp32 [n_v_heads][d][d], row-major (value channel major).
+ *   - Masked or unused rows are excluded by selection, never by multiplying with a
+ *     mask, so NaN bit patterns in rows a call must not read cannot reach a result
+ *     ("Prefix caching on Gated DeltaNet hybrids", "The in-page layout", defect 1).
+ *
+ * Determinism.  For one sequence, given its inputs, its start position, the bits of
+ * its state source and the layer descriptor, every output, checkpoint and final state
+ * is bit-identical whatever the other sequences of the call are, however many there
+ * are and in which order, and however the sequence is split across calls, provided
+ * each split falls on a multiple of 64 tokens or of the block.  This is what makes a
+ * resume from a checkpoint equal a cold run ("The prefix cache changed the answer",
+ * section "The fix: one line").  Decode versus prefill, and a replay flush versus
+ * token-by-token updates, agree within rounding but not bitwise.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL_ARG = 1,        /* a required pointer is NULL */
+  GDN_ERR_BAD_SHAPE = 2,       /* head counts, head_dim, conv width or strides not supported */
+  GDN_ERR_BAD_DTYPE = 3,       /* unknown dtype or activation code */
+  GDN_ERR_BAD_VARLEN = 4,      /* cu_seqlens not starting at 0 / decreasing, negative start_pos */
+  GDN_ERR_OFF_BOUNDARY = 5,    /* state source inconsistent with start_pos (see gdn_src) */
+  GDN_ERR_PAGE_TOO_SMALL = 6,  /* page_bytes < gdn_checkpoint_bytes, or misaligned pool */
+  GDN_ERR_BAD_PAGE = 7,        /* page id outside [-1, n_pages) or a page used twice */
+  GDN_ERR_CAPACITY = 8,        /* a count exceeds what the call supports (rows, slots) */
+  GDN_ERR_WORKSPACE = 9,       /* workspace NULL, too small or misaligned */
+  GDN_ERR_HIP = 10,            /* a HIP runtime call failed while enqueueing */
+  GDN_ERR_BAD_SOURCE = 11      /* unknown state source kind */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_act { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_act;
+
+/* Layer descriptor.  head_dim is d_k = d_v and must be 16, 32, 64 or 128.
+ * n_v_heads must be a positive multiple of n_qk_heads: invalid dimensions and head
+ * counts that do not divide are refused, as "Hybrid linear attention (gated
+ * DeltaNet)", section "Packed-core traces", requires.  conv_width must be 4.
+ * io_dtype is the type of q, k, v and of the conv input, output, weights and tails.
+ * The conv activation is applied after the conv sum. */
+typedef struct gdn_layer {
+  int32_t n_qk_heads;
+  int32_t n_v_heads;
+  int32_t head_dim;
+  int32_t conv_width;
+  int32_t io_dtype;  /* gdn_dtype */
+  int32_t conv_act;  /* gdn_act */
+  float scale;       /* output scale, e.g. 1.0 or 1/sqrt(d) */
+} gdn_layer;
+
+/* Variable-length batch, all [host].  Sequence s owns packed rows
+ * [cu_seqlens[s], cu_seqlens[s+1]); cu_seqlens[0] == 0 and it never decreases (a
+ * sequence may have zero rows).  start_pos[s] >= 0 is the absolute position, counted
+ * from the start of that sequence, of its first row in this call. */
+typedef struct gdn_varlen {
+  int32_t n_seqs;
+  const int64_t* cu_seqlens; /* [host] n_seqs + 1 */
+  const int64_t* start_pos;  /* [host] n_seqs */
+} gdn_varlen;
+
+/* Where a sequence's incoming state (or conv tail) comes from.
+ *   GDN_SRC_ZERO:       all zeros; requires start_pos == 0; no memory is read.
+ *   GDN_SRC_SLOT:       `src` points at the state (or tail) itself; requires start_pos > 0.
+ *   GDN_SRC_CHECKPOINT: `src` points at a checkpoint page (layout below); requires
+ *                       start_pos > 0 and start_pos % block == 0: a resume off a block
+ *                       boundary is refused ("Prefix caching on Gated DeltaNet
+ *                       hybrids", "The in-page layout": fail closed), since a state can
+ *                       only be restored where one was saved ("The cache block that is
+ *                       not a cache setting", "Why a hybrid cannot use a 64-token page"). */
+typedef enum gdn_src { GDN_SRC_ZERO = 0, GDN_SRC_SLOT = 1, GDN_SRC_CHECKPOINT = 2 } gdn_src;
+
+/* Per-sequence state reference, [host] array of n_seqs.  `dst` receives the state (or
+ * tail) after the sequence's last row; it may equal `src` for an in-place update but
+ * must not overlap another sequence's src or dst. */
+typedef struct gdn_state_ref {
+  int32_t src_kind; /* gdn_src */
+  const void* src;  /* device */
+  void* dst;        /* device */
+} gdn_state_ref;
+
+/* Checkpoint pages.  A page holds, from its start: the fp32 state
+ * [n_v_heads][d][d] (gdn_state_bytes), then the conv tail [conv_width-1][channels] in
+ * io_dtype (gdn_conv_tail_bytes).  "Prefix caching on Gated DeltaNet hybrids" ("Why
+ * hits were wrong", "The in-page layout") stores such checkpoints inside attention
+ * pages of block * bytes-per-token; any page_bytes >= gdn_checkpoint_bytes works.
+ * A checkpoint is written when a sequence's absolute position reaches a positive
+ * multiple of `block` (the call's last row included): it holds the state after
+ * exactly that many tokens ("a full block must keep the recurrent state after its
+ * last token", same section).  page_ids lists one page per crossed boundary,
+ * sequences in order and boundaries in order (gdn_count_boundaries gives the count
+ * per sequence); -1 means "do not store this one".  block == 0 disables
+ * checkpoints; the pool and page_ids are then not read. */
+typedef struct gdn_ckpt {
+  void* pool;                /* device, 256-byte aligned */
+  int64_t page_bytes;        /* multiple of 256 */
+  int64_t n_pages;
+  int32_t block;             /* tokens per cache block, >= 0 */
+  const int32_t* page_ids;   /* [host] */
+} gdn_ckpt;
+
+/* ---------------------------------------------------------------- sizes and helpers */
+
+int32_t gdn_abi_version(void);
+const char* gdn_status_string(gdn_status status);
+
+/* Bytes of one fp32 state: n_v_heads * d * d * 4.  -1 if the layer is invalid. */
+int64_t gdn_state_bytes(const gdn_layer* layer);
+/* Bytes of one conv tail: (conv_width - 1) * (2 n_qk_heads + n_v_heads) d * sizeof(io). */
+int64_t gdn_conv_tail_bytes(const gdn_layer* layer);
+/* State plus conv tail, rounded up to 256 bytes: the minimum page_bytes. */
+int64_t gdn_checkpoint_bytes(const gdn_layer* layer);
+/* Number of conv channels (2 n_qk_heads + n_v_heads) * d. */
+int64_t gdn_conv_channels(const gdn_layer* layer);
+
+/* Tokens served from cache for a shared prefix: whole blocks only, the last full
+ * block left open, so max(0, (floor(shared / block) - 1) * block) ("The cache block
+ * that is not a cache setting", section "What that costs, exactly").  0 if block <= 0. */
+int64_t gdn_cached_prefix_tokens(int64_t shared, int64_t block);
+/* A prefill chunk budget floored to a block boundary, floor(budget / block) * block
+ * ("Hybrid linear attention (gated DeltaNet)", "Why this family is different", item 3).
+ * Returns budget when block <= 0. */
+int64_t gdn_floor_chunk(int64_t budget, int64_t block);
+/* Number of block boundaries p * block, p >= 1, in (start_pos, start_pos + n_tokens]. */
+int64_t gdn_count_boundaries(int64_t start_pos, int64_t n_tokens, int64_t block);
+/* Cache block size that lets one attention page hold one state:
+ * alignment * cdiv(state_bytes, alignment * attn_bytes_per_token) ("Hybrid linear
+ * attention (gated DeltaNet)", "Why this family is different", item 2).  -1 on bad input. */
+int64_t gdn_block_size_for_state(int64_t state_bytes, int64_t attn_bytes_per_token,
+                                 int64_t alignment);
+
+/* Workspace bytes gdn_chunk_prefill needs for this batch and block. -1 if invalid. */
+int64_t gdn_prefill_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
+                                    int32_t block);
+/* Workspace bytes gdn_conv_update needs for this batch and block. -1 if invalid. */
+int64_t gdn_conv_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
+                                 int32_t block);
+
+/* ---------------------------------------------------------------- the hot path */
+
+/* Short causal conv update over a varlen batch ("Hybrid linear attention (gated
+ * DeltaNet)", section "The part that is easy to get wrong": gdn_conv_prefill /
+ * gdn_conv_decode).
+ *   x  [tokens][C] io_dtype, C = gdn_conv_channels (packed q | k | v channels)
+ *   w  [C][conv_width] io_dtype; w[c][conv_width-1] multiplies the current token
+ *   y  [tokens][C] io_dtype: act(sum_j w[c][j] * x[t - (W-1) + j][c]), fp32 sums,
+ *      rounded to io_dtype with round-to-nearest-even
+ *   tails [host] n_seqs refs to [W-1][C] io_dtype tails (oldest row first): the rows
+ *      before each sequence's first token (ZERO: none), and the last W-1 rows after
+ *      it.  A CHECKPOINT source is a page base; the tail is read from its tail region.
+ *   ckpt: at every crossed block boundary, the W-1 raw rows before it are written
+ *      to the tail region of that boundary's page.
+ * x and y must not overlap.  Errors: see gdn_status. */
+gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
+                           const void* x, const void* w, const gdn_state_ref* tails,
+                           const gdn_ckpt* ckpt, void* y, void* workspace,
+                           size_t workspace_bytes);
+
+/* Chunked varlen prefill of the gated delta rule with block checkpoints ("Hybrid
+ * linear attention (gated DeltaNet)", "The part that is easy to get wrong":
+ * gdn_prefill; checkpoints and resume as in "Prefix caching on Gated DeltaNet hybrids",
+ * "Why hits were wrong").
+ *   q, k  [tokens][qk_stride] io_dtype, head h at offset h*d; qk_stride >= n_qk_heads*d
+ *         (pass n_qk_heads*d for dense tensors).  The recurrence reads them as given
+ *         (no normalisation).
+ *   v     [tokens][v_stride] io_dtype, v_stride >= n_v_heads*d.
+ *   a, b  [tokens][n_v_heads] fp32.  a in (0, 1], b in [0, 1].
+ *   states [host] n_seqs state refs (ZERO, SLOT or CHECKPOINT); dst gets the final state.
+ *   ckpt  block checkpoints (state region of each page).
+ *   o     [tokens][n_v_heads][d] fp32.
+ *   workspace >= gdn_prefill_workspace_bytes(layer, varlen, ckpt->block), 256-byte aligned.
+ * Each sequence is cut into chunks at every multiple of 64 tokens, at every multiple
+ * of the block and at the call's ends, positions counted from the sequence start, so
+ * every crossed block boundary ends a chunk ("The prefix cache changed the answer",
+ * "The fix: one line").  q, k, v, a, b, o and the workspace must not overlap. */
+gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream,
+                             const gdn_varlen* varlen, const void* q, const void* k,
+                             const void* v, int64_t qk_stride, int64_t v_stride, const float* a,
+                             const float* b, const gdn_state_ref* states, const gdn_ckpt* ckpt,
+                             float* o, void* workspace, size_t workspace_bytes);
+
+/* The two stages of gdn_chunk_prefill, for callers that schedule or time them apart.
+ * gdn_prefill_factorize computes, for every chunk and value head, the state-free
+ * chunk factors (the cumulative log-decay and the inverse of the unit lower
+ * triangular key-interaction matrix, the WY / UT transform of the chunk) into the
+ * workspace.  gdn_prefill_scan then walks each sequence chunk by chunk and applies
+ * them to the state.  The scan must run on the same stream after a factorize with the
+ * same layer, varlen, k, a, b, ckpt->block and workspace.  Together they do exactly
+ * what gdn_chunk_prefill does. */
+gdn_status gdn_prefill_factorize(const gdn_layer* layer, hipStream_t stream,
+                                 const gdn_varlen* varlen, const void* k, int64_t qk_stride,
+                                 const float* a, const float* b, int32_t block, void* workspace,
+                                 size_t workspace_bytes);
+gdn_status gdn_prefill_scan(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
+                            const void* q, const void* k, const void* v, int64_t qk_stride,
+                            int64_t v_stride, const gdn_state_ref* states, const gdn_ckpt* ckpt,
+                            float* o, void* workspace, size_t workspace_bytes);
+
+/* One decode token per request ("Hybrid linear attention (gated DeltaNet)", "The part
+ * that is easy to get wrong": gdn_decode).  Request r updates the state in slot
+ * slot_ids[r] of state_pool [n_slots][n_v_heads][d][d] in place and writes
+ * o[r] = scale * S_new q.
+ *   q, k [n_req][n_qk_heads][d], v [n_req][n_v_heads][d] io_dtype; a, b [n_req][n_v_heads].
+ *   slot_ids [n_req] int32 (device): -1 marks padding: that request reads and writes
+ *   nothing, its o row included ("Prefix caching on Gated DeltaNet hybrids", "The
+ *   in-page layout", defect 2).  A slot id outside [-1, n_slots) is not touched either
+ *   and sets GDN_ERR_CAPACITY in *status.  Two requests must not share a slot.
+ *   status: device int32, may be NULL; data-dependent errors are OR-ed into it. */
+gdn_status gdn_decode_step(const gdn_layer* layer, hipStream_t stream, int32_t n_req,
+                           const void* q, const void* k, const void* v, const float* a,
+                           const float* b, float* state_pool, int64_t n_slots,
+                           const int32_t* slot_ids, float* o, int32_t* status);
+
+/* ReplaySSM flush ("Caching less to serve more requests", section "What we changed"):
+ * each request keeps one state plus a log of per-token inputs since it; the flush
+ * folds the first n_accepted[r] logged rows of request r into its state as one
+ * blocked update, in one launch for all requests.  The state in slot slot_ids[r] of
+ * state_pool [n_slots][n_v_heads][d][d] is read once and written once; rows at or
+ * past n_accepted[r] are never read (a rollback is just a smaller n_accepted).
+ *   buf_k [n_slots][buf_rows][n_qk_heads][d], buf_v [n_slots][buf_rows][n_v_heads][d]
+ *   io_dtype; buf_a, buf_b [n_slots][buf_rows][n_v_heads] fp32: the log of each slot.
+ *   buf_rows <= 64 (the pages use 32).  n_accepted [n_req] int32 (device): requests
+ *   with 0 rows or slot -1 are left untouched; n_accepted outside [0, buf_rows] or a
+ *   slot outside [-1, n_slots) leaves the request untouched and sets GDN_ERR_CAPACITY
+ *   in *status (device int32, may be NULL).  Two requests must not share a slot. */
+gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t n_req,
+                            float* state_pool, int64_t n_slots, const int32_t* slot_ids,
+                            const void* buf_k, const void* buf_v, const float* buf_a,
+                            const float* buf_b, int32_t buf_rows, const int32_t* n_accepted,
+                            int32_t* status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,315 @@
+"""GPU parity: libgdn (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Sizes span several 64-row chunks and a ragged tail; tolerances are the relative L2
+bounds 1e-3 (bf16 inputs) and 1e-5 (fp32 inputs).  Bit-exactness is required only
+GPU against GPU: resume-from-checkpoint against the cold run, and a sequence in a
+varlen batch against the same sequence alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from gpu_util import TOL, bits, f64, make_pool, nan_fill_, rel_l2, same_bits, say
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gated_deltanet_recurrent_chunk_amd as lib
+    return lib
+
+
+def _dev(*ts):
+    return [t.cuda() for t in ts]
+
+
+PREFILL_CASES = [
+    # T, Hqk, Hv, D, dtype, block
+    (64, 2, 2, 16, torch.float32, 16),       # the tiny workload: four 16-token chunks
+    (300, 2, 4, 128, torch.bfloat16, 128),   # value heads sharing key heads, ragged tail
+    (200, 1, 1, 64, torch.bfloat16, 80),     # block off the 64-grid
+    (130, 2, 2, 32, torch.bfloat16, 0),      # no checkpoints
+    (100, 1, 2, 32, torch.float32, 48),
+    (257, 1, 1, 128, torch.bfloat16, 64),
+]
+
+
+@pytest.mark.parametrize("T,Hqk,Hv,D,dtype,block", PREFILL_CASES)
+def test_prefill_cold_matches_oracle(g, T, Hqk, Hv, D, dtype, block):
+    say(f"prefill cold T={T} Hqk={Hqk} Hv={Hv} D={D} {dtype} block={block}")
+    layer = g.Layer(Hqk, Hv, D, dtype, scale=0.5)
+    q, k, v, a, b = gi.qkvab(T, Hqk, Hv, D, dtype, seed=11 + T)
+    n_ck = oracle.count_boundaries(0, T, block)
+    pool = make_pool(g, layer, n_ck + 3, block)
+    page_ids = [int(p) for p in gi.permutation(n_ck + 3, 5)[:n_ck]]
+    qd, kd, vd, ad, bd = _dev(q, k, v, a, b)
+    o = torch.full((T, Hv, D), float("nan"), device="cuda")
+    S = torch.empty(Hv, D, D, device="cuda")
+    g.chunk_prefill(layer, qd, kd, vd, ad, bd, [0, T], [0], [("zero", None, S)], o, ckpt=pool,
+                    page_ids=page_ids)
+    torch.cuda.synchronize()
+    o_ref, S_ref, ck_ref = oracle.recurrence(f64(q), f64(k), f64(v), f64(a), f64(b), 0.5, None, 0, block)
+    tol = TOL[dtype]
+    assert rel_l2(f64(o), o_ref) <= tol
+    assert rel_l2(f64(S), S_ref) <= tol
+    for i in range(n_ck):
+        assert rel_l2(f64(pool.state_view(page_ids[i], layer)), ck_ref[i]) <= tol, i
+    # pages not named by the call keep their contents
+    for p in range(n_ck + 3):
+        if p not in page_ids:
+            assert (pool.pool[p].view(torch.int32) == 0x7FC0DEAD).all()
+
+
+@pytest.mark.parametrize("T,Hqk,Hv,D,dtype,block", [c for c in PREFILL_CASES if c[5] > 0])
+def test_resume_from_checkpoint_is_bit_identical_to_cold(g, T, Hqk, Hv, D, dtype, block):
+    say(f"resume T={T} D={D} {dtype} block={block}")
+    layer = g.Layer(Hqk, Hv, D, dtype)
+    q, k, v, a, b = gi.qkvab(T, Hqk, Hv, D, dtype, seed=21 + T)
+    n_ck = oracle.count_boundaries(0, T, block)
+    pool = make_pool(g, layer, 2 * n_ck + 1, block)
+    qd, kd, vd, ad, bd = _dev(q, k, v, a, b)
+    o = torch.empty(T, Hv, D, device="cuda")
+    S = torch.empty(Hv, D, D, device="cuda")
+    g.chunk_prefill(layer, qd, kd, vd, ad, bd, [0, T], [0], [("zero", None, S)], o, ckpt=pool,
+                    page_ids=list(range(n_ck)))
+    for p in range(1, n_ck + 1):
+        s0 = p * block
+        if s0 >= T:
+            break
+        L = T - s0
+        o2 = torch.empty(L, Hv, D, device="cuda")
+        S2 = torch.empty(Hv, D, D, device="cuda")
+        n2 = oracle.count_boundaries(s0, L, block)
+        g.chunk_prefill(layer, qd[s0:], kd[s0:], vd[s0:], ad[s0:], bd[s0:], [0, L], [s0],
+                        [("checkpoint", pool.page_ptr(p - 1), S2)], o2, ckpt=pool,
+                        page_ids=list(range(n_ck, n_ck + n2)))
+        torch.cuda.synchronize()
+        assert same_bits(o2, o[s0:]), f"outputs after resume at {s0}"
+        assert same_bits(S2, S), f"final state after resume at {s0}"
+        for i in range(n2):
+            assert torch.equal(pool.pool[n_ck + i, :layer.state_bytes], pool.pool[p + i, :layer.state_bytes])
+
+
+def test_varlen_batch_is_bit_identical_to_solo_runs(g):
+    D, H, dtype, block = 128, 2, torch.bfloat16, 128
+    layer = g.Layer(H, H, D, dtype)
+    lens = [150, 64, 1, 300, 0, 77]
+    starts = [0, 128, 256, 0, 0, 384]
+    say(f"varlen lens={lens} starts={starts}")
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    T = cu[-1]
+    q, k, v, a, b = gi.qkvab(T, H, H, D, dtype, seed=31)
+    qd, kd, vd, ad, bd = _dev(q, k, v, a, b)
+    S0 = (0.1 * torch.randn(len(lens), H, D, D, generator=torch.Generator().manual_seed(3))).cuda()
+    n_b = [oracle.count_boundaries(s, L, block) for s, L in zip(starts, lens)]
+    pool = make_pool(g, layer, 2 * sum(n_b) + 1, block)
+    o = torch.empty(T, H, D, device="cuda")
+    Sf = torch.empty(len(lens), H, D, D, device="cuda")
+    refs = [("zero" if s == 0 else "slot", None if s == 0 else S0[i], Sf[i]) for i, s in enumerate(starts)]
+    g.chunk_prefill(layer, qd, kd, vd, ad, bd, cu, starts, refs, o, ckpt=pool, page_ids=list(range(sum(n_b))))
+    base = sum(n_b)
+    for i, (s, L) in enumerate(zip(starts, lens)):
+        r0 = cu[i]
+        o1 = torch.empty(max(L, 1), H, D, device="cuda")
+        S1 = torch.empty(H, D, D, device="cuda")
+        ref = ("zero" if s == 0 else "slot", None if s == 0 else S0[i], S1)
+        g.chunk_prefill(layer, qd[r0:r0 + L] if L else qd, kd[r0:r0 + L] if L else kd, vd[r0:r0 + L] if L else vd,
+                        ad[r0:r0 + L] if L else ad, bd[r0:r0 + L] if L else bd, [0, L], [s], [ref], o1, ckpt=pool,
+                        page_ids=list(range(base, base + n_b[i])))
+        torch.cuda.synchronize()
+        if L:
+            assert same_bits(o1[:L], o[r0:r0 + L]), i
+        assert same_bits(S1, Sf[i]), i
+        off = sum(n_b[:i])
+        for j in range(n_b[i]):
+            assert torch.equal(pool.pool[base + j, :layer.state_bytes], pool.pool[off + j, :layer.state_bytes])
+        # and the oracle agrees
+        if L:
+            o_ref, S_ref, _ = oracle.recurrence(f64(q[r0:r0 + L]), f64(k[r0:r0 + L]), f64(v[r0:r0 + L]),
+                                                f64(a[r0:r0 + L]), f64(b[r0:r0 + L]), 1.0,
+                                                None if s == 0 else f64(S0[i]), s, block)
+            assert rel_l2(f64(o1[:L]), o_ref) <= TOL[dtype]
+            assert rel_l2(f64(S1), S_ref) <= TOL[dtype]
+        elif s != 0:
+            assert same_bits(S1, S0[i])
+        else:
+            assert not S1.any()
+
+
+def test_identity_gate_is_bitwise_identity(g):
+    """a = 1, b = 0: the state comes back bit for bit, o = scale * S_0 q."""
+    D, H, T = 128, 2, 150
+    layer = g.Layer(H, H, D, torch.bfloat16, scale=1.0)
+    q, k, v, _, _ = gi.qkvab(T, H, H, D, torch.bfloat16, seed=41)
+    a = torch.ones(T, H)
+    b = torch.zeros(T, H)
+    S0 = (0.1 * torch.randn(H, D, D, generator=torch.Generator().manual_seed(4))).cuda()
+    o = torch.empty(T, H, D, device="cuda")
+    S = torch.empty(H, D, D, device="cuda")
+    qd, kd, vd, ad, bd = _dev(q, k, v, a, b)
+    say("identity gate")
+    g.chunk_prefill(layer, qd, kd, vd, ad, bd, [0, T], [64], [("slot", S0, S)], o)
+    torch.cuda.synchronize()
+    assert same_bits(S, S0)
+    o_ref = np.einsum("hij,thj->thi", f64(S0), f64(q))
+    assert rel_l2(f64(o), o_ref) <= 1e-3
+
+
+# ------------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (16, torch.float32), (64, torch.bfloat16)])
+def test_decode_matches_oracle_and_skips_padding(g, D, dtype):
+    Hqk, Hv, n_slots = 2, 4, 5
+    layer = g.Layer(Hqk, Hv, D, dtype, scale=0.7)
+    slots = [3, -1, 0, 4]
+    n = len(slots)
+    say(f"decode D={D} {dtype} slots={slots}")
+    q, k, v, a, b = gi.qkvab(n, Hqk, Hv, D, dtype, seed=51)
+    pool = gi.states(n_slots, Hv, D, seed=52).cuda()
+    nan_fill_(pool[1])
+    nan_fill_(pool[2])
+    before = pool.clone()
+    o = nan_fill_(torch.empty(n, Hv, D, device="cuda"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qd, kd, vd, ad, bd = _dev(q, k, v, a, b)
+    g.decode_step(layer, qd, kd, vd, ad, bd, pool, torch.tensor(slots, dtype=torch.int32, device="cuda"), o,
+                  status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    tol = TOL[dtype]
+    for r, s in enumerate(slots):
+        if s < 0:
+            assert same_bits(o[r], nan_fill_(torch.empty_like(o[r])))
+            continue
+        o_ref, S_ref, _ = oracle.recurrence(f64(q[r:r + 1]), f64(k[r:r + 1]), f64(v[r:r + 1]), f64(a[r:r + 1]),
+                                            f64(b[r:r + 1]), 0.7, f64(before[s]))
+        assert rel_l2(f64(o[r]), o_ref[0]) <= tol
+        assert rel_l2(f64(pool[s]), S_ref) <= tol
+    assert same_bits(pool[1], before[1]) and same_bits(pool[2], before[2])
+
+
+def test_decode_rejects_bad_slot_on_device(g):
+    D, H = 32, 2
+    layer = g.Layer(H, H, D, torch.bfloat16)
+    q, k, v, a, b = [t.cuda() for t in gi.qkvab(2, H, H, D, torch.bfloat16, seed=61)]
+    pool = gi.states(2, H, D, seed=62).cuda()
+    before = pool.clone()
+    o = torch.zeros(2, H, D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("decode bad slot")
+    g.decode_step(layer, q, k, v, a, b, pool, torch.tensor([7, -1], dtype=torch.int32, device="cuda"), o,
+                  status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1 << 8
+    assert same_bits(pool, before)
+
+
+# ------------------------------------------------------------------------- flush
+
+@pytest.mark.parametrize("D,dtype,rows", [(128, torch.bfloat16, 32), (16, torch.float32, 32),
+                                          (64, torch.bfloat16, 64), (32, torch.bfloat16, 16)])
+def test_flush_matches_sequential_oracle(g, D, dtype, rows):
+    Hqk, Hv, n_slots = 2, 4, 6
+    layer = g.Layer(Hqk, Hv, D, dtype)
+    slots = [4, 0, 2, 5, -1, 1]
+    acc = [min(rows, x) for x in [16, 1, 17, 0, 5, rows]]
+    say(f"flush D={D} {dtype} rows={rows} acc={acc}")
+    pool = gi.states(n_slots, Hv, D, seed=71).cuda()
+    kk, vv, aa, bb = [], [], [], []
+    for s in range(n_slots):
+        _, k, v, a, b = gi.qkvab(rows, Hqk, Hv, D, dtype, seed=72 + s)
+        kk.append(k), vv.append(v), aa.append(a), bb.append(b)
+    buf_k, buf_v = torch.stack(kk).cuda(), torch.stack(vv).cuda()
+    buf_a, buf_b = torch.stack(aa).cuda(), torch.stack(bb).cuda()
+    # rejected rows hold NaN: they must never be read
+    for r, s in enumerate(slots):
+        if s >= 0:
+            n = acc[r]
+            nan_fill_(buf_k[s, n:]), nan_fill_(buf_v[s, n:]), nan_fill_(buf_a[s, n:]), nan_fill_(buf_b[s, n:])
+    before = pool.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.replay_flush(layer, pool, torch.tensor(slots, dtype=torch.int32, device="cuda"), buf_k, buf_v, buf_a, buf_b,
+                   torch.tensor(acc, dtype=torch.int32, device="cuda"), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    touched = set()
+    for r, s in enumerate(slots):
+        if s < 0:
+            continue
+        touched.add(s)
+        n = acc[r]
+        if n == 0:
+            assert same_bits(pool[s], before[s])
+            continue
+        _, S_ref, _ = oracle.recurrence(None, f64(buf_k[s, :n]), f64(buf_v[s, :n]), f64(buf_a[s, :n]),
+                                        f64(buf_b[s, :n]), 1.0, f64(before[s]), want_o=False)
+        assert rel_l2(f64(pool[s]), S_ref) <= TOL[dtype], (r, s, n)
+    for s in range(n_slots):
+        if s not in touched:
+            assert same_bits(pool[s], before[s])
+
+
+def test_flush_rejects_bad_count_on_device(g):
+    D, H = 32, 2
+    layer = g.Layer(H, H, D, torch.bfloat16)
+    pool = gi.states(2, H, D, seed=81).cuda()
+    before = pool.clone()
+    buf = torch.zeros(2, 32, H, D, dtype=torch.bfloat16, device="cuda")
+    ab = torch.full((2, 32, H), 0.5, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("flush bad count")
+    g.replay_flush(layer, pool, torch.tensor([0, 1], dtype=torch.int32, device="cuda"), buf, buf, ab, ab,
+                   torch.tensor([33, -2], dtype=torch.int32, device="cuda"), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1 << 8
+    assert same_bits(pool, before)
+
+
+# ------------------------------------------------------------------------- conv
+
+@pytest.mark.parametrize("dtype,act", [(torch.bfloat16, 1), (torch.float32, 1), (torch.bfloat16, 0)])
+def test_conv_matches_oracle_with_tails_and_checkpoints(g, dtype, act):
+    Hqk, Hv, D, block = 2, 4, 16, 16
+    layer = g.Layer(Hqk, Hv, D, dtype, conv_act=act)
+    C = layer.conv_channels
+    lens = [37, 64, 5, 2, 0, 130]
+    starts = [0, 100, 32, 7, 9, 16]
+    kinds = ["zero", "slot", "checkpoint", "slot", "slot", "checkpoint"]
+    say(f"conv {dtype} act={act} lens={lens}")
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    x, w = gi.conv_inputs(cu[-1], C, 4, dtype, seed=91)
+    tails0 = gi.conv_tail(len(lens), C, 4, dtype, seed=92)
+    n_b = [oracle.count_boundaries(s, L, block) for s, L in zip(starts, lens)]
+    pool = make_pool(g, layer, sum(n_b) + len(lens), block)
+    # checkpoint sources: the tail region of a page
+    src_pages = list(range(sum(n_b), sum(n_b) + len(lens)))
+    for i, kd in enumerate(kinds):
+        if kd == "checkpoint":
+            pool.tail_view(src_pages[i], layer).copy_(tails0[i].cuda())
+    xd, wd = x.cuda(), w.cuda()
+    td = tails0.cuda()
+    out_t = nan_fill_(torch.empty(len(lens), 3, C, dtype=dtype, device="cuda"))
+    refs = []
+    for i, kd in enumerate(kinds):
+        src = None if kd == "zero" else (td[i] if kd == "slot" else pool.page_ptr(src_pages[i]))
+        refs.append((kd, src, out_t[i]))
+    y = nan_fill_(torch.empty(cu[-1], C, dtype=dtype, device="cuda"))
+    g.conv_update(layer, xd, wd, refs, cu, starts, y, ckpt=pool, page_ids=list(range(sum(n_b))))
+    torch.cuda.synchronize()
+    off = 0
+    for i, (s, L) in enumerate(zip(starts, lens)):
+        r0 = cu[i]
+        tail_in = None if kinds[i] == "zero" else f64(tails0[i])
+        y_ref, t_ref, ck_ref = oracle.conv(f64(x[r0:r0 + L]), f64(w), tail_in, act, s, block)
+        if L:
+            if dtype == torch.bfloat16:
+                assert rel_l2(f64(y[r0:r0 + L]), oracle.bf16_round(y_ref)) <= 1e-3
+            else:
+                assert rel_l2(f64(y[r0:r0 + L]), y_ref) <= 1e-5
+        assert np.array_equal(f64(out_t[i]), t_ref), i
+        for j in range(n_b[i]):
+            assert np.array_equal(f64(pool.tail_view(off + j, layer)), ck_ref[j]), (i, j)
+        off += n_b[i]
