@@ -43,10 +43,25 @@ __device__ __forceinline__ bf16x8 row_operand(const bf16_bits* plane, int ld, in
   return lds_operand(p, p + 16);
 }
 
-// All terms of a row operand from NT planes spaced `pstride` elements apart.
-template <int NT>
+// All terms of a row operand from NT planes spaced `pstride` elements apart.  LEN is
+// the length of the contracted row: when it is not a multiple of 32 the last k-step
+// has only 16 real elements and elements 4..7 of every lane are zero (not read).
+template <int NT, int LEN = 64>
 __device__ __forceinline__ void row_operand_terms(const bf16_bits* planes, int pstride, int ld, int row,
                                                   int s, int g, bf16x8 (&out)[NT]) {
+  if constexpr (LEN % 32 != 0) {
+    if (s == LEN / 32) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const bf16_bits* p = planes + i * pstride + row * ld + 32 * s + 4 * g;
+        uint2 lo = *reinterpret_cast<const uint2*>(p);
+        typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+        u32x4 w = {lo.x, lo.y, 0u, 0u};
+        out[i] = __builtin_bit_cast(bf16x8, w);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NT; ++i) out[i] = row_operand(planes + i * pstride, ld, row, s, g);
 }
@@ -107,8 +122,8 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
 #pragma unroll
       for (int s = 0; s < KSD; ++s) {
         bf16x8 a[NTI], b[NTI];
-        row_operand_terms<NTI>(Ks, kps, KP, 16 * mt + col, s, grp, a);
-        row_operand_terms<NTI>(Ks, kps, KP, 16 * nt + col, s, grp, b);
+        row_operand_terms<NTI, D>(Ks, kps, KP, 16 * mt + col, s, grp, a);
+        row_operand_terms<NTI, D>(Ks, kps, KP, 16 * nt + col, s, grp, b);
         mma_terms<NTI, NTI, ORD>(acc, a, b);
       }
       const int sc = 16 * nt + col;
@@ -350,8 +365,8 @@ __global__ __launch_bounds__(64 * ScanShape<D>::NW) void scan_kernel(ScanArgs<IO
 #pragma unroll
           for (int s = 0; s < KSD; ++s) {
             bf16x8 a[NTI], b[NTI];
-            row_operand_terms<NTI>(Ks, CT * KP, KP, 16 * ms + col, s, grp, a);
-            row_operand_terms<NTI>(Qs, CT * KP, KP, 16 * nt + col, s, grp, b);
+            row_operand_terms<NTI, D>(Ks, CT * KP, KP, 16 * ms + col, s, grp, a);
+            row_operand_terms<NTI, D>(Qs, CT * KP, KP, 16 * nt + col, s, grp, b);
             mma_terms<NTI, NTI, ORD>(acc, a, b);
           }
         }
@@ -389,7 +404,7 @@ __global__ __launch_bounds__(64 * ScanShape<D>::NW) void scan_kernel(ScanArgs<IO
 #pragma unroll
       for (int s = 0; s < KSD; ++s) {
         bf16x8 a[NTI];
-        row_operand_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
+        row_operand_terms<NTI, D>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
         mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
       }
 #pragma unroll
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(64 * ScanShape<D>::NW) void scan_kernel(ScanArgs<IO
 #pragma unroll
         for (int s = 0; s < KSD; ++s) {
           bf16x8 a[NTI];
-          row_operand_terms<NTI>(Qs, CT * KP, KP, 16 * mt + col, s, grp, a);
+          row_operand_terms<NTI, D>(Qs, CT * KP, KP, 16 * mt + col, s, grp, a);
           mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
         }
 #pragma unroll
@@ -574,7 +589,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       bf16x8 a[NTI];
-      row_operand_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
+      row_operand_terms<NTI, D>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
       mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
     }
 #pragma unroll

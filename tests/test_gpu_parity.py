@@ -34,6 +34,7 @@ PREFILL_CASES = [
     (130, 2, 2, 32, torch.bfloat16, 0),      # no checkpoints
     (100, 1, 2, 32, torch.float32, 48),
     (257, 1, 1, 128, torch.bfloat16, 64),
+    (90, 2, 2, 16, torch.bfloat16, 32),
 ]
 
 
