@@ -1,0 +1,272 @@
+"""Benchmark of the libgdn hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Step = one pass of the prefill hot path over one 27B-shaped layer: the causal conv
+update over the packed q|k|v channels (18,432 bf16 channels, 8,192 tokens) and the
+chunked prefill of the gated delta rule (48 heads, 128 x 128 fp32 state per head,
+bf16 q/k/v, fp32 o, 64-token chunks) writing a checkpoint page at each of the nine
+896-token block boundaries.  `value` is prefill tokens per second per layer over the
+K timed steps (inputs resident in HBM, synthetic, seeded).
+
+Reported beside it, each timed with HIP events on the stream the kernels run on:
+  * the replay flush at the 4B-shaped layer (16 requests, 32 value heads x 128 x 128
+    fp32 state, a 32-slot log, accepted rows uniform in 1..16, plus all-16 and all-17),
+    rotating over enough state pools that every launch streams from HBM;
+  * the decode step for 256 requests at the 27B shape;
+  * the conv update alone;
+  * the roofline of the dominant kernel (the chunk scan);
+  * the fp64 CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Published MI355X peaks.
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+# Prefill workload: one 27B-shaped GDN layer.
+T, H, D, BLOCK, CHUNK = 8192, 48, 128, 896, 64
+PAGE_BYTES = BLOCK * 4096  # one attention page of 4,096 B per token
+
+
+def scan_algorithmic_flops(tokens, heads, d=D, c=CHUNK):
+    """Products the chunk scan performs, counted once per product (not per bf16 pass):
+    K S^T, Q S^T, the state update (2 d^2 each) and T R, P Delta, Q K^T (2 C d each),
+    per token and value head."""
+    return tokens * heads * (6 * d * d + 6 * c * d)
+
+
+def scan_bf16_pass_flops(tokens, heads, d=D, c=CHUNK):
+    """The same products as issued on the bf16 matrix cores with bf16 inputs: an fp32
+    operand is two bf16 terms, so K S^T, Q S^T and the state update take 2 passes,
+    T R and P Delta 3 passes, Q K^T 1 pass."""
+    return tokens * heads * (2 * 2 * d * d * 3 + 2 * c * d * (3 + 3 + 1))
+
+
+def flush_bytes(n_acc, heads=32, qk_heads=16, d=D):
+    """HBM bytes one flush must move: each touched state read and written once, plus
+    the accepted log rows (bf16 k, v; fp32 a, b)."""
+    state = heads * d * d * 4
+    row = qk_heads * d * 2 + heads * d * 2 + 2 * heads * 4
+    return sum(2 * state + n * row for n in n_acc if n > 0)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_recurrent_chunk_amd as g
+    import gdn_inputs as gi
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    if args.copy_calibration:
+        src = torch.ones(2 ** 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "launches": 5}), flush=True)
+        return
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    # ------------------------------------------------------------ prefill step inputs
+    layer = g.Layer(H, H, D, torch.bfloat16, scale=1.0)
+    C = layer.conv_channels
+    q, k, v, a, b = (t.to(dev) for t in gi.qkvab(T, H, H, D, torch.bfloat16, seed=1001))
+    x, w = (t.to(dev) for t in gi.conv_inputs(T, C, 4, torch.bfloat16, seed=1001))
+    y = torch.empty_like(x)
+    tail = torch.empty(3, C, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(T, H, D, dtype=torch.float32, device=dev)
+    S = torch.empty(H, D, D, dtype=torch.float32, device=dev)
+    n_ck = g.count_boundaries(0, T, BLOCK)
+    pool = g.CheckpointPool(torch.zeros(n_ck + 1, PAGE_BYTES, dtype=torch.uint8, device=dev), BLOCK)
+    page_ids = list(range(n_ck))
+    cu, sp = [0, T], [0]
+    ws = torch.empty(g.prefill_workspace_bytes(layer, cu, sp, BLOCK), dtype=torch.uint8, device=dev)
+    cws = torch.empty(g.conv_workspace_bytes(layer, cu, sp, BLOCK), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        g.conv_update(layer, x, w, [("zero", None, tail)], cu, sp, y, ckpt=pool, page_ids=page_ids, workspace=cws)
+        if ev:
+            ev[1].record()
+        g.prefill_factorize(layer, k, a, b, cu, sp, BLOCK, ws)
+        if ev:
+            ev[2].record()
+        g.prefill_scan(layer, q, k, v, cu, sp, [("zero", None, S)], o, ws, ckpt=pool, page_ids=page_ids)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = T * args.steps / elapsed
+
+    # per-kernel durations on the stream the kernels run on
+    t_conv, t_fact, t_scan = [], [], []
+    for _ in range(args.steps):
+        ev = events(4)
+        step(ev)
+        torch.cuda.synchronize()
+        t_conv.append(ev[0].elapsed_time(ev[1]))
+        t_fact.append(ev[1].elapsed_time(ev[2]))
+        t_scan.append(ev[2].elapsed_time(ev[3]))
+    scan_ms = statistics.mean(t_scan)
+    fact_ms = statistics.mean(t_fact)
+    conv_ms = statistics.mean(t_conv)
+    alg = scan_algorithmic_flops(T, H)
+    achieved_tflops = alg / (scan_ms * 1e-3) / 1e12
+
+    # ------------------------------------------------------------ replay flush (4B layer)
+    fl_layer = g.Layer(16, 32, D, torch.bfloat16)
+    n_req, rows = 16, 32
+    state_mib = n_req * 32 * D * D * 4 / 2 ** 20
+    n_pools = int(np.ceil(2 * 256 / state_mib)) + 1  # > 2 x 256 MB last-level cache in rotation
+    fpools = [gi.states(n_req, 32, D, seed=1003 + i).to(dev) for i in range(n_pools)]
+    _, bk, bv, ba, bb = gi.qkvab(n_req * rows, 16, 32, D, torch.bfloat16, seed=1003)
+    bk = bk.view(n_req, rows, 16, D).to(dev)
+    bv = bv.view(n_req, rows, 32, D).to(dev)
+    ba = ba.view(n_req, rows, 32).to(dev)
+    bb = bb.view(n_req, rows, 32).to(dev)
+    slots = torch.arange(n_req, dtype=torch.int32, device=dev)
+    acc_u = gi.accepted_counts(n_req, 1003)
+
+    def time_flush(acc, reps):
+        """Average duration of one flush launch: `reps` launches back to back between two
+        events (rotating state pools), so launch gaps do not count."""
+        acc_d = acc.to(torch.int32).to(dev)
+        for i in range(3):
+            g.replay_flush(fl_layer, fpools[i % n_pools], slots, bk, bv, ba, bb, acc_d)
+        torch.cuda.synchronize()
+        ev = events(2)
+        ev[0].record()
+        for r in range(reps):
+            g.replay_flush(fl_layer, fpools[r % n_pools], slots, bk, bv, ba, bb, acc_d)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    reps = max(100, 5 * args.steps)
+    flush_u = time_flush(acc_u, reps)
+    flush_16 = time_flush(torch.full((n_req,), 16), reps)
+    flush_17 = time_flush(torch.full((n_req,), 17), reps)
+    fb_u = flush_bytes(acc_u.tolist())
+
+    # ------------------------------------------------------------ decode (27B layer, 256 requests)
+    n_dec = 256
+    dpool = gi.states(n_dec, H, D, seed=1005).to(dev)
+    dq, dk, dv, da, db = (t.to(dev) for t in gi.qkvab(n_dec, H, H, D, torch.bfloat16, seed=1005))
+    dout = torch.empty(n_dec, H, D, dtype=torch.float32, device=dev)
+    dslots = torch.arange(n_dec, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        g.decode_step(layer, dq, dk, dv, da, db, dpool, dslots, dout)
+    torch.cuda.synchronize()
+    ev = events(2)
+    ev[0].record()
+    for _ in range(reps):
+        g.decode_step(layer, dq, dk, dv, da, db, dpool, dslots, dout)
+    ev[1].record()
+    torch.cuda.synchronize()
+    decode_us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    dec_bytes = n_dec * (2 * H * D * D * 4 + 3 * H * D * 2 + 2 * H * 4 + H * D * 4)
+
+    conv_bytes = 2 * T * C * 2
+    result = {
+        "metric": "GDN prefill tokens/s/layer (48h x 128^2, fp32 state) + flush us/layer",
+        "value": round(value, 1),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, fp32 state/outputs (bf16-split fp32 products)",
+        "data": "synthetic, seeded",
+        "config": {"workload": "prefill_27b_T8192_H48_d128_block896 (conv 18432 ch + chunked prefill, "
+                               "9 checkpoints)", "tokens": T, "heads": H, "head_dim": D, "block": BLOCK,
+                   "chunk": CHUNK},
+        "stages_ms": {"conv": round(conv_ms, 4), "factorize": round(fact_ms, 4), "scan": round(scan_ms, 4)},
+        "flush_us_per_layer": {"accepted_u1_16": round(flush_u, 2), "all_16": round(flush_16, 2),
+                               "all_17": round(flush_17, 2),
+                               "workload": "flush_4b_16req_H32_d128_32slots",
+                               "hbm_gbs_u1_16": round(fb_u / (flush_u * 1e-6) / 1e9, 1),
+                               "roof_us_u1_16": round(fb_u / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
+        "decode_us": {"value": round(decode_us, 2), "workload": "decode_27b_256req_H48_d128",
+                      "hbm_gbs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
+                      "roof_us": round(dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
+        "conv": {"us": round(conv_ms * 1e3, 2), "hbm_gbs": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1)},
+        "roofline": {
+            "kernel": "scan_kernel<bf16,128>",
+            "bound": "mfma",
+            "achieved": round(achieved_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": alg,
+            "bf16_pass_flops_per_launch": scan_bf16_pass_flops(T, H),
+            "fp32_mfma_equivalent_frac": round(achieved_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        },
+    }
+
+    # ------------------------------------------------------------ CPU oracle, bounded sample
+    if not args.no_cpu:
+        from oracle import oracle
+        # the whole prefill workload (all tokens, all heads), run repeatedly until about
+        # 10 s of CPU time have passed; the median run gives the rate
+        qs, ks, vs, as_, bs = (t.float().double().cpu().numpy() for t in (q, k, v, a, b))
+        threads = min(os.cpu_count() or 1, 16)
+        runs = []
+        while sum(runs) < 10.0 and len(runs) < 50:
+            t1 = time.perf_counter()
+            oracle.recurrence(qs, ks, vs, as_, bs, 1.0, None, 0, BLOCK, threads=threads)
+            runs.append(time.perf_counter() - t1)
+        cpu_s = statistics.median(runs)
+        result["cpu_baseline"] = {"value": round(T / cpu_s, 1), "unit": "tokens/s/layer",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"the full prefill workload ({T} tokens x {H} heads, checkpoints "
+                                            f"every {BLOCK}), fp64 token loop, median of {len(runs)} runs "
+                                            f"({round(cpu_s, 3)} s each)"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

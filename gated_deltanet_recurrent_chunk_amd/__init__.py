@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the computation runs in the HIP kernels of
 ``libgdn.so`` behind the C ABI declared in ``include/gdn.h``.  PyTorch supplies device
 memory and the current stream.  Importing this module loads the library and fails
-loudly when it has not been built (``python -m gated_deltanet_recurrent_chunk_amd.build``).
+loudly when it has not been built (``python gated_deltanet_recurrent_chunk_amd/build.py``).
 
 Layouts (token-major, packed over a varlen batch), as in ``include/gdn.h``:
   q, k  [tokens, n_qk_heads, d]  (or rows of a wider packed tensor, see ``qk_stride``)
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libgdn.so not found at {LIB_PATH}; build it with "
-        "`python -m gated_deltanet_recurrent_chunk_amd.build` (there is no CPU fallback)")
+        "`python gated_deltanet_recurrent_chunk_amd/build.py` (there is no CPU fallback)")
 _lib = ctypes.CDLL(LIB_PATH)
 
 GDN_F32, GDN_BF16 = 0, 1

@@ -1,6 +1,8 @@
 """Build libgdn.so (gfx950) in-tree with hipcc.
 
-    python -m gated_deltanet_recurrent_chunk_amd.build [--verbose]
+    python gated_deltanet_recurrent_chunk_amd/build.py [--verbose]
+
+(run by path: importing the package loads the library this script builds)
 
 Objects go to gated_deltanet_recurrent_chunk_amd/_build/, the library to
 gated_deltanet_recurrent_chunk_amd/libgdn.so.
@@ -17,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["plan.cpp", "gdn_api.cpp", "chunk_kernels.hip", "stream_kernels.hip"]
+SOURCES = ["plan.cpp", "gdn_api.cpp", "prefill_kernels.hip", "flush_kernel.hip", "stream_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", os.path.join(ROOT, "include"),

@@ -1,0 +1,180 @@
+// flush_kernel.hip -- the replay flush ("Caching less to serve more requests", section
+// "What we changed"): each request keeps one state plus a log of its per-token inputs
+// since it; the flush folds the first n accepted rows of the log into the state as one
+// block of the chunked gated delta rule (chunk_common.h), one launch for all requests.
+// The state is read once and written once; logged rows at or past n are never read.
+#include <hip/hip_runtime.h>
+
+#include "chunk_common.h"
+#include "device_common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace gdn {
+
+using namespace chunk;
+
+// ==================================================================================
+// Replay flush: one workgroup per (request, value head), one wave per 16-row slab of
+// the state.  Reads the state once, factorizes the accepted rows (wave 0), applies
+// them, writes the state once.
+template <typename IO, int D, int CT>
+__global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
+  constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
+  constexpr int NW = D / 16, NTH = 64 * NW;
+  constexpr int KP = row_stride(D), TP = row_stride(CT), VP = D + 4;
+  constexpr int DT = D / 16, KSD = (D + 31) / 32;
+  constexpr int MT = CT / 16, KST = (MT + 1) / 2;
+  constexpr int VEC = 16 / sizeof(IO);
+  constexpr int PER_ROW = D / VEC;
+
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
+  __shared__ __attribute__((aligned(16))) bf16_bits KTs[NTI * D * TP];
+  __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
+  __shared__ float As[CT][CT + 4];
+  __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
+  __shared__ __attribute__((aligned(16))) float vec[4 * CT];
+  __shared__ float vec_tmp[2 * CT];
+
+  const int r_ = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int slot = p.slot_ids[r_];
+  const int n = p.n_accepted[r_];
+  if (slot < -1 || slot >= p.n_slots || n < 0 || n > p.buf_rows) {
+    if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
+    return;
+  }
+  if (slot < 0 || n == 0) return;  // padding or nothing accepted: untouched
+
+  const int hk = h / p.group;
+  const int my_row = wave * 16 + col;
+  float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
+  f32x4 S[DT];
+#pragma unroll
+  for (int jt = 0; jt < DT; ++jt)
+    S[jt] = *reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp);
+
+  if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), tid, NTH);
+  __syncthreads();
+  // logged rows 0..n-1 of this slot
+  const size_t row0 = (size_t)slot * p.buf_rows;
+  const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
+  const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
+  for (int idx = tid; idx < CT * PER_ROW; idx += NTH) {
+    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    uint4 kv = load16(kb + (size_t)t * p.Hqk * D + j0, t < n);
+    store_row_terms<IO, NTI>(kv, Ks, CT * KP, KP, t, j0);
+    uint4 vv = load16(vb + (size_t)t * p.Hv * D + j0, t < n);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv, e);
+  }
+  __syncthreads();
+  transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
+  if (wave == 0) {
+    float la = 0.f, bb = 0.f;
+    if (lane < n) {
+      const size_t ai = (row0 + lane) * p.Hv + h;
+      la = __logf(p.buf_a[ai]);
+      bb = p.buf_b[ai];
+    }
+    const float g = wave_inclusive_scan(la);
+    factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, n, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
+  } else {
+    // match the barriers inside factorize_chunk
+    __syncthreads();
+    __syncthreads();
+  }
+  __syncthreads();
+
+  bf16x8 Sop[KSD][NTF];
+#pragma unroll
+  for (int s = 0; s < KSD; ++s) reg_operand<NTF>(S[2 * s], (2 * s + 1 < DT) ? S[2 * s + 1] : zero4(), Sop[s]);
+
+  f32x4 R[2 * KST];
+#pragma unroll
+  for (int mt = 0; mt < 2 * KST; ++mt) {
+    R[mt] = zero4();
+    if (mt >= MT) continue;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      bf16x8 a[NTI];
+      op_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
+      mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * mt + 4 * grp + r;
+      float val = 0.f;
+      if (t < n) val = vec[2 * CT + t] * (Vs[t * VP + my_row] - vec[CT + t] * acc[r]);
+      R[mt][r] = val;
+    }
+  }
+  bf16x8 Rop[KST][NTF];
+#pragma unroll
+  for (int s = 0; s < KST; ++s) reg_operand<NTF>(R[2 * s], R[2 * s + 1], Rop[s]);
+  f32x4 Dt[2 * KST];
+#pragma unroll
+  for (int mt = 0; mt < 2 * KST; ++mt) {
+    Dt[mt] = zero4();
+    if (mt >= MT) continue;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s <= (mt >> 1); ++s) {
+      bf16x8 a[NTF];
+      op_terms<NTF>(Ts, CT * TP, TP, 16 * mt + col, s, grp, a);
+      mma_terms<NTF, NTF, ORD>(acc, a, Rop[s]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Dt[mt][r] = vec[3 * CT + 16 * mt + 4 * grp + r] * acc[r];
+  }
+  bf16x8 Dtop[KST][NTF];
+#pragma unroll
+  for (int s = 0; s < KST; ++s) reg_operand<NTF>(Dt[2 * s], Dt[2 * s + 1], Dtop[s]);
+  const float egn = vec[CT + n - 1];
+#pragma unroll
+  for (int jt = 0; jt < DT; ++jt) {
+    f32x4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = egn * S[jt][r];
+#pragma unroll
+    for (int s = 0; s < KST; ++s) {
+      bf16x8 a[NTI];
+      op_terms<NTI>(KTs, D * TP, TP, 16 * jt + col, s, grp, a);
+      mma_terms<NTI, NTF, ORD>(acc, a, Dtop[s]);
+    }
+    *reinterpret_cast<f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp) = acc;
+  }
+}
+
+template <typename IO, int D>
+static hipError_t launch_flush_t(const FlushArgs<IO>& a, int n_req, int ct, hipStream_t st) {
+  if (n_req == 0) return hipSuccess;
+  dim3 grid(n_req, a.Hv);
+  if (ct <= 32)
+    hipLaunchKernelGGL((flush_kernel<IO, D, 32>), grid, dim3(64 * (D / 16)), 0, st, a);
+  else
+    hipLaunchKernelGGL((flush_kernel<IO, D, 64>), grid, dim3(64 * (D / 16)), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_flush_t<bf16_bits, 16>(a, n_req, ct, st);
+    case 32: return launch_flush_t<bf16_bits, 32>(a, n_req, ct, st);
+    case 64: return launch_flush_t<bf16_bits, 64>(a, n_req, ct, st);
+    case 128: return launch_flush_t<bf16_bits, 128>(a, n_req, ct, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, int ct, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_flush_t<float, 16>(a, n_req, ct, st);
+    case 32: return launch_flush_t<float, 32>(a, n_req, ct, st);
+    case 64: return launch_flush_t<float, 64>(a, n_req, ct, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gdn

@@ -36,6 +36,7 @@ gdn_status check_layer(const gdn_layer* layer, LayerInfo* out) {
     L.ckpt_bytes = (int64_t)align_up((size_t)(L.state_bytes + L.tail_bytes));
     // bf16 inputs: fp32 operands as two bf16 terms; fp32 inputs: three terms
     L.ntf = l.io_dtype == GDN_BF16 ? 2 : 3;
+    L.nti = l.io_dtype == GDN_BF16 ? 1 : 3;
   }
   return GDN_OK;
 }
@@ -172,7 +173,7 @@ void plan_prefill(const LayerInfo& L, const std::vector<SeqSpan>& spans, int32_t
   plan->off_chunks = 0;
   plan->off_seqs = align_up(n_chunks * sizeof(ChunkDesc));
   plan->off_factors = plan->off_seqs + align_up(spans.size() * sizeof(ScanSeq));
-  plan->factor_stride = factor_record_bytes(L.ntf);
+  plan->factor_stride = factor_record_bytes(L.ntf, L.nti, L.D);
   plan->total_bytes = plan->off_factors + plan->factor_stride * n_chunks * (size_t)L.Hv;
   if (plan->total_bytes == 0) plan->total_bytes = kAlign;
 }

@@ -72,6 +72,7 @@ struct LayerInfo {
   int64_t tail_bytes;
   int64_t ckpt_bytes;
   int ntf;          // bf16 terms carried by fp32 operands in matrix products
+  int nti;          // bf16 terms carried by an input operand (1 for bf16 inputs)
 };
 
 gdn_status check_layer(const gdn_layer* layer, LayerInfo* out);
@@ -111,10 +112,13 @@ struct ConvPlan {
 };
 void plan_conv(const std::vector<SeqSpan>& spans, size_t n_pages, ConvPlan* plan);
 
-// Bytes of the per-(chunk, head) factor record: ntf planes of kChunk x kChunk bf16
-// (the inverse of I + A, split into bf16 terms) and four fp32 vectors of kChunk.
-inline size_t factor_record_bytes(int ntf) {
-  return align_up((size_t)ntf * kChunk * kChunk * 2 + 4 * kChunk * 4);
+// Bytes of the per-(chunk, value head) factor record written by the prefill pre-pass:
+// the inverse T of (I + A) as 6 x ntf MFMA operand fragments of 1 KiB (the six
+// (row tile, k-step) pairs of its lower triangle, ntf bf16 terms each), nti planes of
+// d x kChunk bf16 (the chunk's keys transposed) and four fp32 vectors of kChunk.
+constexpr size_t factor_record_bytes_c(int ntf, int nti, int d) {
+  return ((size_t)6 * ntf * 1024 + (size_t)nti * d * kChunk * 2 + 4 * kChunk * 4 + kAlign - 1) / kAlign * kAlign;
 }
+inline size_t factor_record_bytes(int ntf, int nti, int d) { return factor_record_bytes_c(ntf, nti, d); }
 
 }  // namespace gdn
