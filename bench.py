@@ -120,7 +120,7 @@ def main():
         g.conv_update(layer, x, w, [("zero", None, tail)], cu, sp, y, ckpt=pool, page_ids=page_ids, workspace=cws)
         if ev:
             ev[1].record()
-        g.prefill_factorize(layer, k, a, b, cu, sp, BLOCK, ws)
+        g.prefill_factorize(layer, q, k, a, b, cu, sp, BLOCK, ws)
         if ev:
             ev[2].record()
         g.prefill_scan(layer, q, k, v, cu, sp, [("zero", None, S)], o, ws, ckpt=pool, page_ids=page_ids)

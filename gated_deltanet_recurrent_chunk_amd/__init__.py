@@ -83,7 +83,7 @@ _decl("gdn_conv_workspace_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
 _decl("gdn_conv_update", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz])
 _decl("gdn_chunk_prefill", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
                                   _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz])
-_decl("gdn_prefill_factorize", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _i64, _vp, _vp, _i32, _vp, _sz])
+_decl("gdn_prefill_factorize", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _i64, _vp, _vp, _i32, _vp, _sz])
 _decl("gdn_prefill_scan", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _P(_StateRef),
                                  _P(_Ckpt), _vp, _vp, _sz])
 _decl("gdn_decode_step", _i32, [_P(_Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp])
@@ -344,14 +344,15 @@ def chunk_prefill(layer: Layer, q, k, v, a, b, cu_seqlens, start_pos, states, o,
     return ws
 
 
-def prefill_factorize(layer: Layer, k, a, b, cu_seqlens, start_pos, block, workspace, stream=None,
+def prefill_factorize(layer: Layer, q, k, a, b, cu_seqlens, start_pos, block, workspace, stream=None,
                       qk_stride=None):
     vl = _Varlens(cu_seqlens, start_pos)
     qs = qk_stride if qk_stride is not None else layer.n_qk_heads * layer.head_dim
-    _check_prefill_operands(layer, cu_seqlens, start_pos, None, k, None, a, b, None,
+    _check_prefill_operands(layer, cu_seqlens, start_pos, q, k, None, a, b, None,
                             [("zero", None, None)] * len(start_pos), qs, 0)
-    st = _lib.gdn_prefill_factorize(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(vl.c), _ptr(k), qs,
-                                    _ptr(a), _ptr(b), int(block), _ptr(workspace), workspace.numel())
+    st = _lib.gdn_prefill_factorize(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(vl.c), _ptr(q),
+                                    _ptr(k), qs, _ptr(a), _ptr(b), int(block), _ptr(workspace),
+                                    workspace.numel())
     _check(st, "gdn_prefill_factorize")
 
 

@@ -277,16 +277,20 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
 #endif
 }
 
-// A chunk descriptor read as wave-uniform values, so that the address arithmetic built
-// on it stays on the scalar unit.
+// A chunk descriptor read through the constant address space: a wave-uniform address
+// there becomes a scalar load (SMEM, counted by lgkmcnt), so waiting for it never waits
+// for the vector loads in flight, and the fields land in SGPRs.  The table is not
+// written while a kernel runs.
 __device__ __forceinline__ ChunkDesc uniform_chunk(const ChunkDesc* cdp) {
-  const ChunkDesc cd = *cdp;
-  ChunkDesc u;
-  u.row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(cd.row >> 32)) << 32) |
-                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cd.row));
-  u.len = __builtin_amdgcn_readfirstlane(cd.len);
-  u.page = __builtin_amdgcn_readfirstlane(cd.page);
-  return u;
+  const auto* cp = (const __attribute__((address_space(4))) ChunkDesc*)cdp;
+  ChunkDesc d;
+  d.row = cp->row;
+  d.len = cp->len;
+  d.page = cp->page;
+  return d;
+}
+__device__ __forceinline__ float uniform_load(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
 }
 
 // Compiler-only fence between phases of a chunk: memory accesses are not moved across

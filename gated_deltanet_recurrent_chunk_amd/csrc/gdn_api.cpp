@@ -96,8 +96,14 @@ gdn_status check_qkv(const LayerInfo& L, const void* q, const void* k, const voi
   if (!aligned(k, 16) || (need_q && !aligned(q, 16)) || (need_v && !aligned(v, 16))) return GDN_ERR_BAD_SHAPE;
   if (qk_stride < (int64_t)L.Hqk * L.D || qk_stride % vec != 0) return GDN_ERR_BAD_SHAPE;
   if (need_v && (v_stride < (int64_t)L.Hv * L.D || v_stride % vec != 0)) return GDN_ERR_BAD_SHAPE;
-  // the chunk kernels stage fp32 inputs as three bf16 terms in LDS: head_dim <= 64
+  // fp32 inputs enter the matrix products as three bf16 terms; the registers of the
+  // chunk kernels hold them for head_dim <= 64
   if (L.io == GDN_F32 && L.D > 64) return GDN_ERR_BAD_SHAPE;
+  // the scan addresses one chunk of rows with 32-bit byte offsets
+  const int64_t lim = (int64_t)INT32_MAX / kChunk;
+  if (qk_stride * (int64_t)L.io_bytes > lim || (need_v && v_stride * (int64_t)L.io_bytes > lim) ||
+      (int64_t)L.Hv * L.D * 4 > lim)
+    return GDN_ERR_BAD_SHAPE;
   return GDN_OK;
 }
 
@@ -131,10 +137,11 @@ gdn_status check_workspace(void* ws, size_t ws_bytes, size_t need) {
 }
 
 template <typename IO>
-gdn_status do_factorize(const PrefillPrep& P, hipStream_t stream, const void* k, int64_t qk_stride,
+gdn_status do_factorize(const PrefillPrep& P, hipStream_t stream, const void* q, const void* k, int64_t qk_stride,
                         const float* a, const float* b, void* ws) {
   FactorizeArgs<IO> fa;
   fa.chunks = reinterpret_cast<const ChunkDesc*>(static_cast<uint8_t*>(ws) + P.plan.off_chunks);
+  fa.q = static_cast<const IO*>(q);
   fa.k = static_cast<const IO*>(k);
   fa.qk_stride = qk_stride;
   fa.a = a;
@@ -144,6 +151,7 @@ gdn_status do_factorize(const PrefillPrep& P, hipStream_t stream, const void* k,
   fa.n_chunks = (int32_t)P.plan.chunks.size();
   fa.Hv = P.L.Hv;
   fa.group = P.L.Hv / P.L.Hqk;
+  fa.scale = P.L.scale;
   return hip_status(launch_factorize(fa, P.L.D, fa.n_chunks, stream));
 }
 
@@ -162,13 +170,13 @@ gdn_status do_scan(const PrefillPrep& P, hipStream_t stream, const void* q, cons
   sa.factors = w + P.plan.off_factors;
   sa.factor_stride = P.plan.factor_stride;
   sa.n_chunks = (int32_t)P.plan.chunks.size();
+  sa.n_seqs = (int32_t)P.spans.size();
   sa.Hv = P.L.Hv;
   sa.group = P.L.Hv / P.L.Hqk;
-  sa.scale = P.L.scale;
   sa.o = o;
   sa.ckpt_pool = static_cast<uint8_t*>(ckpt->pool);
   sa.page_bytes = (size_t)ckpt->page_bytes;
-  return hip_status(launch_scan(sa, P.L.D, (int)P.spans.size(), stream));
+  return hip_status(launch_scan(sa, P.L.D, stream));
 }
 
 // Host image of the chunk table and, when states != null, of the sequence table.
@@ -280,12 +288,12 @@ int64_t gdn_conv_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varle
 }
 
 gdn_status gdn_prefill_factorize(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
-                                 const void* k, int64_t qk_stride, const float* a, const float* b, int32_t block,
-                                 void* workspace, size_t workspace_bytes) {
+                                 const void* q, const void* k, int64_t qk_stride, const float* a, const float* b,
+                                 int32_t block, void* workspace, size_t workspace_bytes) {
   PrefillPrep P;
   gdn_status s = prep_prefill(layer, varlen, block, nullptr, &P);
   if (s != GDN_OK) return s;
-  s = check_qkv(P.L, nullptr, k, nullptr, qk_stride, 0, false, false);
+  s = check_qkv(P.L, q, k, nullptr, qk_stride, 0, true, false);
   if (s != GDN_OK) return s;
   if (!P.plan.chunks.empty() && (!a || !b)) return GDN_ERR_NULL_ARG;
   s = check_workspace(workspace, workspace_bytes, P.plan.total_bytes);
@@ -293,8 +301,8 @@ gdn_status gdn_prefill_factorize(const gdn_layer* layer, hipStream_t stream, con
   std::vector<uint8_t> tab = prefill_tables(P, nullptr, false);
   s = hip_status(upload(workspace, tab.data(), tab.size(), stream));
   if (s != GDN_OK) return s;
-  return P.L.io == GDN_BF16 ? do_factorize<bf16_bits>(P, stream, k, qk_stride, a, b, workspace)
-                            : do_factorize<float>(P, stream, k, qk_stride, a, b, workspace);
+  return P.L.io == GDN_BF16 ? do_factorize<bf16_bits>(P, stream, q, k, qk_stride, a, b, workspace)
+                            : do_factorize<float>(P, stream, q, k, qk_stride, a, b, workspace);
 }
 
 gdn_status gdn_prefill_scan(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen, const void* q,
@@ -338,11 +346,11 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream, const g
   s = hip_status(upload(workspace, tab.data(), tab.size(), stream));
   if (s != GDN_OK) return s;
   if (P.L.io == GDN_BF16) {
-    s = do_factorize<bf16_bits>(P, stream, k, qk_stride, a, b, workspace);
+    s = do_factorize<bf16_bits>(P, stream, q, k, qk_stride, a, b, workspace);
     if (s != GDN_OK) return s;
     return do_scan<bf16_bits>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
   }
-  s = do_factorize<float>(P, stream, k, qk_stride, a, b, workspace);
+  s = do_factorize<float>(P, stream, q, k, qk_stride, a, b, workspace);
   if (s != GDN_OK) return s;
   return do_scan<float>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
 }

@@ -10,15 +10,10 @@ namespace gdn {
 
 typedef uint16_t bf16_bits;
 
-// Workgroup shape of the scan: up to four 16-row waves per (sequence, head) group.
-template <int D>
-struct ScanShape {
-  static constexpr int NW = D >= 64 ? 4 : D / 16;
-};
-
 template <typename IO>
 struct FactorizeArgs {
   const ChunkDesc* chunks;
+  const IO* q;
   const IO* k;
   int64_t qk_stride;  // elements per token row of q and k
   const float* a;
@@ -28,6 +23,7 @@ struct FactorizeArgs {
   int32_t n_chunks;
   int32_t Hv;
   int32_t group;  // value heads per query/key head
+  float scale;
 };
 
 template <typename IO>
@@ -42,9 +38,9 @@ struct ScanArgs {
   const uint8_t* factors;
   size_t factor_stride;
   int32_t n_chunks;
+  int32_t n_seqs;
   int32_t Hv;
   int32_t group;
-  float scale;
   float* o;
   uint8_t* ckpt_pool;
   size_t page_bytes;
@@ -103,8 +99,8 @@ struct ConvArgs {
 
 hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, int n_chunks, hipStream_t st);
 hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, int n_chunks, hipStream_t st);
-hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, int n_seqs, hipStream_t st);
-hipError_t launch_scan(const ScanArgs<float>& a, int D, int n_seqs, hipStream_t st);
+hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, hipStream_t st);
+hipError_t launch_scan(const ScanArgs<float>& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st);
 hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, int ct, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs<bf16_bits>& a, int D, int n_req, hipStream_t st);

@@ -112,12 +112,16 @@ struct ConvPlan {
 };
 void plan_conv(const std::vector<SeqSpan>& spans, size_t n_pages, ConvPlan* plan);
 
-// Bytes of the per-(chunk, value head) factor record written by the prefill pre-pass:
-// the inverse T of (I + A) as 6 x ntf MFMA operand fragments of 1 KiB (the six
-// (row tile, k-step) pairs of its lower triangle, ntf bf16 terms each), nti planes of
-// d x kChunk bf16 (the chunk's keys transposed) and four fp32 vectors of kChunk.
+// Bytes of the per-(chunk, value head) factor record written by the prefill pre-pass.
+// Every matrix in it is stored as ready-made MFMA A-operand fragments of 1 KiB (16
+// bytes per lane of a 64-lane wave), ntf (or nti) bf16 terms each:
+//   T = (I + A)^-1: 6 fragments x ntf (the (row tile, k-step) pairs of its lower triangle)
+//   P = scale * exp(g_t - g_s) q_t.k_s (s <= t): 6 x ntf, same pairs
+//   K^T: (d / 16) row tiles x 2 k-steps x nti
+// then four fp32 row vectors of kChunk and one fp32 chunk scalar (16 bytes).
 constexpr size_t factor_record_bytes_c(int ntf, int nti, int d) {
-  return ((size_t)6 * ntf * 1024 + (size_t)nti * d * kChunk * 2 + 4 * kChunk * 4 + kAlign - 1) / kAlign * kAlign;
+  return ((size_t)12 * ntf * 1024 + (size_t)(d / 16) * 2 * nti * 1024 + 4 * kChunk * 4 + 16 + kAlign - 1) /
+         kAlign * kAlign;
 }
 inline size_t factor_record_bytes(int ntf, int nti, int d) { return factor_record_bytes_c(ntf, nti, d); }
 

@@ -1,13 +1,17 @@
 // prefill_kernels.hip -- chunked varlen prefill of the gated delta rule on gfx950.
 //
 // Two kernels (the chunk algebra is stated in chunk_common.h):
-//   factorize_kernel: for every (chunk, value head) at once, the state-free factors of
-//     the chunk: the cumulative log decay g, T = (I + A)^-1 (the WY / UT transform of
-//     the chunk), and the chunk's keys transposed.  T is written as ready-made MFMA A
-//     operand fragments, K^T in the LDS image layout the scan copies by DMA.
-//   scan_kernel: one workgroup per (sequence, value head, 64 value rows), one wave per
-//     16-row slab of the state, walking the sequence's chunks in order with the slab in
-//     registers.  Rows of the state are independent, so the slabs never exchange data.
+//   factorize_kernel: one wave per (chunk, value head), all of them at once.  Computes
+//     everything about a chunk that does not depend on the state: the gate vectors,
+//     T = (I + A)^-1 (the WY / UT transform), the causal decayed scores
+//     P = scale * exp(g_t - g_s) q_t.k_s (s <= t) and the keys transposed.  The three
+//     matrices are written as ready-made MFMA A-operand fragments (1 KiB each, 16 bytes
+//     per lane) into one record per (value head, chunk).
+//   scan_kernel: one workgroup per (sequence, value head, 16-row slab of the state),
+//     walking the sequence's chunks in order with its slab in registers.  Rows of the
+//     state evolve independently, so the slabs never exchange data; for head dim >= 64
+//     the slab's key columns are split over two waves, which add their partial
+//     contractions through LDS.
 //
 // Chunks are cut at every multiple of 64 tokens, of the cache block and at the call
 // ends (plan.cpp); when a chunk ends on a block boundary the scan stores the bits of
@@ -16,11 +20,12 @@
 // keeps the recurrent state after its last token), so a resume from the page computes
 // exactly what the cold run computes after that point.
 //
-// Scan data flow per chunk (bf16 inputs, head dim 64 or 128): K, Q and K^T of chunk
-// c + 1 are copied global -> LDS by LDS DMA (global_load_lds) into the second of two
-// buffers while chunk c is computed; T fragments and this wave's V column come straight
-// into registers one chunk ahead.  Two barriers per chunk: one after the DMA lands, one
-// after the causal Q K^T tiles (shared by the four waves through LDS) are written.
+// Scan memory access.  Every load and store of the chunk loop is a buffer instruction
+// whose descriptor (SGPRs) holds the chunk's base address and its length in bytes; the
+// per-lane offsets are fixed for the whole kernel.  Rows past the end of a ragged chunk
+// fall outside the descriptor's range, so the hardware returns zeros for them and drops
+// their stores: they are excluded by selection, never read, never written.  Each phase
+// of a chunk requests the operands of the next phase before it computes.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.h"
@@ -36,30 +41,118 @@ namespace {
 
 constexpr int CT = kChunk;
 
-// The (row tile mt, k-step s) pairs of the 64 x 64 lower triangular T that the
-// Delta = T R product reads (k-steps above the diagonal are all zero and skipped).
+// The (row tile mt, k-step s) pairs of a 64 x 64 lower triangular matrix whose k-steps
+// are not all zero: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
 constexpr int kFragCombos = 6;
 __host__ __device__ constexpr int frag_combo(int mt, int s) { return mt < 2 ? mt : 2 + 2 * (mt - 2) + s; }
 
 template <typename IO, int D>
 struct PrefillCfg {
   static constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
-  static constexpr int KRB = 2 * phys_width(D);  // bytes per row of a K / Q plane
-  static constexpr int KPL = CT * KRB / 2;         // elements per K / Q plane
-  static constexpr int TRB = 2 * CT;               // bytes per row of a K^T / P plane
-  static constexpr int KTPL = D * CT;              // elements per K^T plane
-  static constexpr int PPL = CT * CT;              // elements per P plane
-  // factor record: [T fragments][K^T planes][g, exp g, b, exp(g_n - g)]
-  static constexpr int FRAG_BYTES = kFragCombos * NTF * 1024;
-  static constexpr int KT_BYTES = NTI * KTPL * 2;
-  static constexpr int VEC_OFF = FRAG_BYTES + KT_BYTES;
-  static constexpr int REC_BYTES = VEC_OFF + 4 * CT * 4;
+  static constexpr int DT = D / 16;
+  // factor record: [T fragments][P fragments][K^T fragments][row vectors][chunk scalar]
+  static constexpr int T_OFF = 0;
+  static constexpr int P_OFF = kFragCombos * NTF * 1024;
+  static constexpr int KT_OFF = 2 * kFragCombos * NTF * 1024;
+  static constexpr int VEC_OFF = KT_OFF + DT * 2 * NTI * 1024;
+  // row vector planes (kChunk floats each): b, b exp(g), scale exp(g), exp(g_n - g)
+  static constexpr int V_B = 0, V_BEG = 1, V_EGS = 2, V_EDEC = 3;
+  static constexpr int EGN_OFF = VEC_OFF + 4 * CT * 4;  // exp(g_n)
+  static constexpr int REC_BYTES = EGN_OFF + 16;
+  static_assert(REC_BYTES <= (int)factor_record_bytes_c(NTF, NTI, D), "factor record layout");
 };
 
-}  // namespace
+// ---------------------------------------------------------------- buffer access
+typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-static_assert(PrefillCfg<bf16_bits, 128>::REC_BYTES <= (int)factor_record_bytes_c(2, 1, 128), "record size");
-static_assert(PrefillCfg<float, 64>::REC_BYTES <= (int)factor_record_bytes_c(3, 3, 64), "record size");
+// Raw buffer descriptor: base, length in bytes (accesses at or past it read 0 and
+// write nothing), 32-bit data format (gfx9 word 3).  Both are wave-uniform; they are
+// passed through readfirstlane so that a value the compiler happened to compute on
+// the vector unit still lands in SGPRs (a descriptor in VGPRs costs a waterfall loop
+// around every access).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x2 ld8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, soff, 0));
+}
+__device__ __forceinline__ f32x4 ld16f(rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(f32x4, ld16(r, off, soff));
+}
+__device__ __forceinline__ bf16x8 ld16h(rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(bf16x8, ld16(r, off, soff));
+}
+template <typename IO>
+__device__ __forceinline__ float ld_elem(rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(IO) == 2)
+    return bf16_to_f32((bf16_bits)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+  else
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void st4(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+
+// Key-column order of the scan's registers.  Register position (state tile jt, lane
+// group g, element r) holds key column kcol(jt, g) + r.  For d >= 32 this makes the 8
+// contraction elements a lane supplies at k-step s (tiles 2s and 2s+1, see the kappa
+// order in device_common.h) the 8 adjacent columns 32 s + 8 g .. + 7 of a key or query
+// row: one 16-byte load.  d = 16 keeps the natural order 4 g + r.
+template <int D>
+__host__ __device__ constexpr int kcol(int jt, int g) {
+  return D >= 32 ? 32 * (jt >> 1) + 8 * g + 4 * (jt & 1) : 4 * g;
+}
+
+// One A-operand load of a row-major input matrix (K or Q rows) in the kcol order.
+// off: byte offset of this lane's row and first column.  bf16 inputs are one exact
+// term; fp32 inputs are kept raw and split at use.
+template <typename IO>
+struct RowOp;
+template <>
+struct RowOp<bf16_bits> {
+  bf16x8 v;
+};
+template <>
+struct RowOp<float> {
+  f32x4 lo, hi;
+};
+
+template <typename IO, int D>
+__device__ __forceinline__ RowOp<IO> load_row_op(rsrc_t r, uint32_t off, int s) {
+  RowOp<IO> o;
+  if constexpr (sizeof(IO) == 2) {
+    if constexpr (D >= 32) {
+      o.v = ld16h(r, off + 64 * s, 0);
+    } else {
+      const u32x2 lo = ld8(r, off);
+      o.v = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], 0u, 0u});
+    }
+  } else {
+    o.lo = ld16f(r, off + 128 * s, 0);
+    o.hi = D >= 32 ? ld16f(r, off + 128 * s + 16, 0) : zero4();
+  }
+  return o;
+}
+template <int NT>
+__device__ __forceinline__ void row_terms(const RowOp<bf16_bits>& o, bf16x8 (&t)[NT]) {
+  static_assert(NT == 1, "bf16 rows are one term");
+  t[0] = o.v;
+}
+template <int NT>
+__device__ __forceinline__ void row_terms(const RowOp<float>& o, bf16x8 (&t)[NT]) {
+  reg_operand<NT>(o.lo, o.hi, t);
+}
+
+}  // namespace
 
 // ==================================================================================
 // Pre-pass: one wave per (chunk, value head).
@@ -68,25 +161,40 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
   using Cfg = PrefillCfg<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
   constexpr int KP = row_stride(D), TP = row_stride(CT);
+  constexpr int KSD = (D + 31) / 32, DT = D / 16;
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int PER_ROW = D / VEC;
-  __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
-  __shared__ float As[CT][CT + 4];
-  __shared__ __attribute__((aligned(16))) bf16_bits Tl[NTF * CT * TP];
+  constexpr int KS_BYTES = NTI * CT * KP * 2, TL_BYTES = NTF * CT * TP * 2, AS_BYTES = CT * (CT + 4) * 4;
+  constexpr int L0_BYTES = KS_BYTES > TL_BYTES ? KS_BYTES : TL_BYTES;
+  constexpr int L1_BYTES = KS_BYTES > AS_BYTES ? KS_BYTES : AS_BYTES;
+  // L0: key rows, later T; L1: query rows, later A
+  __shared__ __attribute__((aligned(16))) uint8_t L0[L0_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t L1[L1_BYTES];
+  __shared__ float gl[CT];
+  __shared__ float vec_tmp[4 * CT];
   __shared__ float vec_lds[2 * CT];
+  bf16_bits* Ks = reinterpret_cast<bf16_bits*>(L0);
+  bf16_bits* Qs = reinterpret_cast<bf16_bits*>(L1);
+  bf16_bits* Tl = reinterpret_cast<bf16_bits*>(L0);
+  auto As = reinterpret_cast<float (*)[CT + 4]>(L1);
 
   const int c = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int grp = lane >> 4, col = lane & 15;
   const ChunkDesc cd = p.chunks[c];
   const int n = cd.len;
   const int hk = h / p.group;
-  if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), lane, 64);
+  if constexpr (D < 32) {
+    // the kappa groups past a 16-wide row are contracted: keep them zero
+    zero_lds(L0, L0_BYTES, lane, 64);
+    zero_lds(L1, L1_BYTES, lane, 64);
+  }
   __syncthreads();
   const IO* kb = p.k + cd.row * p.qk_stride + (int64_t)hk * D;
+  const IO* qb = p.q + cd.row * p.qk_stride + (int64_t)hk * D;
   for (int idx = lane; idx < CT * PER_ROW; idx += 64) {
     const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    uint4 v = load16(kb + (int64_t)t * p.qk_stride + j0, t < n);
-    store_row_terms<IO, NTI>(v, Ks, CT * KP, KP, t, j0);
+    store_row_terms<IO, NTI>(load16(kb + (int64_t)t * p.qk_stride + j0, t < n), Ks, CT * KP, KP, t, j0);
+    store_row_terms<IO, NTI>(load16(qb + (int64_t)t * p.qk_stride + j0, t < n), Qs, CT * KP, KP, t, j0);
   }
   float la = 0.f, bb = 0.f;
   if (lane < n) {
@@ -94,13 +202,88 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
     la = __logf(p.a[ai]);
     bb = p.b[ai];
   }
-  const float g = wave_inclusive_scan(la);
-  uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
-  float* vec_out = reinterpret_cast<float*>(rec + Cfg::VEC_OFF);
-  factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, n, g, bb, Tl, CT * TP, TP, vec_out, vec_lds);
+  const float g = wave_inclusive_scan(la);  // rows past n keep g_{n-1}
+  gl[lane] = g;
   __syncthreads();
+  uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
 
-  // T as A-operand fragments: fragment (combo, term) holds lane l's 16 bytes at l * 16
+  // ---- P fragments.  Tile (ms, mt) of P^T = K Q^T has the C layout "lane (col, grp)
+  //      holds P[16 mt + col][16 ms + 4 grp + r]", i.e. elements 0..3 (ms = 2s) or 4..7
+  //      (ms = 2s + 1) of the A operand of P for (mt, s).
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int s = 0; s <= (mt >> 1); ++s) {
+      const bool two = 2 * s + 1 <= mt;  // tile 2s+1 lies above the diagonal otherwise
+      f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        bf16x8 bq[NTI], a0[NTI], a1[NTI];
+        op_terms<NTI>(Qs, CT * KP, KP, 16 * mt + col, ks, grp, bq);
+        op_terms<NTI>(Ks, CT * KP, KP, 32 * s + col, ks, grp, a0);
+        mma_terms<NTI, NTI, ORD>(acc0, a0, bq);
+        if (two) {
+          op_terms<NTI>(Ks, CT * KP, KP, 32 * s + 16 + col, ks, grp, a1);
+          mma_terms<NTI, NTI, ORD>(acc1, a1, bq);
+        }
+      }
+      const int t = 16 * mt + col;
+      const float gt = gl[t];
+      bf16_bits tt[8][NTF];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sp = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
+        const float dot = e < 4 ? acc0[e] : acc1[e - 4];
+        float val = 0.f;
+        if (sp <= t && t < n && (e < 4 || two)) val = p.scale * __expf(gt - gl[sp]) * dot;
+        split_terms<NTF>(val, tt[e]);
+      }
+#pragma unroll
+      for (int i = 0; i < NTF; ++i) {
+        bf16_bits v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
+        *reinterpret_cast<bf16x8*>(rec + Cfg::P_OFF + (frag_combo(mt, s) * NTF + i) * 1024 + lane * 16) =
+            pack8(v8);
+      }
+    }
+  }
+
+  // ---- K^T fragments: A operand of the state update.  Row col of tile jt is the key
+  //      column the scan keeps at register position (jt, col / 4, col % 4), kcol order;
+  //      contraction over the chunk rows t = kappa(s, grp, e).
+#pragma unroll
+  for (int jt = 0; jt < DT; ++jt) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < NTI; ++i) {
+        bf16_bits v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
+          v8[e] = Ks[i * CT * KP + t * KP + swz(kcol<D>(jt, col >> 2) + (col & 3))];
+        }
+        *reinterpret_cast<bf16x8*>(rec + Cfg::KT_OFF + ((jt * 2 + s) * NTI + i) * 1024 + lane * 16) = pack8(v8);
+      }
+    }
+  }
+
+  // ---- row vectors and exp(g_n)
+  {
+    const float gn = __shfl(g, n - 1, 64);
+    const float eg = __expf(g);
+    float* vo = reinterpret_cast<float*>(rec + Cfg::VEC_OFF);
+    vo[Cfg::V_B * CT + lane] = bb;
+    vo[Cfg::V_BEG * CT + lane] = bb * eg;
+    vo[Cfg::V_EGS * CT + lane] = p.scale * eg;
+    vo[Cfg::V_EDEC * CT + lane] = lane < n ? __expf(gn - g) : 0.f;
+    if (lane == 0) *reinterpret_cast<float*>(rec + Cfg::EGN_OFF) = __expf(gn);
+  }
+
+  // ---- T = (I + A)^-1 (reads the key rows, then overwrites them with T)
+  factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, n, g, bb, Tl, CT * TP, TP, vec_tmp, vec_lds);
+  __syncthreads();
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -108,350 +291,302 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
 #pragma unroll
       for (int i = 0; i < NTF; ++i) {
         const bf16x8 v = op_read(Tl + i * CT * TP, TP, 16 * mt + col, s, grp);
-        *reinterpret_cast<bf16x8*>(rec + ((size_t)frag_combo(mt, s) * NTF + i) * 1024 + lane * 16) = v;
+        *reinterpret_cast<bf16x8*>(rec + Cfg::T_OFF + (frag_combo(mt, s) * NTF + i) * 1024 + lane * 16) = v;
       }
     }
-  }
-  // K^T planes in the xor layout: row j, kappa-ordered columns t, 4 per 8-byte store
-  bf16_bits* KTout = reinterpret_cast<bf16_bits*>(rec + Cfg::FRAG_BYTES);
-  for (int task = lane; task < NTI * D * (CT / 4); task += 64) {
-    const int i = task / (D * (CT / 4));
-    const int rem = task % (D * (CT / 4));
-    const int j = rem / (CT / 4), t0 = (rem % (CT / 4)) * 4;
-    const bf16_bits* src = Ks + i * CT * KP + swz(j);
-    const uint32_t w0 = (uint32_t)src[(t0 + 0) * KP] | ((uint32_t)src[(t0 + 1) * KP] << 16);
-    const uint32_t w1 = (uint32_t)src[(t0 + 2) * KP] | ((uint32_t)src[(t0 + 3) * KP] << 16);
-    *reinterpret_cast<uint2*>(KTout + i * Cfg::KTPL + xrun<Cfg::TRB>(j, swz(t0))) = uint2{w0, w1};
   }
 }
 
 // ==================================================================================
-// Scan.
+// Scan: one workgroup per (sequence, value head, slab of 16 value rows), NSP waves.
+//
+// With NSP = 2 (head dim >= 64) the key columns of the slab are split between the two
+// waves: each keeps its half of the state, forms its half of the contractions
+// X = K S^T and Y = Q S^T over the key index, and the two halves are added through
+// LDS (one barrier per chunk; fp addition is commutative, so both waves hold the same
+// bits).  Both waves then form R and Delta = T R; each updates its half of the state
+// and writes half of the output rows.
+//
+// Register layouts (lane = 16 grp + col):
+//   state    S[j][r]  = S[16 slab + col][kcol(jt, grp) + r], jt = DTH w + j  (C layout of
+//            S^T tiles)
+//   X = K S^T, Y = Q S^T, R, Delta, O: [mt][r] = M[16 mt + 4 grp + r][16 slab + col]
+// Per chunk:
+//   A: X, Y            (K, Q rows and the state split into bf16 terms)
+//   B: R = b V - b exp(g) X;  Delta = T R
+//   C: O = scale exp(g) Y + P Delta   (stored)
+//   D: S^T <- exp(g_n) S^T + K^T (exp(g_n - g) o Delta);  checkpoint
+template <int D>
+struct ScanSplit {
+  static constexpr int NSP = D >= 64 ? 2 : 1;
+};
+
 template <typename IO, int D>
-__global__ __launch_bounds__(64 * ScanShape<D>::NW) void scan_kernel(ScanArgs<IO> p) {
+__global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<IO> p) {
   using Cfg = PrefillCfg<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
-  constexpr int NW = ScanShape<D>::NW, RW = 16 * NW, NTH = 64 * NW;
-  constexpr int DT = D / 16, KSD = (D + 31) / 32;
-  constexpr int KRB = Cfg::KRB, KPL = Cfg::KPL, TRB = Cfg::TRB, KTPL = Cfg::KTPL, PPL = Cfg::PPL;
+  constexpr int DT = D / 16, KSD = (D + 31) / 32, NS = D / 16;
+  constexpr int NSP = ScanSplit<D>::NSP;
+  constexpr int KSH = KSD / NSP, DTH = DT / NSP;  // k-steps and state tiles per wave
+  constexpr int MR = 4 / NSP;                     // output row tiles per wave
   constexpr int ESZ = sizeof(IO);
-  constexpr int VRB = RW * ESZ;          // bytes per row of the V slice (xor layout)
-  constexpr int REC = Cfg::REC_BYTES;    // the factor record is copied whole
-  // bf16 inputs with 128-byte or wider key rows: LDS DMA with double buffering
-  constexpr bool DMA = ESZ == 2 && D >= 64;
-  constexpr int NBUF = DMA ? 2 : 1;
-  constexpr int VEC = 16 / ESZ;
-  constexpr int PER_ROW = D / VEC, PER_VROW = RW / VEC;
+  static_assert(KSH * NSP == KSD && DTH * NSP == DT, "key split");
 
-  __shared__ __attribute__((aligned(16))) bf16_bits Kb[NBUF][NTI * KPL];
-  __shared__ __attribute__((aligned(16))) bf16_bits Qb[NBUF][NTI * KPL];
-  __shared__ __attribute__((aligned(16))) uint8_t Vb[NBUF][CT * VRB];
-  __shared__ __attribute__((aligned(16))) uint8_t Rb[NBUF][REC];  // T fragments, K^T, vectors
-  __shared__ __attribute__((aligned(16))) bf16_bits Ps[NTF * PPL];
+  // partial sums exchanged between the two waves: [chunk parity][wave][X 0..3, Y 4..7][lane]
+  __shared__ f32x4 xch[NSP == 2 ? 2 * 2 * 8 * 64 : 1];
 
-  const int seq = blockIdx.x, h = blockIdx.y, rg = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address math
-  const int grp = lane >> 4, col = lane & 15;
+  // All slabs of one (sequence, head) go to the same XCD (workgroups are dealt to the
+  // eight XCDs round robin), so their shared chunk operands meet in one L2.
+  const int blk = blockIdx.x;
+  const int u = (blk / (8 * NS)) * 8 + (blk & 7);
+  const int sl = (blk >> 3) % NS;
+  if (u >= p.n_seqs * p.Hv) return;
+  const int seq = u / p.Hv, h = u - seq * p.Hv;
   const int hk = h / p.group;
-  const int i0 = rg * RW;               // first value row of the workgroup
-  const ScanSeq sq = p.seqs[seq];
-  const size_t head_off = (size_t)h * D * D;
-  const int vcol = wave * 16 + col;     // this lane's column in the V slice
-  const int my_row = i0 + vcol;         // value row held by this lane
+  const int w = NSP == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int my_row = 16 * sl + col;
+  const auto* sqp = (const __attribute__((address_space(4))) ScanSeq*)(p.seqs + seq);  // scalar loads
+  const ScanSeq sq{sqp->src, sqp->dst, sqp->chunk_begin, sqp->chunk_end, 0, 0};
   const int cb = sq.chunk_begin, ce = sq.chunk_end;
+  const size_t head_off = (size_t)h * D * D;
+  const int jt0 = DTH * w, s0 = KSH * w;  // first state tile and k-step of this wave
+  const int mt0 = MR * w;                 // first output row tile of this wave
 
-  if constexpr (D < 32) {
-    // the kappa groups past a 16-wide key row are contracted: keep them zero
-    zero_lds(Kb, sizeof(Kb), tid, NTH);
-    zero_lds(Qb, sizeof(Qb), tid, NTH);
-  }
-
-  // ---- incoming state slab: lane holds S[my_row][16 jt + 4 grp + r]
-  f32x4 S[DT];
+  f32x4 S[DTH];
 #pragma unroll
-  for (int jt = 0; jt < DT; ++jt) {
+  for (int j = 0; j < DTH; ++j) {
     if (sq.src)
-      S[jt] = *reinterpret_cast<const f32x4*>(sq.src + head_off + (size_t)my_row * D + 16 * jt + 4 * grp);
+      S[j] = *reinterpret_cast<const f32x4*>(sq.src + head_off + (size_t)my_row * D + kcol<D>(jt0 + j, grp));
     else
-      S[jt] = zero4();
+      S[j] = zero4();
+  }
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int j = 0; j < DTH; ++j) *reinterpret_cast<f32x4*>(dst + kcol<D>(jt0 + j, grp)) = S[j];
+  };
+  if (cb >= ce) {
+    store_state(sq.dst + head_off + (size_t)my_row * D);
+    return;
   }
 
-  // ---- DMA source offsets (elements) of this lane, one per xor key its rows take
-  constexpr int LPR = KRB / 4, RPI = 64 / LPR;          // key rows: lanes per row, rows per DMA
-  constexpr int VLPR = VRB / 4, VRPI = 64 / VLPR;       // V rows
-  // the xor key of a row repeats every 16 rows (xkey), so a wave striding NW * RPI rows
-  // sees 16 / (NW * RPI) distinct keys
-  constexpr int KCYC = DMA ? 16 / (NW * RPI) : 1;
-  constexpr int VCYC = DMA ? 16 / (NW * VRPI) : 1;
-  const int rsub = lane / LPR, vsub = lane / VLPR;
-  uint32_t koff[KCYC], voff[VCYC];  // byte offsets from the row-group base
-  if constexpr (DMA) {
-    const int d = lane % LPR, vd = lane % VLPR;
+  // ---- per-lane byte offsets, fixed for the kernel
+  const uint32_t qsb = (uint32_t)p.qk_stride * ESZ, vsb = (uint32_t)p.v_stride * ESZ;
+  const uint32_t osb = (uint32_t)p.Hv * D * 4;
+  uint32_t kq_off[4], v_off[4], o_off[4];
 #pragma unroll
-    for (int k = 0; k < KCYC; ++k) {
-      const int t = wave * RPI + k * NW * RPI + rsub;
-      koff[k] = ESZ * (rsub * (uint32_t)p.qk_stride + unswz(8 * ((d >> 2) ^ xkey<KRB>(t)) + 2 * (d & 3)));
-    }
-#pragma unroll
-    for (int k = 0; k < VCYC; ++k) {
-      const int t = wave * VRPI + k * NW * VRPI + vsub;
-      voff[k] = ESZ * (vsub * (uint32_t)p.v_stride + 8 * ((vd >> 2) ^ xkey<VRB>(t)) + 2 * (vd & 3));
-    }
+  for (int i = 0; i < 4; ++i) {
+    kq_off[i] = (16 * i + col) * qsb + kcol<D>(0, grp) * ESZ;
+    v_off[i] = (4 * grp + i) * vsb + col * ESZ;
+    o_off[i] = (4 * grp + i) * osb + col * 4;
   }
+  const uint32_t frag_lane = 16 * lane;
+  const uint32_t vec_lane = 16 * grp;  // + 64 mt: rows 16 mt + 4 grp .. + 3 of a vector plane
 
-  // ---- per-chunk operands staged in LDS: K, Q rows, the V slice, the factor record
-  auto stage = [&](int c, int buf) {
-    const ChunkDesc cd = uniform_chunk(p.chunks + c);
-    const int n = cd.len;
-    const IO* kb = p.k + cd.row * p.qk_stride + (int64_t)hk * D;
-    const IO* qb = p.q + cd.row * p.qk_stride + (int64_t)hk * D;
-    const IO* vb = p.v + cd.row * p.v_stride + (int64_t)h * D + i0;
-    const uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
-    if constexpr (DMA) {
-      // one dword DMA per key row (two V rows): the lane owning physical dword d of row t
-      // reads the logical columns the xor / kappa layout places there.  The rows of one
-      // wave cycle through KCYC (VCYC) xor keys, so the per-lane source offsets are
-      // precomputed (koff, voff) and each DMA is a uniform row address plus that offset.
-#pragma nounroll
-      for (int k = 0; k < CT / (NW * RPI); ++k) {
-        const int t0 = wave * RPI + k * NW * RPI;
-        if (t0 >= n) break;
-        if (t0 + RPI <= n || t0 + rsub < n) {
-          const uint32_t off = koff[k % KCYC];
-          lds_dma4(reinterpret_cast<const char*>(kb + (int64_t)t0 * p.qk_stride) + off, &Kb[buf][t0 * (KRB / 2)]);
-          lds_dma4(reinterpret_cast<const char*>(qb + (int64_t)t0 * p.qk_stride) + off, &Qb[buf][t0 * (KRB / 2)]);
-        }
-      }
-#pragma nounroll
-      for (int k = 0; k < CT / (NW * VRPI); ++k) {
-        const int t0 = wave * VRPI + k * NW * VRPI;
-        if (t0 >= n) break;
-        if (t0 + VRPI <= n || t0 + vsub < n)
-          lds_dma4(reinterpret_cast<const char*>(vb + (int64_t)t0 * p.v_stride) + voff[k % VCYC], &Vb[buf][t0 * VRB]);
-      }
-#pragma nounroll
-      for (int u = wave; u < REC / 1024; u += NW) lds_dma16(rec + u * 1024 + lane * 16, &Rb[buf][u * 1024]);
-    } else {
-      for (int idx = tid; idx < CT * PER_ROW; idx += NTH) {
-        const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-        xstore_row_terms<IO, NTI, KRB>(load16(kb + (int64_t)t * p.qk_stride + j0, t < n), Kb[buf], KPL, t, j0);
-        xstore_row_terms<IO, NTI, KRB>(load16(qb + (int64_t)t * p.qk_stride + j0, t < n), Qb[buf], KPL, t, j0);
-      }
-      for (int idx = tid; idx < CT * PER_VROW; idx += NTH) {
-        const int t = idx / PER_VROW, pc = idx % PER_VROW;  // one 16-byte piece
-        *reinterpret_cast<uint4*>(&Vb[buf][t * VRB + 16 * (pc ^ xkey<VRB>(t))]) =
-            load16(vb + (int64_t)t * p.v_stride + pc * VEC, t < n);
-      }
-      for (int idx = tid; idx < REC / 16; idx += NTH)
-        reinterpret_cast<uint4*>(Rb[buf])[idx] = reinterpret_cast<const uint4*>(rec)[idx];
-    }
+  auto rec_rsrc = [&](int c) {
+    return make_rsrc(p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
   };
 
-  if constexpr (DMA) {
-    if (cb < ce) stage(cb, 0);
-  }
+  // ---- operands of one chunk
+  RowOp<IO> Kop[4][KSH], Qop[4][KSH];
+  float Vv[4][4];
+  f32x4 vb[4], vbeg[4], vegs[MR], vedec[4];
+  bf16x8 Tf[kFragCombos][NTF], Pf[MR][2][NTF], KTf[DTH][2][NTI];
+  float egn;
 
+  auto load_A = [&](const ChunkDesc& cd) {
+    const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
+    const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
+#pragma unroll
+    for (int s = 0; s < KSH; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        Kop[mt][s] = load_row_op<IO, D>(rk, kq_off[mt], s0 + s);
+        Qop[mt][s] = load_row_op<IO, D>(rq, kq_off[mt], s0 + s);
+      }
+  };
+  auto load_B = [&](const ChunkDesc& cd, int c) {
+    // one descriptor for the chunk's rows: the tile row goes into the offset, so the
+    // descriptor's length bounds every row
+    const rsrc_t rv = make_rsrc(p.v + cd.row * p.v_stride + (int64_t)h * D + 16 * sl, (uint32_t)cd.len * vsb);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Vv[mt][r] = ld_elem<IO>(rv, v_off[r] + 16 * mt * vsb);
+    const rsrc_t rr = rec_rsrc(c);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      vb[mt] = ld16f(rr, vec_lane + 64 * mt, Cfg::VEC_OFF + Cfg::V_B * CT * 4);
+      vbeg[mt] = ld16f(rr, vec_lane + 64 * mt, Cfg::VEC_OFF + Cfg::V_BEG * CT * 4);
+    }
+#pragma unroll
+    for (int f = 0; f < kFragCombos; ++f)
+#pragma unroll
+      for (int i = 0; i < NTF; ++i) Tf[f][i] = ld16h(rr, frag_lane, Cfg::T_OFF + (f * NTF + i) * 1024);
+  };
+  auto load_C = [&](int c) {
+    const rsrc_t rr = rec_rsrc(c);
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const int mt = mt0 + i;
+      vegs[i] = ld16f(rr, vec_lane, Cfg::VEC_OFF + Cfg::V_EGS * CT * 4 + 64 * mt);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s <= (mt >> 1))
+#pragma unroll
+          for (int t = 0; t < NTF; ++t)
+            Pf[i][s][t] = ld16h(rr, frag_lane, Cfg::P_OFF + (frag_combo(mt, s) * NTF + t) * 1024);
+    }
+  };
+  auto load_D = [&](int c) {
+    const rsrc_t rr = rec_rsrc(c);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) vedec[mt] = ld16f(rr, vec_lane + 64 * mt, Cfg::VEC_OFF + Cfg::V_EDEC * CT * 4);
+#pragma unroll
+    for (int j = 0; j < DTH; ++j)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < NTI; ++i)
+          KTf[j][s][i] = ld16h(rr, frag_lane, Cfg::KT_OFF + (((jt0 + j) * 2 + s) * NTI + i) * 1024);
+    egn = uniform_load(reinterpret_cast<const float*>(p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride +
+                                                      Cfg::EGN_OFF));
+  };
+
+  // The loads of a phase are issued where they are written: the scheduler may not sink
+  // them below the computation that follows (which would cost the lookahead).
+  auto issue_point = [] { __builtin_amdgcn_sched_barrier(0); };
+
+  // One phase of lookahead: each phase first requests the operands of the next one
+  // (the last phase those of the next chunk's first), then computes.  About 20-40
+  // vector loads are in flight at a time, within the 63 the wave's counter tracks.
+  ChunkDesc cur = uniform_chunk(p.chunks + cb);
+  load_A(cur);
+
+#pragma unroll 1
   for (int c = cb; c < ce; ++c) {
-    const int buf = DMA ? ((c - cb) & 1) : 0;
-    const ChunkDesc cd = uniform_chunk(p.chunks + c);
-    const int n = cd.len;
-    if constexpr (DMA) {
-      full_barrier();  // chunk c's DMA has landed; every wave is done with chunk c - 1
-      if (c + 1 < ce) stage(c + 1, buf ^ 1);
-    } else {
-      lds_barrier();   // every wave is done with chunk c - 1
-      stage(c, 0);
-      lds_barrier();
-    }
-    const bf16_bits* Ks = Kb[buf];
-    const bf16_bits* Qs = Qb[buf];
-    const uint8_t* Vs = Vb[buf];
-    const bf16_bits* frag = reinterpret_cast<const bf16_bits*>(Rb[buf]);
-    const bf16_bits* KTs = reinterpret_cast<const bf16_bits*>(Rb[buf] + Cfg::FRAG_BYTES);
-    const float* vec = reinterpret_cast<const float*>(Rb[buf] + Cfg::VEC_OFF);
+    // the next chunk (the last one loads itself again: in bounds, and unused)
+    const int cn = __builtin_amdgcn_readfirstlane(c + 1 < ce ? c + 1 : c);
+    const ChunkDesc nxt = uniform_chunk(p.chunks + cn);
 
-    // ---- P = mask o exp(g_t - g_s) (Q K^T), as P^T = K Q^T tiles (M = s, N = t): the
-    //      C layout of a P^T tile is the A-operand layout of P.  Twelve tiles (the ten
-    //      causal ones and the two upper ones the P Delta k-steps touch, all zero) are
-    //      shared out over the waves and exchanged through LDS.
-    {
-      // tile it -> (ms, nt), two bits each: ms = 0,0,1,0,1,2,0,1,2,3,1,3  nt = 0,1,1,2,2,2,3,3,3,3,0,2
-      constexpr int NPT = 12, TPW = (NPT + NW - 1) / NW;
-      constexpr uint32_t MS_CODE = 0u | (0u << 2) | (1u << 4) | (0u << 6) | (1u << 8) | (2u << 10) | (0u << 12) |
-                                   (1u << 14) | (2u << 16) | (3u << 18) | (1u << 20) | (3u << 22);
-      constexpr uint32_t NT_CODE = 0u | (1u << 2) | (1u << 4) | (2u << 6) | (2u << 8) | (2u << 10) | (3u << 12) |
-                                   (3u << 14) | (3u << 16) | (3u << 18) | (0u << 20) | (2u << 22);
-      f32x4 pacc[TPW];
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) pacc[u] = zero4();
-#pragma unroll
-      for (int s = 0; s < KSD; ++s) {
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const int it = wave + u * NW;
-          const int ms = (MS_CODE >> (2 * it)) & 3, nt = (NT_CODE >> (2 * it)) & 3;
-          if (it < NPT && ms <= nt) {
-            bf16x8 a[NTI], b[NTI];
-            xop_terms<KRB, NTI>(Ks, KPL, 16 * ms + col, s, grp, a);
-            xop_terms<KRB, NTI>(Qs, KPL, 16 * nt + col, s, grp, b);
-            mma_terms<NTI, NTI, ORD>(pacc[u], a, b);
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        const int it = wave + u * NW;
-        if (it < NPT) {
-          const int ms = (MS_CODE >> (2 * it)) & 3, nt = (NT_CODE >> (2 * it)) & 3;
-          const int t = 16 * nt + col;
-          const float gt = vec[t];
-          bf16_bits terms[4][NTF];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int s = 16 * ms + 4 * grp + r;
-            float val = 0.f;
-            if (s <= t && t < n) val = __expf(gt - vec[s]) * pacc[u][r];
-            split_terms<NTF>(val, terms[r]);
-          }
-          const int off = xrun<TRB>(t, swz(16 * ms + 4 * grp));
-#pragma unroll
-          for (int i = 0; i < NTF; ++i)
-            *reinterpret_cast<uint2*>(Ps + i * PPL + off) =
-                uint2{(uint32_t)terms[0][i] | ((uint32_t)terms[1][i] << 16),
-                      (uint32_t)terms[2][i] | ((uint32_t)terms[3][i] << 16)};
-        }
-      }
-    }
-
-    // ---- X = K S^T and Y = Q S^T together: eight independent accumulator chains; the
-    //      state operand terms of each k-step are formed just before use
-    phase_fence();
+    // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains
+    load_B(cur, c);
+    issue_point();
     f32x4 X[4], Y[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) X[mt] = Y[mt] = zero4();
 #pragma unroll
-    for (int s = 0; s < KSD; ++s) {
+    for (int s = 0; s < KSH; ++s) {
       bf16x8 sop[NTF];
-      reg_operand<NTF>(S[2 * s], (2 * s + 1 < DT) ? S[2 * s + 1] : zero4(), sop);
-      bf16x8 ak[4][NTI], aq[4][NTI];
+      reg_operand<NTF>(S[2 * s], (2 * s + 1 < DTH) ? S[2 * s + 1] : zero4(), sop);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        xop_terms<KRB, NTI>(Ks, KPL, 16 * mt + col, s, grp, ak[mt]);
-        xop_terms<KRB, NTI>(Qs, KPL, 16 * mt + col, s, grp, aq[mt]);
+        bf16x8 ak[NTI], aq[NTI];
+        row_terms<NTI>(Kop[mt][s], ak);
+        row_terms<NTI>(Qop[mt][s], aq);
+        mma_terms<NTI, NTF, ORD>(X[mt], ak, sop);
+        mma_terms<NTI, NTF, ORD>(Y[mt], aq, sop);
       }
+    }
+    // this wave's output rows of Y
+    f32x4 Ym[MR];
+    if constexpr (NSP == 1) {
+#pragma unroll
+      for (int i = 0; i < MR; ++i) Ym[i] = Y[i];
+    } else {
+      f32x4* mine = xch + (((c & 1) * 2 + w) * 8) * 64 + lane;
+      f32x4* other = xch + (((c & 1) * 2 + (w ^ 1)) * 8) * 64 + lane;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        mma_terms<NTI, NTF, ORD>(X[mt], ak[mt], sop);
-        mma_terms<NTI, NTF, ORD>(Y[mt], aq[mt], sop);
+        mine[mt * 64] = X[mt];
+        mine[(4 + mt) * 64] = Y[mt];
       }
-      phase_fence();
+      lds_barrier();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 xo = other[mt * 64];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X[mt][r] += xo[r];
+      }
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        const f32x4 ya = mine[(4 + mt0 + i) * 64], yb = other[(4 + mt0 + i) * 64];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ym[i][r] = ya[r] + yb[r];
+      }
     }
 
-    // ---- R = b (V - exp(g) X), rows past n selected to zero
+    // ---- B: R = b V - b exp(g) X (zero past the chunk end: b = 0 there, V and X read
+    //      as zeros), Delta = T R over the nonzero k-steps of T
+    load_C(c);
+    issue_point();
     f32x4 R[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mt + 4 * grp + r;
-        const int vb = vcol * ESZ;
-        const float vt = to_f32(*reinterpret_cast<const IO*>(Vs + t * VRB + 16 * ((vb >> 4) ^ xkey<VRB>(t)) + (vb & 15)));
-        R[mt][r] = t < n ? vec[2 * CT + t] * (vt - vec[CT + t] * X[mt][r]) : 0.f;
-      }
+      for (int r = 0; r < 4; ++r) R[mt][r] = fmaf(-vbeg[mt][r], X[mt][r], vb[mt][r] * Vv[mt][r]);
     bf16x8 Rop[2][NTF];
     reg_operand<NTF>(R[0], R[1], Rop[0]);
     reg_operand<NTF>(R[2], R[3], Rop[1]);
-    phase_fence();
-
-    // ---- Delta = T R  (T fragments from LDS; upper k-steps skipped)
     f32x4 Dl[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) Dl[mt] = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int mt = 2 * s; mt < 4; ++mt) {
-        bf16x8 a[NTF];
-#pragma unroll
-        for (int i = 0; i < NTF; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(frag + (frag_combo(mt, s) * NTF + i) * 512 + lane * 8);
-        mma_terms<NTF, NTF, ORD>(Dl[mt], a, Rop[s]);
-      }
+      for (int mt = 2 * s; mt < 4; ++mt) mma_terms<NTF, NTF, ORD>(Dl[mt], Tf[frag_combo(mt, s)], Rop[s]);
 
-    bf16x8 Dop[2][NTF];
-    reg_operand<NTF>(Dl[0], Dl[1], Dop[0]);
-    reg_operand<NTF>(Dl[2], Dl[3], Dop[1]);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Y[mt][r] *= vec[CT + 16 * mt + 4 * grp + r];
-
-    lds_barrier();  // P tiles from all waves are in LDS
-
-    // ---- O = scale (exp(g) Q S^T + P Delta); stored before the state update so the
-    //      stores drain while it runs
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int mt = 2 * s; mt < 4; ++mt) {
-        bf16x8 a[NTF];
-        xop_terms<TRB, NTF>(Ps, PPL, 16 * mt + col, s, grp, a);
-        mma_terms<NTF, NTF, ORD>(Y[mt], a, Dop[s]);
-      }
+    // ---- C: O = scale exp(g) Y + (scale P) Delta for this wave's row tiles
+    load_D(c);
+    issue_point();
     {
-      float* ob = p.o + (size_t)cd.row * p.Hv * D + (size_t)h * D + my_row;
-      const size_t orow = (size_t)p.Hv * D;
+      bf16x8 Dop[2][NTF];
+      reg_operand<NTF>(Dl[0], Dl[1], Dop[0]);
+      reg_operand<NTF>(Dl[2], Dl[3], Dop[1]);
+      const rsrc_t ro = make_rsrc(p.o + cur.row * (int64_t)p.Hv * D + (int64_t)h * D + 16 * sl, (uint32_t)cur.len * osb);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int i = 0; i < MR; ++i) {
+        const int mt = mt0 + i;
+        f32x4 acc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * mt + 4 * grp + r;
-          if (t < n) ob[(size_t)t * orow] = p.scale * Y[mt][r];
-        }
+        for (int r = 0; r < 4; ++r) acc[r] = Ym[i][r] * vegs[i][r];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Dop[s]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st4(ro, o_off[r] + 16 * mt * osb, acc[r]);
+      }
     }
 
-    // ---- S^T <- exp(g_n) S^T + K^T (exp(g_n - g) o Delta): DT independent chains
-    phase_fence();
+    // ---- D: S^T <- exp(g_n) S^T + K^T (exp(g_n - g) o Delta) for this wave's tiles
+    load_A(nxt);
+    issue_point();
     {
       f32x4 Dt[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Dt[mt][r] = vec[3 * CT + 16 * mt + 4 * grp + r] * Dl[mt][r];
+        for (int r = 0; r < 4; ++r) Dt[mt][r] = vedec[mt][r] * Dl[mt][r];
       bf16x8 Dtop[2][NTF];
       reg_operand<NTF>(Dt[0], Dt[1], Dtop[0]);
       reg_operand<NTF>(Dt[2], Dt[3], Dtop[1]);
-      const float egn = vec[CT + n - 1];
 #pragma unroll
-      for (int jt = 0; jt < DT; ++jt)
+      for (int j = 0; j < DTH; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[jt][r] *= egn;
+        for (int r = 0; r < 4; ++r) S[j][r] *= egn;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 a[DT][NTI];
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int jt = 0; jt < DT; ++jt) xop_terms<TRB, NTI>(KTs, KTPL, 16 * jt + col, s, grp, a[jt]);
-#pragma unroll
-        for (int jt = 0; jt < DT; ++jt) mma_terms<NTI, NTF, ORD>(S[jt], a[jt], Dtop[s]);
-        phase_fence();
-      }
+        for (int j = 0; j < DTH; ++j) mma_terms<NTI, NTF, ORD>(S[j], KTf[j][s], Dtop[s]);
     }
 
     // ---- checkpoint: the state after this chunk, bit for bit
-    if (cd.page >= 0) {
-      float* dst = reinterpret_cast<float*>(p.ckpt_pool + (size_t)cd.page * p.page_bytes) + head_off +
-                   (size_t)my_row * D;
-#pragma unroll
-      for (int jt = 0; jt < DT; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt + 4 * grp) = S[jt];
-    }
+    if (cur.page >= 0)
+      store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)cur.page * p.page_bytes) + head_off +
+                  (size_t)my_row * D);
+    cur = nxt;
   }
-
-  {
-    float* dst = sq.dst + head_off + (size_t)my_row * D;
-#pragma unroll
-    for (int jt = 0; jt < DT; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt + 4 * grp) = S[jt];
-  }
+  store_state(sq.dst + head_off + (size_t)my_row * D);
 }
 
 // ==================================================================================
@@ -465,11 +600,12 @@ static hipError_t launch_factorize_t(const FactorizeArgs<IO>& a, int n_chunks, h
 }
 
 template <typename IO, int D>
-static hipError_t launch_scan_t(const ScanArgs<IO>& a, int n_seqs, hipStream_t st) {
-  if (n_seqs == 0) return hipSuccess;
-  constexpr int NW = ScanShape<D>::NW;
-  dim3 grid(n_seqs, a.Hv, D / (16 * NW));
-  hipLaunchKernelGGL((scan_kernel<IO, D>), grid, dim3(64 * NW), 0, st, a);
+static hipError_t launch_scan_t(const ScanArgs<IO>& a, hipStream_t st) {
+  const int64_t units = (int64_t)a.n_seqs * a.Hv;
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + 7) / 8 * 8 * (D / 16);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((scan_kernel<IO, D>), dim3((unsigned)blocks), dim3(64 * ScanSplit<D>::NSP), 0, st, a);
   return hipGetLastError();
 }
 
@@ -490,20 +626,20 @@ hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, int n_chunks, 
     default: return hipErrorInvalidValue;
   }
 }
-hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, int n_seqs, hipStream_t st) {
+hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, hipStream_t st) {
   switch (D) {
-    case 16: return launch_scan_t<bf16_bits, 16>(a, n_seqs, st);
-    case 32: return launch_scan_t<bf16_bits, 32>(a, n_seqs, st);
-    case 64: return launch_scan_t<bf16_bits, 64>(a, n_seqs, st);
-    case 128: return launch_scan_t<bf16_bits, 128>(a, n_seqs, st);
+    case 16: return launch_scan_t<bf16_bits, 16>(a, st);
+    case 32: return launch_scan_t<bf16_bits, 32>(a, st);
+    case 64: return launch_scan_t<bf16_bits, 64>(a, st);
+    case 128: return launch_scan_t<bf16_bits, 128>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
-hipError_t launch_scan(const ScanArgs<float>& a, int D, int n_seqs, hipStream_t st) {
+hipError_t launch_scan(const ScanArgs<float>& a, int D, hipStream_t st) {
   switch (D) {
-    case 16: return launch_scan_t<float, 16>(a, n_seqs, st);
-    case 32: return launch_scan_t<float, 32>(a, n_seqs, st);
-    case 64: return launch_scan_t<float, 64>(a, n_seqs, st);
+    case 16: return launch_scan_t<float, 16>(a, st);
+    case 32: return launch_scan_t<float, 32>(a, st);
+    case 64: return launch_scan_t<float, 64>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

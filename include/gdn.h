@@ -222,16 +222,19 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream,
 
 /* The two stages of gdn_chunk_prefill, for callers that schedule or time them apart.
  * gdn_prefill_factorize computes, for every chunk and value head, the state-free
- * chunk factors (the cumulative log-decay and the inverse of the unit lower
- * triangular key-interaction matrix, the WY / UT transform of the chunk) into the
- * workspace.  gdn_prefill_scan then walks each sequence chunk by chunk and applies
+ * chunk factors into the workspace: the gate vectors from the cumulative log-decay,
+ * the inverse of the unit lower triangular key-interaction matrix (the WY / UT
+ * transform of the chunk), the causal decayed query-key scores and the keys
+ * transposed.  gdn_prefill_scan then walks each sequence chunk by chunk and applies
  * them to the state.  The scan must run on the same stream after a factorize with the
- * same layer, varlen, k, a, b, ckpt->block and workspace.  Together they do exactly
- * what gdn_chunk_prefill does. */
+ * same layer, varlen, q, k, a, b, ckpt->block and workspace.  Together they do exactly
+ * what gdn_chunk_prefill does.  Strides: qk_stride * io bytes, v_stride * io bytes and
+ * n_v_heads * d * 4 must each stay below 2^31 / 64 (GDN_ERR_BAD_SHAPE otherwise; the
+ * same holds for gdn_chunk_prefill). */
 gdn_status gdn_prefill_factorize(const gdn_layer* layer, hipStream_t stream,
-                                 const gdn_varlen* varlen, const void* k, int64_t qk_stride,
-                                 const float* a, const float* b, int32_t block, void* workspace,
-                                 size_t workspace_bytes);
+                                 const gdn_varlen* varlen, const void* q, const void* k,
+                                 int64_t qk_stride, const float* a, const float* b, int32_t block,
+                                 void* workspace, size_t workspace_bytes);
 gdn_status gdn_prefill_scan(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
                             const void* q, const void* k, const void* v, int64_t qk_stride,
                             int64_t v_stride, const gdn_state_ref* states, const gdn_ckpt* ckpt,
