@@ -166,31 +166,40 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * mt + 4 * grp + r;
-        float val = 0.f;
-        if (sc < t && t < n) val = vec_lds[CT + t] * __expf(vec_lds[t] - gs) * acc[r];
-        As[t][sc] = val;
+        // computed for every element (pinned, so that the compiler does not move the LDS
+        // reads into a branch per element) and kept or dropped by the select
+        float dec = __expf(vec_lds[t] - gs), bt = vec_lds[CT + t];
+        asm volatile("" : "+v"(dec), "+v"(bt));
+        As[t][sc] = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
       }
     }
   }
   __syncthreads();
 
   // Forward substitution, lane j owns column j:  T[t][j] = [t == j] - sum_{s<t} A[t][s] T[s][j].
-  // The sum runs as four interleaved partial sums (s mod 4) added in a fixed order.
+  // The sum runs as four interleaved partial sums (s mod 4) added in a fixed order.  Row
+  // t + 1 of A is requested from LDS before the sums of row t run, so the LDS latency
+  // overlaps them; two rows of A are live in registers.
   float Tc[CT];
+  f32x4 arow[2][CT / 4];
 #pragma unroll
   for (int t = 0; t < CT; ++t) {
+    if (t + 1 < CT) {
+#pragma unroll
+      for (int i = 0; i < (t + 4) / 4; ++i) arow[(t + 1) & 1][i] = *reinterpret_cast<const f32x4*>(&As[t + 1][4 * i]);
+    }
+    asm volatile("" ::: "memory");
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
     for (int s = 0; s < t; ++s) {
-      const float av = As[t][s];
+      const float av = arow[t & 1][s >> 2][s & 3];
       if ((s & 3) == 0) p0 = fmaf(av, Tc[s], p0);
       if ((s & 3) == 1) p1 = fmaf(av, Tc[s], p1);
       if ((s & 3) == 2) p2 = fmaf(av, Tc[s], p2);
       if ((s & 3) == 3) p3 = fmaf(av, Tc[s], p3);
     }
     Tc[t] = (t == lane ? 1.f : 0.f) - ((p0 + p1) + (p2 + p3));
-    // row t is finished before the loads of row t + 1 start: at most one row of A is
-    // live in registers
+    // row t is finished before the requests for row t + 2 are issued
     asm volatile("" : "+v"(Tc[t]) : : "memory");
   }
   if (lane < CT) {

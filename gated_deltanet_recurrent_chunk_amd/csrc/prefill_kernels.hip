@@ -189,20 +189,35 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
     zero_lds(L1, L1_BYTES, lane, 64);
   }
   __syncthreads();
-  const IO* kb = p.k + cd.row * p.qk_stride + (int64_t)hk * D;
-  const IO* qb = p.q + cd.row * p.qk_stride + (int64_t)hk * D;
-  for (int idx = lane; idx < CT * PER_ROW; idx += 64) {
+  // Every row load is issued before any is used: buffer loads whose descriptor ends at
+  // the chunk's last row, so rows past n read as zeros without a branch.
+  constexpr int PER_LANE = CT * PER_ROW / 64;
+  const uint32_t qsb = (uint32_t)p.qk_stride * sizeof(IO);
+  const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
+  const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
+  const rsrc_t ra = make_rsrc(p.a + cd.row * p.Hv + h, (uint32_t)n * p.Hv * 4);
+  const rsrc_t rb = make_rsrc(p.b + cd.row * p.Hv + h, (uint32_t)n * p.Hv * 4);
+  u32x4 kv[PER_LANE], qv[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int idx = lane + 64 * i;
     const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    store_row_terms<IO, NTI>(load16(kb + (int64_t)t * p.qk_stride + j0, t < n), Ks, CT * KP, KP, t, j0);
-    store_row_terms<IO, NTI>(load16(qb + (int64_t)t * p.qk_stride + j0, t < n), Qs, CT * KP, KP, t, j0);
+    const uint32_t off = t * qsb + j0 * sizeof(IO);
+    kv[i] = ld16(rk, off, 0);
+    qv[i] = ld16(rq, off, 0);
   }
-  float la = 0.f, bb = 0.f;
-  if (lane < n) {
-    const int64_t ai = (cd.row + lane) * (int64_t)p.Hv + h;
-    la = __logf(p.a[ai]);
-    bb = p.b[ai];
+  const float av = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, lane * p.Hv * 4, 0, 0));
+  const float bb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, lane * p.Hv * 4, 0, 0));
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int idx = lane + 64 * i;
+    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    const uint4 k4{kv[i][0], kv[i][1], kv[i][2], kv[i][3]}, q4{qv[i][0], qv[i][1], qv[i][2], qv[i][3]};
+    store_row_terms<IO, NTI>(k4, Ks, CT * KP, KP, t, j0);
+    store_row_terms<IO, NTI>(q4, Qs, CT * KP, KP, t, j0);
   }
-  const float g = wave_inclusive_scan(la);  // rows past n keep g_{n-1}
+  const float la = lane < n ? __logf(av) : 0.f;  // rows past n: b = 0, log-decay 0
+  const float g = wave_inclusive_scan(la);        // rows past n keep g_{n-1}
   gl[lane] = g;
   __syncthreads();
   uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
@@ -234,8 +249,11 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
       for (int e = 0; e < 8; ++e) {
         const int sp = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
         const float dot = e < 4 ? acc0[e] : acc1[e - 4];
-        float val = 0.f;
-        if (sp <= t && t < n && (e < 4 || two)) val = p.scale * __expf(gt - gl[sp]) * dot;
+        // the exponent g_t - g_s is <= 0 on the causal side kept by the select; the
+        // other side is computed and discarded
+        float dec = __expf(gt - gl[sp]);
+        asm volatile("" : "+v"(dec));  // computed for every element, see factorize_chunk
+        const float val = (sp <= t && t < n && (e < 4 || two)) ? p.scale * dec * dot : 0.f;
         split_terms<NTF>(val, tt[e]);
       }
 #pragma unroll
