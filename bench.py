@@ -42,17 +42,26 @@ PAGE_BYTES = BLOCK * 4096  # one attention page of 4,096 B per token
 
 
 def scan_algorithmic_flops(tokens, heads, d=D, c=CHUNK):
-    """Products the chunk scan performs, counted once per product (not per bf16 pass):
-    K S^T, Q S^T, the state update (2 d^2 each) and T R, P Delta, Q K^T (2 C d each),
-    per token and value head."""
-    return tokens * heads * (6 * d * d + 6 * c * d)
+    """Products of the chunk scan, each counted once (not per bf16 pass), per token and
+    value head: K S^T, Q S^T and the state update K^T Delta (2 d^2 each), and the two
+    64 x 64 triangular products T R and P Delta (C d each, half of a full 2 C d)."""
+    return tokens * heads * (6 * d * d + 2 * c * d)
 
 
-def scan_bf16_pass_flops(tokens, heads, d=D, c=CHUNK):
-    """The same products as issued on the bf16 matrix cores with bf16 inputs: an fp32
-    operand is two bf16 terms, so K S^T, Q S^T and the state update take 2 passes,
-    T R and P Delta 3 passes, Q K^T 1 pass."""
-    return tokens * heads * (2 * 2 * d * d * 3 + 2 * c * d * (3 + 3 + 1))
+def scan_pass_flops(tokens, heads, d=D, c=CHUNK):
+    """The same products weighted by the bf16 matrix-core passes they need with bf16
+    inputs: an fp32 operand is two bf16 terms, so a bf16 x fp32 product (K S^T, Q S^T,
+    the update) is 2 passes and an fp32 x fp32 product (T R, P Delta) keeps 3 of the 4
+    term pairs.  Time at the bf16 peak for this many flops is the kernel's MFMA roof."""
+    return tokens * heads * (2 * 6 * d * d + 3 * 2 * c * d)
+
+
+def scan_issued_flops(tokens, heads, d=D, c=CHUNK):
+    """Matrix-core flops the scan kernel actually issues (16x16x32 bf16 MFMAs): per 16-row
+    slab and chunk, 32 for K S^T, 32 for Q S^T, 2 x 18 for T R (both key halves form it),
+    18 for P Delta, 32 for the update."""
+    chunks = tokens // c
+    return chunks * heads * (d // 16) * (32 + 32 + 36 + 18 + 32) * 16 * 16 * 32 * 2
 
 
 def flush_bytes(n_acc, heads=32, qk_heads=16, d=D):
@@ -114,18 +123,10 @@ def main():
     ws = torch.empty(g.prefill_workspace_bytes(layer, cu, sp, BLOCK), dtype=torch.uint8, device=dev)
     cws = torch.empty(g.conv_workspace_bytes(layer, cu, sp, BLOCK), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record()
+    def step():
         g.conv_update(layer, x, w, [("zero", None, tail)], cu, sp, y, ckpt=pool, page_ids=page_ids, workspace=cws)
-        if ev:
-            ev[1].record()
         g.prefill_factorize(layer, q, k, a, b, cu, sp, BLOCK, ws)
-        if ev:
-            ev[2].record()
         g.prefill_scan(layer, q, k, v, cu, sp, [("zero", None, S)], o, ws, ckpt=pool, page_ids=page_ids)
-        if ev:
-            ev[3].record()
 
     for _ in range(args.warmup):
         step()
@@ -138,20 +139,30 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     value = T * args.steps / elapsed
 
-    # per-kernel durations on the stream the kernels run on
-    t_conv, t_fact, t_scan = [], [], []
-    for _ in range(args.steps):
-        ev = events(4)
-        step(ev)
+    # Per-kernel launch durations: each stage launched `reps` times back to back between
+    # two events on the stream the kernels run on (torch's current stream), so the host
+    # planning of one call overlaps the previous launch and only GPU time counts.
+    def time_stage(fn, reps):
+        fn()
         torch.cuda.synchronize()
-        t_conv.append(ev[0].elapsed_time(ev[1]))
-        t_fact.append(ev[1].elapsed_time(ev[2]))
-        t_scan.append(ev[2].elapsed_time(ev[3]))
-    scan_ms = statistics.mean(t_scan)
-    fact_ms = statistics.mean(t_fact)
-    conv_ms = statistics.mean(t_conv)
+        ev = events(2)
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    kreps = max(10, args.steps)
+    conv_ms = time_stage(lambda: g.conv_update(layer, x, w, [("zero", None, tail)], cu, sp, y, ckpt=pool,
+                                               page_ids=page_ids, workspace=cws), kreps)
+    fact_ms = time_stage(lambda: g.prefill_factorize(layer, q, k, a, b, cu, sp, BLOCK, ws), kreps)
+    scan_ms = time_stage(lambda: g.prefill_scan(layer, q, k, v, cu, sp, [("zero", None, S)], o, ws, ckpt=pool,
+                                                page_ids=page_ids), kreps)
     alg = scan_algorithmic_flops(T, H)
+    passes = scan_pass_flops(T, H)
     achieved_tflops = alg / (scan_ms * 1e-3) / 1e12
+    eff_peak = PEAK_BF16_TFLOPS * alg / passes
 
     # ------------------------------------------------------------ replay flush (4B layer)
     fl_layer = g.Layer(16, 32, D, torch.bfloat16)
@@ -223,7 +234,7 @@ def main():
         "config": {"workload": "prefill_27b_T8192_H48_d128_block896 (conv 18432 ch + chunked prefill, "
                                "9 checkpoints)", "tokens": T, "heads": H, "head_dim": D, "block": BLOCK,
                    "chunk": CHUNK},
-        "stages_ms": {"conv": round(conv_ms, 4), "factorize": round(fact_ms, 4), "scan": round(scan_ms, 4)},
+        "kernel_ms": {"conv": round(conv_ms, 4), "factorize": round(fact_ms, 4), "scan": round(scan_ms, 4)},
         "flush_us_per_layer": {"accepted_u1_16": round(flush_u, 2), "all_16": round(flush_16, 2),
                                "all_17": round(flush_17, 2),
                                "workload": "flush_4b_16req_H32_d128_32slots",
@@ -237,13 +248,19 @@ def main():
             "kernel": "scan_kernel<bf16,128>",
             "bound": "mfma",
             "achieved": round(achieved_tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            # the bf16 dense peak scaled by algorithmic / pass-weighted flops: the peak of
+            # this product mix on the bf16 matrix cores
+            "peak": round(eff_peak, 1),
             "unit": "TFLOP/s",
-            "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(achieved_tflops / eff_peak, 4),
             "traffic": None,
+            "launch_us": round(scan_ms * 1e3, 2),
             "algorithmic_flops_per_launch": alg,
-            "bf16_pass_flops_per_launch": scan_bf16_pass_flops(T, H),
-            "fp32_mfma_equivalent_frac": round(achieved_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+            "pass_weighted_flops_per_launch": passes,
+            "issued_mfma_flops_per_launch": scan_issued_flops(T, H),
+            "bf16_dense_peak": PEAK_BF16_TFLOPS,
+            "fp32_mfma_equivalent": {"peak": PEAK_FP32_MFMA_TFLOPS,
+                                     "frac": round(achieved_tflops / PEAK_FP32_MFMA_TFLOPS, 4)},
         },
     }
 

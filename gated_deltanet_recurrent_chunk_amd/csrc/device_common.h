@@ -50,6 +50,12 @@ __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(bf16_bits, h);
 }
+// Two values rounded to bf16 (nearest even) in one conversion; lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, h2));
+}
 __device__ __forceinline__ float to_f32(bf16_bits x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename IO>

@@ -15,7 +15,7 @@
 namespace gdn {
 
 constexpr int kChunk = 64;          // rows per prefill chunk (the MFMA tile height x 4)
-constexpr int kConvTile = 64;       // rows per conv tile
+constexpr int kConvTile = 16;       // rows per conv tile
 constexpr int kMaxBufRows = 64;     // replay-flush log rows per request
 constexpr size_t kAlign = 256;
 

@@ -44,8 +44,7 @@ __device__ __forceinline__ void store_vec(IO* p, const float (&in)[N]) {
     for (int u = 0; u < N / 8; ++u) {
       uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)f32_to_bf16(in[8 * u + 2 * e]) | ((uint32_t)f32_to_bf16(in[8 * u + 2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(in[8 * u + 2 * e], in[8 * u + 2 * e + 1]);
       reinterpret_cast<uint4*>(p)[u] = uint4{w[0], w[1], w[2], w[3]};
     }
   } else {
@@ -143,22 +142,62 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
 
 // ==================================================================================
 // Conv: thread = VEC consecutive channels x one tile of up to kConvTile rows of one
-// sequence.  The three previous raw rows travel in registers; the rows before a
-// sequence's first token come from its tail source (or are zero, never read).
+// sequence.  All kConvTile + 3 input rows the tile needs are requested before any is
+// used; rows before a sequence's first token come from its tail source (or are zero,
+// never read), rows past the tile's end are clamped to its last row and not used.
 //   y[t][c] = act(w[c][0] x[t-3][c] + w[c][1] x[t-2][c] + w[c][2] x[t-1][c] + w[c][3] x[t][c])
 // At an absolute block boundary the three raw rows before it go to that page's tail
 // region.  The first tile of each sequence also writes the sequence's new tail; it is
 // the only tile that reads the old one, so an in-place tail update is safe.
 template <typename IO>
+__device__ __forceinline__ void unpack_row(const uint4& v, float (&out)[16 / sizeof(IO)]) {
+  if constexpr (sizeof(IO) == 2) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = bf16_to_f32((bf16_bits)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu)));
+  } else {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  }
+}
+
+template <typename IO, bool SILU>
 __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
   constexpr int VEC = 16 / sizeof(IO);
+  constexpr int TR = kConvTile;
   const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * VEC;
   if (c0 >= p.channels) return;
   const ConvTile tile = p.tiles[blockIdx.x];
   const ConvSeq sq = p.seqs[tile.seq];
   const int64_t C = p.channels;
   const int64_t rel0 = tile.row - sq.row0;
+  const int n = tile.len;
+  const IO* src = reinterpret_cast<const IO*>(sq.src_tail);
+  auto row_ptr = [&](int64_t rel) -> const uint4* {
+    if (rel >= 0) return reinterpret_cast<const uint4*>(p.x + (sq.row0 + rel) * C + c0);
+    if (src) return reinterpret_cast<const uint4*>(src + (3 + rel) * C + c0);
+    return nullptr;  // zero rows: never read
+  };
 
+  // rows rel0 - 3 + i, i = 0 .. TR + 2
+  uint4 raw[TR + 3];
+  if (rel0 >= 3) {
+    // a running row pointer (no 64-bit multiply per row); rows past the tile repeat its last
+    const IO* ptr = p.x + (sq.row0 + rel0 - 3) * C + c0;
+#pragma unroll
+    for (int i = 0; i < TR + 3; ++i) {
+      raw[i] = *reinterpret_cast<const uint4*>(ptr);
+      if (i + 1 < n + 3) ptr += C;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TR + 3; ++i) {
+      const uint4* ptr = row_ptr(rel0 - 3 + (i < n + 3 ? i : n + 2));
+      raw[i] = ptr ? *ptr : uint4{0u, 0u, 0u, 0u};
+    }
+  }
   float w[4][VEC];
   {
     float wr[4 * VEC];
@@ -168,60 +207,71 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j][e] = wr[4 * e + j];
   }
-  const IO* src = reinterpret_cast<const IO*>(sq.src_tail);
-  auto load_row = [&](int64_t rel, float (&out)[VEC]) {
-    if (rel >= 0) {
-      load_vec<IO, VEC>(p.x + (sq.row0 + rel) * C + c0, out);
-    } else if (src) {
-      load_vec<IO, VEC>(src + (3 + rel) * C + c0, out);
-    } else {
+
+  // rows of this tile that end on an absolute block boundary (bit t: position
+  // p0 + rel0 + t + 1), and the ordinal of the first such boundary in the sequence
+  uint32_t bmask = 0;
+  int64_t bord0 = 0;
+  if (p.block > 0) {
+    const int64_t first = sq.p0 + rel0 + 1, last = sq.p0 + rel0 + n;
+    const int64_t nb = (first + p.block - 1) / p.block;  // first boundary index >= first
+    bord0 = nb - sq.p0 / p.block - 1;
+    for (int64_t P = nb * p.block; P <= last; P += p.block) bmask |= 1u << (uint32_t)(P - first);
+  }
+  int64_t bord = bord0;
+  // sliding window over the unpacked rows: each input row is converted once
+  float x0[VEC], x1[VEC], x2[VEC];
+  unpack_row<IO>(raw[0], x0);
+  unpack_row<IO>(raw[1], x1);
+  unpack_row<IO>(raw[2], x2);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) out[e] = 0.f;
-    }
-  };
-  float h0[VEC], h1[VEC], h2[VEC];
-  load_row(rel0 - 3, h0);
-  load_row(rel0 - 2, h1);
-  load_row(rel0 - 1, h2);
-  const int64_t pblk = p.block > 0 ? sq.p0 / p.block : 0;
-  for (int t = 0; t < tile.len; ++t) {
-    float xt[VEC], yv[VEC];
-    load_row(rel0 + t, xt);
+  for (int t = 0; t < TR; ++t) {
+    if (t >= n) continue;  // uniform; keeps the loop fully unrolled (raw[] stays in registers)
+    float x3[VEC], yv[VEC];
+    unpack_row<IO>(raw[t + 3], x3);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      float acc = w[0][e] * h0[e];
-      acc = fmaf(w[1][e], h1[e], acc);
-      acc = fmaf(w[2][e], h2[e], acc);
-      acc = fmaf(w[3][e], xt[e], acc);
-      if (p.act == GDN_ACT_SILU) acc = acc / (1.f + expf(-acc));
+      float acc = w[0][e] * x0[e];
+      acc = fmaf(w[1][e], x1[e], acc);
+      acc = fmaf(w[2][e], x2[e], acc);
+      acc = fmaf(w[3][e], x3[e], acc);
+      // SiLU with the hardware exp and reciprocal: acc / (1 + exp(-acc)); the limits
+      // (exp overflow to inf -> rcp 0 -> -0) come out right
+      if constexpr (SILU) acc = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));
       yv[e] = acc;
-      h0[e] = h1[e];
-      h1[e] = h2[e];
-      h2[e] = xt[e];
     }
     store_vec<IO, VEC>(p.y + (tile.row + t) * C + c0, yv);
-    if (p.block > 0) {
-      const int64_t pos = sq.p0 + rel0 + t + 1;
-      if (pos % p.block == 0) {
-        const int32_t pid = p.pages[sq.page_begin + (pos / p.block - pblk - 1)];
+    if (bmask & (1u << t)) {
+      {
+        const int32_t pid = p.pages[sq.page_begin + bord++];
         if (pid >= 0) {
-          IO* dst = reinterpret_cast<IO*>(p.ckpt_pool + (size_t)pid * p.page_bytes + p.tail_offset);
-          store_vec<IO, VEC>(dst + c0, h0);
-          store_vec<IO, VEC>(dst + C + c0, h1);
-          store_vec<IO, VEC>(dst + 2 * C + c0, h2);
+          uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<IO*>(p.ckpt_pool + (size_t)pid * p.page_bytes +
+                                                                      p.tail_offset) + c0);
+          const size_t rs = C * sizeof(IO) / 16;
+          dst[0] = raw[t + 1];
+          dst[rs] = raw[t + 2];
+          dst[2 * rs] = raw[t + 3];
         }
       }
     }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      x0[e] = x1[e];
+      x1[e] = x2[e];
+      x2[e] = x3[e];
+    }
   }
   if (rel0 == 0) {
-    float t0[VEC], t1[VEC], t2[VEC];
-    load_row(sq.len - 3, t0);
-    load_row(sq.len - 2, t1);
-    load_row(sq.len - 1, t2);
-    IO* dst = reinterpret_cast<IO*>(sq.dst_tail);
-    store_vec<IO, VEC>(dst + c0, t0);
-    store_vec<IO, VEC>(dst + C + c0, t1);
-    store_vec<IO, VEC>(dst + 2 * C + c0, t2);
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<IO*>(sq.dst_tail) + c0);
+    const size_t rs = C * sizeof(IO) / 16;
+    uint4 tl[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {  // all read before any is written (the tail may be updated in place)
+      const uint4* ptr = row_ptr(sq.len - 3 + i);
+      tl[i] = ptr ? *ptr : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dst[i * rs] = tl[i];
   }
 }
 
@@ -260,7 +310,10 @@ static hipError_t launch_conv_t(const ConvArgs<IO>& a, int n_tiles, hipStream_t 
   constexpr int VEC = 16 / sizeof(IO);
   const int64_t groups = a.channels / VEC;
   dim3 grid((unsigned)n_tiles, (unsigned)((groups + 255) / 256));
-  hipLaunchKernelGGL((conv_kernel<IO>), grid, dim3(256), 0, st, a);
+  if (a.act == GDN_ACT_SILU)
+    hipLaunchKernelGGL((conv_kernel<IO, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((conv_kernel<IO, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st) {
