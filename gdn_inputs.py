@@ -114,6 +114,30 @@ def qkvab(T: int, n_qk: int, n_v: int, d: int, io_dtype=torch.bfloat16, seed: in
     return q, k, v, a, b
 
 
+def qkvab_device(T: int, n_qk: int, n_v: int, d: int, io_dtype=torch.bfloat16, seed: int = 0,
+                 device="cuda"):
+    """Same recipe as qkvab, drawn on the device with the device's seeded generator (for
+    the long workload, whose host draw and upload would dominate a test).  The values
+    differ from the host draw of the same seed; a test copies back the heads it checks.
+    Drawn in token blocks into preallocated outputs, so temporaries stay bounded."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 77)
+    q = torch.empty(T, n_qk, d, dtype=io_dtype, device=device)
+    k = torch.empty(T, n_qk, d, dtype=io_dtype, device=device)
+    v = torch.empty(T, n_v, d, dtype=io_dtype, device=device)
+    a = torch.empty(T, n_v, dtype=torch.float32, device=device)
+    b = torch.empty(T, n_v, dtype=torch.float32, device=device)
+    for t0 in range(0, T, TOKEN_BLOCK):
+        n = min(TOKEN_BLOCK, T - t0)
+        q[t0:t0 + n] = _unit_rows(torch.randn(n, n_qk, d, generator=g, device=device)).to(io_dtype)
+        k[t0:t0 + n] = _unit_rows(torch.randn(n, n_qk, d, generator=g, device=device)).to(io_dtype)
+        v[t0:t0 + n] = torch.randn(n, n_v, d, generator=g, device=device).to(io_dtype)
+        b[t0:t0 + n] = torch.sigmoid(torch.randn(n, n_v, generator=g, device=device))
+        a[t0:t0 + n] = torch.exp(-torch.nn.functional.softplus(torch.randn(n, n_v, generator=g, device=device))
+                                 * 0.1)
+    return q, k, v, a, b
+
+
 def conv_inputs(T: int, channels: int, width: int = 4, io_dtype=torch.bfloat16, seed: int = 0):
     """Draw conv inputs x [T, C] and weights w [C, width] in the io dtype."""
     g = _gen(seed, 10_000)
