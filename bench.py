@@ -64,6 +64,27 @@ def scan_issued_flops(tokens, heads, d=D, c=CHUNK):
     return chunks * heads * (d // 16) * (32 + 32 + 36 + 18 + 32) * 16 * 16 * 32 * 2
 
 
+def measured_scan_traffic():
+    """HBM bytes per scan launch from the committed counter profile (FETCH_SIZE and
+    WRITE_SIZE, calibrated against a plain copy), or None once the kernel sources differ
+    from the ones the counters were taken on."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "prefill_27b_T8192_H48_hbm_traffic.md")
+    csrc = os.path.join(ROOT, "gated_deltanet_recurrent_chunk_amd", "csrc")
+    try:
+        text = open(path).read()
+        src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                       for f in ("prefill_kernels.hip", "chunk_common.h", "device_common.h"))
+    except OSError:
+        return None
+    sha = re.search(r"source_sha256[^:]*: ([0-9a-f]{64})", text)
+    nbytes = re.search(r"scan_traffic_bytes_per_launch: (\d+)", text)
+    if not sha or not nbytes or sha.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(nbytes.group(1))
+
+
 def flush_bytes(n_acc, heads=32, qk_heads=16, d=D):
     """HBM bytes one flush must move: each touched state read and written once, plus
     the accepted log rows (bf16 k, v; fp32 a, b)."""
@@ -163,6 +184,7 @@ def main():
     passes = scan_pass_flops(T, H)
     achieved_tflops = alg / (scan_ms * 1e-3) / 1e12
     eff_peak = PEAK_BF16_TFLOPS * alg / passes
+    traffic = measured_scan_traffic()
 
     # ------------------------------------------------------------ replay flush (4B layer)
     fl_layer = g.Layer(16, 32, D, torch.bfloat16)
@@ -253,7 +275,7 @@ def main():
             "peak": round(eff_peak, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / eff_peak, 4),
-            "traffic": None,
+            "traffic": traffic,
             "launch_us": round(scan_ms * 1e3, 2),
             "algorithmic_flops_per_launch": alg,
             "pass_weighted_flops_per_launch": passes,

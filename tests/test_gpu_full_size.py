@@ -98,10 +98,11 @@ def test_varlen_27b_stepped_resume_is_bit_identical_to_cold(g):
     """Four sequences of 2,688 / 5,000 / 6,272 / 12,000 tokens at the 27B layer, processed
     in steps of at most floor_chunk(2048, 896) = 1,792 tokens per sequence per call, with
     checkpoints written by one call and read by the next.  Sequences 1 and 3 share a
-    seeded common prefix of 2,688 tokens, of which the cache rule keeps 1,792 (two
-    blocks), so both resume at block 2 from a page stored by an earlier request over the
-    prefix.  Every output row, final state and checkpoint page must equal the sequence's
-    cold solo run bit for bit."""
+    seeded common prefix of 3,000 tokens, of which the cache rule keeps 1,792 (two
+    blocks), and each resumes at block 2 from the page the other one's cold run wrote
+    (a writer of a different length, the case the prefix-cache page traces).  Every
+    output row, final state and checkpoint page must equal the sequence's cold solo run
+    bit for bit."""
     w = gi.VARLEN_27B
     H, D, block, dtype = w.n_v_heads, w.head_dim, w.block, w.io_dtype
     lens = list(w.seqlens)
@@ -112,7 +113,7 @@ def test_varlen_27b_stepped_resume_is_bit_identical_to_cold(g):
     cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
     q, k, v, a, b = gi.qkvab(cu[-1], H, H, D, dtype, seed=w.seed)
     # the common prefix of sequences 1 and 3, and the tokens of it a cache hit keeps
-    shared = 2688
+    shared = 3000
     assert g.cached_prefix_tokens(shared, block) == step
     for t_ in (q, k, v, a, b):
         t_[cu[3]:cu[3] + shared] = t_[cu[1]:cu[1] + shared]
@@ -141,15 +142,9 @@ def test_varlen_27b_stepped_resume_is_bit_identical_to_cold(g):
         cold_o.append(o1)
         cold_S.append(S1)
         cold_pages.append(ids)
-    # the earlier request over the common prefix: its block-2 page is what 1 and 3 resume from
-    prefix_ids = take(2)
-    So = torch.empty(H, D, D, device="cuda")
-    op = torch.empty(step, H, D, device="cuda")
-    _prefill_staged(g, layer, rows(qd, 1, 0, step), rows(kd, 1, 0, step), rows(vd, 1, 0, step),
-                    rows(ad, 1, 0, step), rows(bd, 1, 0, step), [0, step], [0], [("zero", None, So)], op, pool,
-                    prefix_ids, block)
+    # 1 and 3 resume from the block-2 page the other's cold run wrote
     pos = [0, step, 0, step]
-    src = [None, pool.page_ptr(prefix_ids[1]), None, pool.page_ptr(prefix_ids[1])]
+    src = [None, pool.page_ptr(cold_pages[3][1]), None, pool.page_ptr(cold_pages[1][1])]
     outs = [[] for _ in lens]
     Sfin = torch.empty(len(lens), H, D, D, device="cuda")
     written = [dict() for _ in lens]  # boundary index -> page
