@@ -54,10 +54,22 @@ __device__ __forceinline__ void store_vec(IO* p, const float (&in)[N]) {
   }
 }
 
+// Value of lane (lane with the DPP pattern CTRL applied) within its 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPR lanes (2, 4, 8 or 16) by DPP moves inside a 16-lane
+// row: swap neighbours, swap pairs, mirror halves of 8, mirror the 16.  Each step adds
+// two groups that hold equal values, so every lane of a group ends with the same bits.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off, 64);
+  static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "group of 1..16 lanes");
+  if constexpr (LPR >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (LPR >= 16) x += dpp<0x140>(x); // row_mirror
   return x;
 }
 
@@ -65,17 +77,20 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // ==================================================================================
 // Decode: one workgroup per (request, value head).  A state row is covered by D/8
-// lanes holding 8 consecutive floats each; one pass computes, per row i,
+// lanes; lane `sub` of a row holds columns 4 sub .. 4 sub + 3 and D/2 + 4 sub .. + 3, so
+// each load or store instruction covers whole 256-byte row halves.  One pass computes,
+// per row i,
 //   r_k = s_i . k,  r_q = s_i . q,  delta_i = b (v_i - a r_k),
 //   s_i <- a s_i + delta_i k,  o_i = scale (a r_q + delta_i (k . q)),
 // which is S_t = a S (I - b k k^T) + b v k^T and o = S_t q expanded, with the state
-// read and written exactly once.
+// read and written exactly once (non-temporal: it is not reused by this launch).
 template <typename IO, int D>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
   constexpr int LPR = D / 8;
   constexpr int NTH = (D * LPR < 256) ? D * LPR : 256;
   constexpr int RPP = NTH / LPR;
   constexpr int NP = D / RPP;
+  constexpr int HALF = D / 2;
   const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int slot = p.slot_ids[r];
   if (slot < -1 || slot >= p.n_slots) {
@@ -84,7 +99,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
   }
   if (slot < 0) return;  // padding: nothing read, nothing written
   const int sub = tid % LPR, rowi = tid / LPR;
-  const int j0 = sub * 8;
+  const int j0 = 4 * sub, j1 = HALF + 4 * sub;
   const int hk = h / p.group;
   float* st = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
 
@@ -92,12 +107,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
     const int i = pp * RPP + rowi;
-    s[pp][0] = *reinterpret_cast<const f32x4*>(st + (size_t)i * D + j0);
-    s[pp][1] = *reinterpret_cast<const f32x4*>(st + (size_t)i * D + j0 + 4);
+    s[pp][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (size_t)i * D + j0));
+    s[pp][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + (size_t)i * D + j1));
   }
   float k[8], q[8];
-  load_vec<IO, 8>(p.k + ((size_t)r * p.Hqk + hk) * D + j0, k);
-  load_vec<IO, 8>(p.q + ((size_t)r * p.Hqk + hk) * D + j0, q);
+  {
+    const IO* kr = p.k + ((size_t)r * p.Hqk + hk) * D;
+    const IO* qr = p.q + ((size_t)r * p.Hqk + hk) * D;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k[e] = to_f32(kr[j0 + e]);
+      k[4 + e] = to_f32(kr[j1 + e]);
+      q[e] = to_f32(qr[j0 + e]);
+      q[4 + e] = to_f32(qr[j1 + e]);
+    }
+  }
   const float a = p.a[(size_t)r * p.Hv + h];
   const float b = p.b[(size_t)r * p.Hv + h];
   const IO* vrow = p.v + ((size_t)r * p.Hv + h) * D;
@@ -134,8 +158,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
       n0[e] = fmaf(a, s[pp][0][e], delta * k[e]);
       n1[e] = fmaf(a, s[pp][1][e], delta * k[4 + e]);
     }
-    *reinterpret_cast<f32x4*>(st + (size_t)i * D + j0) = n0;
-    *reinterpret_cast<f32x4*>(st + (size_t)i * D + j0 + 4) = n1;
+    __builtin_nontemporal_store(n0, reinterpret_cast<f32x4*>(st + (size_t)i * D + j0));
+    __builtin_nontemporal_store(n1, reinterpret_cast<f32x4*>(st + (size_t)i * D + j1));
     if (sub == 0) orow[i] = p.scale * fmaf(a, rq, delta * kq);
   }
 }
