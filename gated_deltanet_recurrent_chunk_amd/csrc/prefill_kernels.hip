@@ -608,6 +608,366 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
 }
 
 // ==================================================================================
+// Scan, staged form (bf16 inputs, head dim >= 64): one workgroup per (sequence, value
+// head, pair of 16-row slabs), four waves (two slabs x two key halves).  The chunk
+// operands that all slabs of a head share -- the factor record (T, P, K^T, the row
+// vectors, exp(g_n)) -- and the value columns of the pair are copied into LDS once
+// per workgroup by LDS DMA (buffer loads that write LDS directly), a chunk ahead, into
+// two alternating buffers; each wave reads its operands from there one phase before
+// it needs them.  Key and query rows go straight to registers, as in scan_kernel.
+// Compared with one workgroup per slab, a compute unit moves about half the bytes per
+// chunk and issues a quarter of the vector memory instructions.
+//
+// Per chunk c, with buffers Bc (chunk c) and Bn (chunk c + 1):
+//   wait for this wave's copies into Bc; barrier (all copies landed, every wave is
+//   done with chunk c - 1, so Bn and the exchange slots are free); start the copies
+//   of chunk c + 1 into Bn; then phases A-D of scan_kernel with LDS operands.
+template <typename IO, int D>
+struct ScanStaged {
+  static constexpr bool OK = sizeof(IO) == 2 && D >= 64;
+  static constexpr int NS = D / 16, NSP = 2, SP = 2, NW = SP * NSP, NG = NS / SP;
+};
+
+__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
+}
+
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
+  using Cfg = PrefillCfg<IO, D>;
+  using Shp = ScanStaged<IO, D>;
+  constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
+  constexpr int DT = D / 16, KSD = D / 32;
+  constexpr int NSP = Shp::NSP, SP = Shp::SP, NW = Shp::NW, NG = Shp::NG;
+  constexpr int KSH = KSD / NSP, DTH = DT / NSP, MR = 4 / NSP;
+  constexpr int ESZ = sizeof(IO);
+  // staged chunk: the factor record (its last 1 KiB granule partial), then 64 value
+  // rows of the pair's 32 columns; 16-byte pieces of a value row are permuted by an
+  // XOR with (row / 4) % 4, so that the four row groups of one read hit distinct banks
+  constexpr int RG = (Cfg::REC_BYTES + 1023) / 1024;
+  constexpr int VRB = SP * 16 * ESZ, VNP = VRB / 16, VG = 64 * VRB / 1024;
+  constexpr int V_OFF = RG * 1024, G = RG + VG;
+  constexpr int GPW = (G + NW - 1) / NW;  // copies per wave; granules past G are padding
+  constexpr int BUF = GPW * NW * 1024;
+  constexpr int XCH = SP * NSP * 6 * 64;  // f32x4 exchange slots
+  // key and query rows of a chunk (one buffer, refilled once every wave has read
+  // them): rows of RB bytes whose 16-byte pieces are permuted by an XOR with the row
+  // index, so that the 16 rows of one operand read land in distinct banks
+  constexpr int RB = D * ESZ, PPR = RB / 16, RPG = 1024 / RB, KQG = 64 / RPG, KQPW = 2 * KQG / NW;
+  static_assert(KSH * NSP == KSD && DTH * NSP == DT && VNP == 4 && VG * 1024 == 64 * VRB, "shape");
+  static_assert(RPG * RB == 1024 && KQPW * NW == 2 * KQG, "key/query staging");
+  static_assert(2 * BUF + 16 * XCH + 2 * 64 * RB <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t kqs[2 * 64 * RB];
+  // [slab][wave][X tiles 0..3, partner's Y tiles][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xch[XCH];
+
+  // All workgroups of one (sequence, head) go to the same XCD (workgroups are dealt
+  // to the eight XCDs round robin), so their shared chunk data meets in one L2.
+  const int blk = blockIdx.x;
+  const int u = (blk / (8 * NG)) * 8 + (blk & 7);
+  const int sg = (blk >> 3) % NG;
+  if (u >= p.n_seqs * p.Hv) return;
+  const int seq = u / p.Hv, h = u - seq * p.Hv;
+  const int hk = h / p.group;
+  const int q = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int jj = q / NSP, w = q % NSP;  // slab within the pair, key half
+  const int sl = SP * sg + jj;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int my_row = 16 * sl + col;
+  const auto* sqp = (const __attribute__((address_space(4))) ScanSeq*)(p.seqs + seq);  // scalar loads
+  const ScanSeq sq{sqp->src, sqp->dst, sqp->chunk_begin, sqp->chunk_end, 0, 0};
+  const int cb = sq.chunk_begin, ce = sq.chunk_end;
+  const size_t head_off = (size_t)h * D * D;
+  const int jt0 = DTH * w, s0 = KSH * w;  // first state tile and k-step of this wave
+  const int mt0 = MR * w;                 // first output row tile of this wave
+
+  f32x4 S[DTH];
+#pragma unroll
+  for (int j = 0; j < DTH; ++j) {
+    if (sq.src)
+      S[j] = *reinterpret_cast<const f32x4*>(sq.src + head_off + (size_t)my_row * D + kcol<D>(jt0 + j, grp));
+    else
+      S[j] = zero4();
+  }
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int j = 0; j < DTH; ++j) *reinterpret_cast<f32x4*>(dst + kcol<D>(jt0 + j, grp)) = S[j];
+  };
+  if (cb >= ce) {
+    store_state(sq.dst + head_off + (size_t)my_row * D);
+    return;
+  }
+
+  // ---- per-lane byte offsets, fixed for the kernel
+  const uint32_t qsb = (uint32_t)p.qk_stride * ESZ, vsb = (uint32_t)p.v_stride * ESZ;
+  const uint32_t osb = (uint32_t)p.Hv * D * 4;
+  uint32_t kq_off[4], o_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kq_off[i] = (16 * i + col) * qsb + kcol<D>(0, grp) * ESZ;
+    o_off[i] = (4 * grp + i) * osb + col * 4;
+  }
+  // this lane's value column in a staged row (row t adds t * VRB); (t / 4) % 4 = grp
+  // for every row the lane reads
+  const int v_byte = (16 * jj + col) * ESZ;
+  const int v_rd = V_OFF + 16 * ((v_byte >> 4) ^ grp) + (v_byte & 15);
+
+  // chunk descriptors: one vector load (every lane the same 16 bytes) a chunk ahead;
+  // a scalar load would make every wait on LDS reads a wait for all of them
+  const rsrc_t rcd = make_rsrc(p.chunks, (uint32_t)p.n_chunks * (uint32_t)sizeof(ChunkDesc));
+  auto chunk_raw = [&](int c) { return ld16(rcd, (uint32_t)c * (uint32_t)sizeof(ChunkDesc), 0); };
+  auto to_desc = [](const u32x4& v) {
+    ChunkDesc d;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(v[0]), hi = __builtin_amdgcn_readfirstlane(v[1]);
+    d.row = (int64_t)(((uint64_t)hi << 32) | lo);
+    d.len = __builtin_amdgcn_readfirstlane(v[2]);
+    d.page = __builtin_amdgcn_readfirstlane(v[3]);
+    return d;
+  };
+
+  // ---- copies of chunk c into buffer B: 1 KiB granules g = q, q + NW, ...  Every wave
+  //      issues the same GPW copies on every path (padding granules read past the
+  //      record's end), so the compiler's counts of outstanding loads stay exact.  The
+  //      bounds of both descriptors are in the per-lane offset: lanes past the record
+  //      or past the chunk's last row write zeros.
+  const IO* v_pair = p.v + (int64_t)h * D + 16 * SP * sg;
+  auto stage_chunk = [&](const ChunkDesc& cd, int c, const uint8_t* B) {
+    const rsrc_t rr = make_rsrc(p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
+    const rsrc_t rv = make_rsrc(v_pair + cd.row * p.v_stride, (uint32_t)cd.len * vsb);
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = q + gi * NW;  // wave-uniform
+      const bool is_v = g >= RG && g < G;
+      const uint32_t t = 16u * (uint32_t)(g - RG) + (uint32_t)lane / VNP;
+      const uint32_t lp = ((uint32_t)lane % VNP) ^ ((t >> 2) & (VNP - 1));
+      const uint32_t voff = g < RG ? 1024u * g + 16u * lane : is_v ? t * vsb + 16u * lp : (uint32_t)Cfg::REC_BYTES;
+      dma16(is_v ? rv : rr, B + 1024 * g, voff);
+    }
+  };
+
+  // copies of the chunk's key and query rows: KQPW granules per wave, same on every path
+  auto stage_kq = [&](const ChunkDesc& cd) {
+    const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
+    const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
+#pragma unroll
+    for (int gi = 0; gi < KQPW; ++gi) {
+      const int g = q + gi * NW;  // wave-uniform: granules 0 .. KQG-1 keys, then queries
+      const uint32_t r = RPG * (uint32_t)(g % KQG) + (uint32_t)lane / PPR;
+      const uint32_t lp = ((uint32_t)lane % PPR) ^ (r % PPR);
+      dma16(g >= KQG ? rq : rk, kqs + 1024 * g, r * qsb + 16u * lp);
+    }
+  };
+  // this wave's A operands of X and Y: row 16 mt + col, key columns 32 (s0 + s) + 8 grp ..
+  RowOp<IO> Kop[4][KSH], Qop[4][KSH];
+  auto read_kq = [&]() {
+#pragma unroll
+    for (int s = 0; s < KSH; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int r = 16 * mt + col;
+        const int off = r * RB + 16 * ((grp + 4 * (s0 + s)) ^ (r % PPR));
+        Kop[mt][s].v = *reinterpret_cast<const bf16x8*>(kqs + off);
+        Qop[mt][s].v = *reinterpret_cast<const bf16x8*>(kqs + 64 * RB + off);
+      }
+  };
+  auto frag = [&](const uint8_t* B, int off, int f) {
+    return *reinterpret_cast<const bf16x8*>(B + off + 1024 * f + 16 * lane);
+  };
+  auto vrow4 = [&](const uint8_t* B, int plane, int mt) {  // rows 16 mt + 4 grp .. + 3 of a vector plane
+    return *reinterpret_cast<const f32x4*>(B + Cfg::VEC_OFF + plane * CT * 4 + 64 * mt + 16 * grp);
+  };
+  auto issue_point = [] { __builtin_amdgcn_sched_barrier(0); };
+
+  ChunkDesc cur = to_desc(chunk_raw(cb));
+  u32x4 nxt_raw = chunk_raw(cb + 1 < ce ? cb + 1 : cb);
+  stage_chunk(cur, cb, stage0);
+  stage_kq(cur);
+
+  auto step = [&](const int c, const uint8_t* Bc, const uint8_t* Bn) {
+    const bool more = c + 1 < ce;
+    const ChunkDesc nxt = to_desc(nxt_raw);
+    {
+      // wait for this wave's copies into Bc and kqs (the compiler counts LDS DMA per
+      // LDS object)
+      const float probe = *(const __attribute__((address_space(3))) float*)(Bc + 16 * lane);
+      const float probe_kq = *(const __attribute__((address_space(3))) float*)(kqs + 16 * lane);
+      asm volatile("" ::"v"(probe), "v"(probe_kq));
+    }
+    lds_barrier();
+    // (the last chunk stages itself again: every path issues the same copies, so the
+    // compiler's counts of outstanding loads stay exact)
+    stage_chunk(nxt, more ? c + 1 : c, Bn);
+    nxt_raw = chunk_raw(c + 2 < ce ? c + 2 : c + 1 - (more ? 0 : 1));
+
+    read_kq();
+    // ---- operands of phase B
+    float Vv[4][4];
+    f32x4 vb[4], vbeg[4];
+    bf16x8 Tf[kFragCombos][NTF];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Vv[mt][r] = bf16_to_f32(*reinterpret_cast<const bf16_bits*>(Bc + v_rd + (16 * mt + 4 * grp + r) * VRB));
+      vb[mt] = vrow4(Bc, Cfg::V_B, mt);
+      vbeg[mt] = vrow4(Bc, Cfg::V_BEG, mt);
+    }
+#pragma unroll
+    for (int f = 0; f < kFragCombos; ++f)
+#pragma unroll
+      for (int i = 0; i < NTF; ++i) Tf[f][i] = frag(Bc, Cfg::T_OFF, f * NTF + i);
+    issue_point();
+
+    // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains
+    f32x4 X[4], Y[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) X[mt] = Y[mt] = zero4();
+#pragma unroll
+    for (int s = 0; s < KSH; ++s) {
+      bf16x8 sop[NTF];
+      reg_operand<NTF>(S[2 * s], (2 * s + 1 < DTH) ? S[2 * s + 1] : zero4(), sop);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        bf16x8 ak[NTI], aq[NTI];
+        row_terms<NTI>(Kop[mt][s], ak);
+        row_terms<NTI>(Qop[mt][s], aq);
+        mma_terms<NTI, NTF, ORD>(X[mt], ak, sop);
+        mma_terms<NTI, NTF, ORD>(Y[mt], aq, sop);
+      }
+    }
+    issue_point();
+    // add the partner's partial sums: X for all rows, Y for this wave's output rows
+    f32x4 Ym[MR];
+    {
+      f32x4* mine = xch + ((jj * NSP + w) * 6) * 64 + lane;
+      const f32x4* other = xch + ((jj * NSP + (w ^ 1)) * 6) * 64 + lane;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) mine[mt * 64] = X[mt];
+#pragma unroll
+      for (int i = 0; i < MR; ++i) mine[(4 + i) * 64] = Y[MR * (w ^ 1) + i];
+      lds_barrier();
+      // every wave has read this chunk's key and query rows: copy the next chunk's
+      // (the last chunk copies its own again, so that every path issues the same copies)
+      stage_kq(more ? nxt : cur);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 xo = other[mt * 64];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X[mt][r] += xo[r];
+      }
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        const f32x4 yo = other[(4 + i) * 64];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ym[i][r] = Y[mt0 + i][r] + yo[r];
+      }
+    }
+
+    // ---- operands of phase C
+    f32x4 vegs[MR];
+    bf16x8 Pf[MR][2][NTF];
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const int mt = mt0 + i;
+      vegs[i] = vrow4(Bc, Cfg::V_EGS, mt);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s <= (mt >> 1))
+#pragma unroll
+          for (int t = 0; t < NTF; ++t) Pf[i][s][t] = frag(Bc, Cfg::P_OFF, frag_combo(mt, s) * NTF + t);
+    }
+    issue_point();
+
+    // ---- B: R = b V - b exp(g) X (zero past the chunk end), Delta = T R
+    f32x4 R[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[mt][r] = fmaf(-vbeg[mt][r], X[mt][r], vb[mt][r] * Vv[mt][r]);
+    bf16x8 Rop[2][NTF];
+    reg_operand<NTF>(R[0], R[1], Rop[0]);
+    reg_operand<NTF>(R[2], R[3], Rop[1]);
+    f32x4 Dl[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) Dl[mt] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int mt = 2 * s; mt < 4; ++mt) mma_terms<NTF, NTF, ORD>(Dl[mt], Tf[frag_combo(mt, s)], Rop[s]);
+
+    // ---- operands of phase D
+    f32x4 vedec[4];
+    bf16x8 KTf[DTH][2][NTI];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) vedec[mt] = vrow4(Bc, Cfg::V_EDEC, mt);
+#pragma unroll
+    for (int j = 0; j < DTH; ++j)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < NTI; ++i) KTf[j][s][i] = frag(Bc, Cfg::KT_OFF, ((jt0 + j) * 2 + s) * NTI + i);
+    const float egn = *reinterpret_cast<const float*>(Bc + Cfg::EGN_OFF);
+    issue_point();
+
+    // ---- C: O = scale exp(g) Y + (scale P) Delta for this wave's row tiles
+    {
+      bf16x8 Dop[2][NTF];
+      reg_operand<NTF>(Dl[0], Dl[1], Dop[0]);
+      reg_operand<NTF>(Dl[2], Dl[3], Dop[1]);
+      const rsrc_t ro = make_rsrc(p.o + cur.row * (int64_t)p.Hv * D + (int64_t)h * D + 16 * sl, (uint32_t)cur.len * osb);
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        const int mt = mt0 + i;
+        f32x4 acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = Ym[i][r] * vegs[i][r];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Dop[s]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st4(ro, o_off[r] + 16 * mt * osb, acc[r]);
+      }
+    }
+
+    // ---- D: S^T <- exp(g_n) S^T + K^T (exp(g_n - g) o Delta) for this wave's tiles
+    {
+      f32x4 Dt[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Dt[mt][r] = vedec[mt][r] * Dl[mt][r];
+      bf16x8 Dtop[2][NTF];
+      reg_operand<NTF>(Dt[0], Dt[1], Dtop[0]);
+      reg_operand<NTF>(Dt[2], Dt[3], Dtop[1]);
+#pragma unroll
+      for (int j = 0; j < DTH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[j][r] *= egn;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < DTH; ++j) mma_terms<NTI, NTF, ORD>(S[j], KTf[j][s], Dtop[s]);
+    }
+
+    // ---- checkpoint: the state after this chunk, bit for bit
+    if (cur.page >= 0)
+      store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)cur.page * p.page_bytes) + head_off +
+                  (size_t)my_row * D);
+    cur = nxt;
+  };
+
+  // two steps per trip, so that each step's buffers are fixed LDS objects
+#pragma unroll 1
+  for (int c = cb; c < ce; c += 2) {
+    step(c, stage0, stage1);
+    if (c + 1 < ce) step(c + 1, stage1, stage0);
+  }
+  store_state(sq.dst + head_off + (size_t)my_row * D);
+}
+
+// ==================================================================================
 // Launchers
 template <typename IO, int D>
 static hipError_t launch_factorize_t(const FactorizeArgs<IO>& a, int n_chunks, hipStream_t st) {
@@ -621,9 +981,16 @@ template <typename IO, int D>
 static hipError_t launch_scan_t(const ScanArgs<IO>& a, hipStream_t st) {
   const int64_t units = (int64_t)a.n_seqs * a.Hv;
   if (units == 0) return hipSuccess;
-  const int64_t blocks = (units + 7) / 8 * 8 * (D / 16);
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((scan_kernel<IO, D>), dim3((unsigned)blocks), dim3(64 * ScanSplit<D>::NSP), 0, st, a);
+  if constexpr (ScanStaged<IO, D>::OK) {
+    using Shp = ScanStaged<IO, D>;
+    const int64_t blocks = (units + 7) / 8 * 8 * Shp::NG;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((scan_staged_kernel<IO, D>), dim3((unsigned)blocks), dim3(64 * Shp::NW), 0, st, a);
+  } else {
+    const int64_t blocks = (units + 7) / 8 * 8 * (D / 16);
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((scan_kernel<IO, D>), dim3((unsigned)blocks), dim3(64 * ScanSplit<D>::NSP), 0, st, a);
+  }
   return hipGetLastError();
 }
 
