@@ -632,8 +632,12 @@ __device__ __forceinline__ void dma16(rsrc_t r, const void* lds, uint32_t voff) 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
 }
 
-template <typename IO, int D>
-__global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
+// The work of wave Q of a staged-scan workgroup (slab Q / 2 of the pair, key half
+// Q % 2), compiled once per wave index so that every register index and every copy
+// assignment is a constant.
+template <typename IO, int D, int Q>
+__device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const int u, const int sg, uint8_t* stage0,
+                                                 uint8_t* stage1, uint8_t* kqs, f32x4* xch) {
   using Cfg = PrefillCfg<IO, D>;
   using Shp = ScanStaged<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
@@ -657,22 +661,9 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   static_assert(KSH * NSP == KSD && DTH * NSP == DT && VNP == 4 && VG * 1024 == 64 * VRB, "shape");
   static_assert(RPG * RB == 1024 && KQPW * NW == 2 * KQG, "key/query staging");
   static_assert(2 * BUF + 16 * XCH + 2 * 64 * RB <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t kqs[2 * 64 * RB];
-  // [slab][wave][X tiles 0..3, partner's Y tiles][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 xch[XCH];
-
-  // All workgroups of one (sequence, head) go to the same XCD (workgroups are dealt
-  // to the eight XCDs round robin), so their shared chunk data meets in one L2.
-  const int blk = blockIdx.x;
-  const int u = (blk / (8 * NG)) * 8 + (blk & 7);
-  const int sg = (blk >> 3) % NG;
-  if (u >= p.n_seqs * p.Hv) return;
   const int seq = u / p.Hv, h = u - seq * p.Hv;
   const int hk = h / p.group;
-  const int q = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int jj = q / NSP, w = q % NSP;  // slab within the pair, key half
+  constexpr int q = Q, jj = Q / NSP, w = Q % NSP;  // slab within the pair, key half
   const int sl = SP * sg + jj;
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
   const int my_row = 16 * sl + col;
@@ -680,8 +671,8 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   const ScanSeq sq{sqp->src, sqp->dst, sqp->chunk_begin, sqp->chunk_end, 0, 0};
   const int cb = sq.chunk_begin, ce = sq.chunk_end;
   const size_t head_off = (size_t)h * D * D;
-  const int jt0 = DTH * w, s0 = KSH * w;  // first state tile and k-step of this wave
-  const int mt0 = MR * w;                 // first output row tile of this wave
+  constexpr int jt0 = DTH * w, s0 = KSH * w;  // first state tile and k-step of this wave
+  constexpr int mt0 = MR * w;                 // first output row tile of this wave
 
   f32x4 S[DTH];
 #pragma unroll
@@ -965,6 +956,42 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
     if (c + 1 < ce) step(c + 1, stage1, stage0);
   }
   store_state(sq.dst + head_off + (size_t)my_row * D);
+}
+
+// LDS of a staged-scan workgroup (the layout is stated in scan_staged_wave).
+template <typename IO, int D>
+struct StagedLds {
+  using Cfg = PrefillCfg<IO, D>;
+  using Shp = ScanStaged<IO, D>;
+  static constexpr int RG = (Cfg::REC_BYTES + 1023) / 1024;
+  static constexpr int G = RG + 64 * Shp::SP * 16 * (int)sizeof(IO) / 1024;
+  static constexpr int BUF = (G + Shp::NW - 1) / Shp::NW * Shp::NW * 1024;
+  static constexpr int XCH = Shp::SP * Shp::NSP * 6 * 64;
+  static constexpr int KQ = 2 * 64 * D * (int)sizeof(IO);
+};
+
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
+  using L = StagedLds<IO, D>;
+  constexpr int NG = ScanStaged<IO, D>::NG;
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[L::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[L::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t kqs[L::KQ];
+  // [slab][wave][X tiles 0..3, partner's Y tiles][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xch[L::XCH];
+
+  // All workgroups of one (sequence, head) go to the same XCD (workgroups are dealt
+  // to the eight XCDs round robin), so their shared chunk data meets in one L2.
+  const int blk = blockIdx.x;
+  const int u = (blk / (8 * NG)) * 8 + (blk & 7);
+  const int sg = (blk >> 3) % NG;
+  if (u >= p.n_seqs * p.Hv) return;
+  switch (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))) {
+    case 0: scan_staged_wave<IO, D, 0>(p, u, sg, stage0, stage1, kqs, xch); break;
+    case 1: scan_staged_wave<IO, D, 1>(p, u, sg, stage0, stage1, kqs, xch); break;
+    case 2: scan_staged_wave<IO, D, 2>(p, u, sg, stage0, stage1, kqs, xch); break;
+    default: scan_staged_wave<IO, D, 3>(p, u, sg, stage0, stage1, kqs, xch); break;
+  }
 }
 
 // ==================================================================================
