@@ -124,10 +124,12 @@ __device__ __forceinline__ void transpose_keys(const bf16_bits* Ks, int KP, bf16
 //   g, bb: this lane's g_t and b_t for t = lane (t >= n: g_t = g_{n-1}, b_t = 0).
 // Writes T = (I + A)^-1 as NTF swizzled bf16 planes (row stride tld, plane stride
 // tps) and the four per-row vectors g, exp(g), b, exp(g_n - g) into vec_out.
-template <int CT, int D, int NTI, int NTF, int ORD>
+// FOLD: writes T'' = diag(exp(g_n - g)) T diag(b) to Tout instead, and T^T (unscaled,
+// row j = column j of T) to Ttr in the same plane format.
+template <int CT, int D, int NTI, int NTF, int ORD, bool FOLD = false>
 __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n,
                                                 float g, float bb, bf16_bits* Tout, int tps, int tld,
-                                                float* vec_out, float* vec_lds) {
+                                                float* vec_out, float* vec_lds, bf16_bits* Ttr = nullptr) {
   constexpr int KP = row_stride(D);
   constexpr int KSD = (D + 31) / 32;
   constexpr int MT = CT / 16;
@@ -207,9 +209,24 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
       bf16_bits tt[NTF];
-      split_terms<NTF>(Tc[t], tt);
+      float x = Tc[t];
+      if constexpr (FOLD) x = (x * vec_out[3 * CT + t]) * bb;
+      split_terms<NTF>(x, tt);
 #pragma unroll
       for (int i = 0; i < NTF; ++i) Tout[i * tps + t * tld + pc] = tt[i];
+    }
+    if constexpr (FOLD) {
+      // row `lane` of T^T: runs of four columns are contiguous in the swizzled order
+#pragma unroll
+      for (int t0 = 0; t0 < CT; t0 += 4) {
+        bf16_bits tt[4][NTF];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_terms<NTF>(Tc[t0 + e], tt[e]);
+#pragma unroll
+        for (int i = 0; i < NTF; ++i)
+          *reinterpret_cast<uint2*>(Ttr + i * tps + lane * tld + swz(t0)) =
+              uint2{(uint32_t)tt[0][i] | ((uint32_t)tt[1][i] << 16), (uint32_t)tt[2][i] | ((uint32_t)tt[3][i] << 16)};
+      }
     }
   }
 }

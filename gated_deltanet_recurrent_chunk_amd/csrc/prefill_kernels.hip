@@ -4,9 +4,10 @@
 //   factorize_kernel: one wave per (chunk, value head), all of them at once.  Computes
 //     everything about a chunk that does not depend on the state: the gate vectors,
 //     T = (I + A)^-1 (the WY / UT transform), the causal decayed scores
-//     P = scale * exp(g_t - g_s) q_t.k_s (s <= t) and the keys transposed.  The three
-//     matrices are written as ready-made MFMA A-operand fragments (1 KiB each, 16 bytes
-//     per lane) into one record per (value head, chunk).
+//     P = scale * exp(g_t - g_s) q_t.k_s (s <= t) and the keys transposed.  It writes
+//     T'' = diag(exp(g_n - g)) T diag(b), PT'' = P T diag(b) and K^T as ready-made MFMA
+//     A-operand fragments (1 KiB each, 16 bytes per lane) into one record per (value
+//     head, chunk).
 //   scan_kernel: one workgroup per (sequence, value head, 16-row slab of the state),
 //     walking the sequence's chunks in order with its slab in registers.  Rows of the
 //     state evolve independently, so the slabs never exchange data; for head dim >= 64
@@ -50,14 +51,15 @@ template <typename IO, int D>
 struct PrefillCfg {
   static constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
   static constexpr int DT = D / 16;
-  // factor record: [T fragments][P fragments][K^T fragments][row vectors][chunk scalar]
+  // factor record: [T'' fragments][PT'' fragments][K^T fragments][row vectors][chunk
+  // scalar], with T'' = diag(exp(g_n - g)) T diag(b) and PT'' = (scale P) T diag(b)
   static constexpr int T_OFF = 0;
   static constexpr int P_OFF = kFragCombos * NTF * 1024;
   static constexpr int KT_OFF = 2 * kFragCombos * NTF * 1024;
   static constexpr int VEC_OFF = KT_OFF + DT * 2 * NTI * 1024;
-  // row vector planes (kChunk floats each): b, b exp(g), scale exp(g), exp(g_n - g)
-  static constexpr int V_B = 0, V_BEG = 1, V_EGS = 2, V_EDEC = 3;
-  static constexpr int EGN_OFF = VEC_OFF + 4 * CT * 4;  // exp(g_n)
+  // row vector planes (kChunk floats each): exp(g), scale exp(g)
+  static constexpr int V_EG = 0, V_EGS = 1, NVEC = 2;
+  static constexpr int EGN_OFF = VEC_OFF + NVEC * CT * 4;  // exp(g_n)
   static constexpr int REC_BYTES = EGN_OFF + 16;
   static_assert(REC_BYTES <= (int)factor_record_bytes_c(NTF, NTI, D), "factor record layout");
 };
@@ -166,8 +168,9 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
   constexpr int PER_ROW = D / VEC;
   constexpr int KS_BYTES = NTI * CT * KP * 2, TL_BYTES = NTF * CT * TP * 2, AS_BYTES = CT * (CT + 4) * 4;
   constexpr int L0_BYTES = KS_BYTES > TL_BYTES ? KS_BYTES : TL_BYTES;
-  constexpr int L1_BYTES = KS_BYTES > AS_BYTES ? KS_BYTES : AS_BYTES;
-  // L0: key rows, later T; L1: query rows, later A
+  constexpr int L1A = KS_BYTES > AS_BYTES ? KS_BYTES : AS_BYTES;
+  constexpr int L1_BYTES = L1A > TL_BYTES ? L1A : TL_BYTES;
+  // L0: key rows, later T''; L1: query rows, later A, later T^T
   __shared__ __attribute__((aligned(16))) uint8_t L0[L0_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t L1[L1_BYTES];
   __shared__ float gl[CT];
@@ -176,6 +179,7 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
   bf16_bits* Ks = reinterpret_cast<bf16_bits*>(L0);
   bf16_bits* Qs = reinterpret_cast<bf16_bits*>(L1);
   bf16_bits* Tl = reinterpret_cast<bf16_bits*>(L0);
+  bf16_bits* Tt = reinterpret_cast<bf16_bits*>(L1);
   auto As = reinterpret_cast<float (*)[CT + 4]>(L1);
 
   const int c = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
@@ -224,7 +228,9 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
 
   // ---- P fragments.  Tile (ms, mt) of P^T = K Q^T has the C layout "lane (col, grp)
   //      holds P[16 mt + col][16 ms + 4 grp + r]", i.e. elements 0..3 (ms = 2s) or 4..7
-  //      (ms = 2s + 1) of the A operand of P for (mt, s).
+  //      (ms = 2s + 1) of the A operand of P for (mt, s).  Kept in registers: they are
+  //      the B operands of PT^T = T^T P^T below.
+  bf16x8 Pfr[kFragCombos][NTF];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -261,8 +267,7 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
         bf16_bits v8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
-        *reinterpret_cast<bf16x8*>(rec + Cfg::P_OFF + (frag_combo(mt, s) * NTF + i) * 1024 + lane * 16) =
-            pack8(v8);
+        Pfr[frag_combo(mt, s)][i] = pack8(v8);
       }
     }
   }
@@ -292,16 +297,54 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
     const float gn = __shfl(g, n - 1, 64);
     const float eg = __expf(g);
     float* vo = reinterpret_cast<float*>(rec + Cfg::VEC_OFF);
-    vo[Cfg::V_B * CT + lane] = bb;
-    vo[Cfg::V_BEG * CT + lane] = bb * eg;
+    vo[Cfg::V_EG * CT + lane] = eg;
     vo[Cfg::V_EGS * CT + lane] = p.scale * eg;
-    vo[Cfg::V_EDEC * CT + lane] = lane < n ? __expf(gn - g) : 0.f;
     if (lane == 0) *reinterpret_cast<float*>(rec + Cfg::EGN_OFF) = __expf(gn);
   }
 
-  // ---- T = (I + A)^-1 (reads the key rows, then overwrites them with T)
-  factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, n, g, bb, Tl, CT * TP, TP, vec_tmp, vec_lds);
+  // ---- T = (I + A)^-1: T'' = diag(exp(g_n - g)) T diag(b) over the key rows, T^T over
+  //      the query rows (both are read by then)
+  factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks, CT * KP, As, n, g, bb, Tl, CT * TP, TP, vec_tmp, vec_lds, Tt);
   __syncthreads();
+
+  // ---- PT'' = (scale P) T diag(b), through its transpose: tile (jt, ut) of
+  //      PT^T = T^T P^T, with A = T^T rows (planes Tt) and B = P^T, whose B operand at
+  //      k-step s' is the A operand of P for (ut, s').  Its C layout "lane (col, grp)
+  //      holds PT[16 ut + col][16 jt + 4 grp + r]" is elements 0..3 (jt = 2s) or 4..7
+  //      (jt = 2s + 1) of the A operand of PT'' for (ut, s).  T^T[j][t'] is zero for
+  //      t' < j and P[u][t'] for t' > u, so s' runs over jt/2 .. ut/2.
+#pragma unroll
+  for (int ut = 0; ut < 4; ++ut) {
+#pragma unroll
+    for (int s = 0; s <= (ut >> 1); ++s) {
+      f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int jt = 2 * s + h2;
+        if (jt > ut) continue;  // above the diagonal: zero
+#pragma unroll
+        for (int sp = jt >> 1; sp <= (ut >> 1); ++sp) {
+          bf16x8 a[NTF];
+          op_terms<NTF>(Tt, CT * TP, TP, 16 * jt + col, sp, grp, a);
+          mma_terms<NTF, NTF, ORD>(acc[h2], a, Pfr[frag_combo(ut, sp)]);
+        }
+      }
+      bf16_bits tt[8][NTF];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float bj = vec_tmp[2 * CT + 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3)];
+        split_terms<NTF>(acc[e >> 2][e & 3] * bj, tt[e]);
+      }
+#pragma unroll
+      for (int i = 0; i < NTF; ++i) {
+        bf16_bits v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
+        *reinterpret_cast<bf16x8*>(rec + Cfg::P_OFF + (frag_combo(ut, s) * NTF + i) * 1024 + lane * 16) =
+            pack8(v8);
+      }
+    }
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -322,18 +365,19 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
 // waves: each keeps its half of the state, forms its half of the contractions
 // X = K S^T and Y = Q S^T over the key index, and the two halves are added through
 // LDS (one barrier per chunk; fp addition is commutative, so both waves hold the same
-// bits).  Both waves then form R and Delta = T R; each updates its half of the state
+// bits).  Both waves then form R' and Dt = T'' R'; each updates its half of the state
 // and writes half of the output rows.
 //
 // Register layouts (lane = 16 grp + col):
 //   state    S[j][r]  = S[16 slab + col][kcol(jt, grp) + r], jt = DTH w + j  (C layout of
 //            S^T tiles)
-//   X = K S^T, Y = Q S^T, R, Delta, O: [mt][r] = M[16 mt + 4 grp + r][16 slab + col]
-// Per chunk:
+//   X = K S^T, Y = Q S^T, R', Dt, O: [mt][r] = M[16 mt + 4 grp + r][16 slab + col]
+// Per chunk, with R = diag(b) R' and the gates folded into the pre-pass factors
+// (T'' = diag(exp(g_n - g)) T diag(b), PT'' = (scale P) T diag(b)):
 //   A: X, Y            (K, Q rows and the state split into bf16 terms)
-//   B: R = b V - b exp(g) X;  Delta = T R
-//   C: O = scale exp(g) Y + P Delta   (stored)
-//   D: S^T <- exp(g_n) S^T + K^T (exp(g_n - g) o Delta);  checkpoint
+//   B: R' = V - exp(g) X;  Dt = T'' R'   (= diag(exp(g_n - g)) Delta)
+//   C: O = scale exp(g) Y + PT'' R'      (= scale P Delta; stored)
+//   D: S^T <- exp(g_n) S^T + K^T Dt;  checkpoint
 template <int D>
 struct ScanSplit {
   static constexpr int NSP = D >= 64 ? 2 : 1;
@@ -408,7 +452,7 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
   // ---- operands of one chunk
   RowOp<IO> Kop[4][KSH], Qop[4][KSH];
   float Vv[4][4];
-  f32x4 vb[4], vbeg[4], vegs[MR], vedec[4];
+  f32x4 veg[4], vegs[MR];
   bf16x8 Tf[kFragCombos][NTF], Pf[MR][2][NTF], KTf[DTH][2][NTI];
   float egn;
 
@@ -433,10 +477,7 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
       for (int r = 0; r < 4; ++r) Vv[mt][r] = ld_elem<IO>(rv, v_off[r] + 16 * mt * vsb);
     const rsrc_t rr = rec_rsrc(c);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      vb[mt] = ld16f(rr, vec_lane + 64 * mt, Cfg::VEC_OFF + Cfg::V_B * CT * 4);
-      vbeg[mt] = ld16f(rr, vec_lane + 64 * mt, Cfg::VEC_OFF + Cfg::V_BEG * CT * 4);
-    }
+    for (int mt = 0; mt < 4; ++mt) veg[mt] = ld16f(rr, vec_lane + 64 * mt, Cfg::VEC_OFF + Cfg::V_EG * CT * 4);
 #pragma unroll
     for (int f = 0; f < kFragCombos; ++f)
 #pragma unroll
@@ -458,8 +499,6 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
   };
   auto load_D = [&](int c) {
     const rsrc_t rr = rec_rsrc(c);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) vedec[mt] = ld16f(rr, vec_lane + 64 * mt, Cfg::VEC_OFF + Cfg::V_EDEC * CT * 4);
 #pragma unroll
     for (int j = 0; j < DTH; ++j)
 #pragma unroll
@@ -534,33 +573,30 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
       }
     }
 
-    // ---- B: R = b V - b exp(g) X (zero past the chunk end: b = 0 there, V and X read
-    //      as zeros), Delta = T R over the nonzero k-steps of T
+    // ---- B: R' = V - exp(g) X (rows past the chunk end read as zeros, and the zero b
+    //      there zeroes their columns of T''), Dt = T'' R' over the nonzero k-steps
     load_C(c);
     issue_point();
     f32x4 R[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) R[mt][r] = fmaf(-vbeg[mt][r], X[mt][r], vb[mt][r] * Vv[mt][r]);
+      for (int r = 0; r < 4; ++r) R[mt][r] = fmaf(-veg[mt][r], X[mt][r], Vv[mt][r]);
     bf16x8 Rop[2][NTF];
     reg_operand<NTF>(R[0], R[1], Rop[0]);
     reg_operand<NTF>(R[2], R[3], Rop[1]);
-    f32x4 Dl[4];
+    f32x4 Dt[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) Dl[mt] = zero4();
+    for (int mt = 0; mt < 4; ++mt) Dt[mt] = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int mt = 2 * s; mt < 4; ++mt) mma_terms<NTF, NTF, ORD>(Dl[mt], Tf[frag_combo(mt, s)], Rop[s]);
+      for (int mt = 2 * s; mt < 4; ++mt) mma_terms<NTF, NTF, ORD>(Dt[mt], Tf[frag_combo(mt, s)], Rop[s]);
 
-    // ---- C: O = scale exp(g) Y + (scale P) Delta for this wave's row tiles
+    // ---- C: O = scale exp(g) Y + PT'' R' for this wave's row tiles
     load_D(c);
     issue_point();
     {
-      bf16x8 Dop[2][NTF];
-      reg_operand<NTF>(Dl[0], Dl[1], Dop[0]);
-      reg_operand<NTF>(Dl[2], Dl[3], Dop[1]);
       const rsrc_t ro = make_rsrc(p.o + cur.row * (int64_t)p.Hv * D + (int64_t)h * D + 16 * sl, (uint32_t)cur.len * osb);
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
@@ -570,21 +606,16 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
         for (int r = 0; r < 4; ++r) acc[r] = Ym[i][r] * vegs[i][r];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Dop[s]);
+          if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Rop[s]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) st4(ro, o_off[r] + 16 * mt * osb, acc[r]);
       }
     }
 
-    // ---- D: S^T <- exp(g_n) S^T + K^T (exp(g_n - g) o Delta) for this wave's tiles
+    // ---- D: S^T <- exp(g_n) S^T + K^T Dt for this wave's tiles
     load_A(nxt);
     issue_point();
     {
-      f32x4 Dt[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Dt[mt][r] = vedec[mt][r] * Dl[mt][r];
       bf16x8 Dtop[2][NTF];
       reg_operand<NTF>(Dt[0], Dt[1], Dtop[0]);
       reg_operand<NTF>(Dt[2], Dt[3], Dtop[1]);
@@ -795,15 +826,14 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     read_kq();
     // ---- operands of phase B
     float Vv[4][4];
-    f32x4 vb[4], vbeg[4];
+    f32x4 veg[4];
     bf16x8 Tf[kFragCombos][NTF];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         Vv[mt][r] = bf16_to_f32(*reinterpret_cast<const bf16_bits*>(Bc + v_rd + (16 * mt + 4 * grp + r) * VRB));
-      vb[mt] = vrow4(Bc, Cfg::V_B, mt);
-      vbeg[mt] = vrow4(Bc, Cfg::V_BEG, mt);
+      veg[mt] = vrow4(Bc, Cfg::V_EG, mt);
     }
 #pragma unroll
     for (int f = 0; f < kFragCombos; ++f)
@@ -871,28 +901,25 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     }
     issue_point();
 
-    // ---- B: R = b V - b exp(g) X (zero past the chunk end), Delta = T R
+    // ---- B: R' = V - exp(g) X, Dt = T'' R' over the nonzero k-steps
     f32x4 R[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) R[mt][r] = fmaf(-vbeg[mt][r], X[mt][r], vb[mt][r] * Vv[mt][r]);
+      for (int r = 0; r < 4; ++r) R[mt][r] = fmaf(-veg[mt][r], X[mt][r], Vv[mt][r]);
     bf16x8 Rop[2][NTF];
     reg_operand<NTF>(R[0], R[1], Rop[0]);
     reg_operand<NTF>(R[2], R[3], Rop[1]);
-    f32x4 Dl[4];
+    f32x4 Dt[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) Dl[mt] = zero4();
+    for (int mt = 0; mt < 4; ++mt) Dt[mt] = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int mt = 2 * s; mt < 4; ++mt) mma_terms<NTF, NTF, ORD>(Dl[mt], Tf[frag_combo(mt, s)], Rop[s]);
+      for (int mt = 2 * s; mt < 4; ++mt) mma_terms<NTF, NTF, ORD>(Dt[mt], Tf[frag_combo(mt, s)], Rop[s]);
 
     // ---- operands of phase D
-    f32x4 vedec[4];
     bf16x8 KTf[DTH][2][NTI];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) vedec[mt] = vrow4(Bc, Cfg::V_EDEC, mt);
 #pragma unroll
     for (int j = 0; j < DTH; ++j)
 #pragma unroll
@@ -902,11 +929,8 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     const float egn = *reinterpret_cast<const float*>(Bc + Cfg::EGN_OFF);
     issue_point();
 
-    // ---- C: O = scale exp(g) Y + (scale P) Delta for this wave's row tiles
+    // ---- C: O = scale exp(g) Y + PT'' R' for this wave's row tiles
     {
-      bf16x8 Dop[2][NTF];
-      reg_operand<NTF>(Dl[0], Dl[1], Dop[0]);
-      reg_operand<NTF>(Dl[2], Dl[3], Dop[1]);
       const rsrc_t ro = make_rsrc(p.o + cur.row * (int64_t)p.Hv * D + (int64_t)h * D + 16 * sl, (uint32_t)cur.len * osb);
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
@@ -916,19 +940,14 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
         for (int r = 0; r < 4; ++r) acc[r] = Ym[i][r] * vegs[i][r];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Dop[s]);
+          if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Rop[s]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) st4(ro, o_off[r] + 16 * mt * osb, acc[r]);
       }
     }
 
-    // ---- D: S^T <- exp(g_n) S^T + K^T (exp(g_n - g) o Delta) for this wave's tiles
+    // ---- D: S^T <- exp(g_n) S^T + K^T Dt for this wave's tiles
     {
-      f32x4 Dt[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Dt[mt][r] = vedec[mt][r] * Dl[mt][r];
       bf16x8 Dtop[2][NTF];
       reg_operand<NTF>(Dt[0], Dt[1], Dtop[0]);
       reg_operand<NTF>(Dt[2], Dt[3], Dtop[1]);
