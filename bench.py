@@ -43,23 +43,23 @@ PAGE_BYTES = BLOCK * 4096  # one attention page of 4,096 B per token
 
 def scan_algorithmic_flops(tokens, heads, d=D, c=CHUNK):
     """Products of the chunk scan, each counted once (not per bf16 pass), per token and
-    value head: K S^T, Q S^T and the state update K^T Delta (2 d^2 each), and the two
-    64 x 64 triangular products T R and P Delta (C d each, half of a full 2 C d)."""
+    value head: K S^T, Q S^T and the state update K^T Dt (2 d^2 each), and the two
+    64 x 64 triangular products T'' R' and PT'' R' (C d each, half of a full 2 C d)."""
     return tokens * heads * (6 * d * d + 2 * c * d)
 
 
 def scan_pass_flops(tokens, heads, d=D, c=CHUNK):
     """The same products weighted by the bf16 matrix-core passes they need with bf16
     inputs: an fp32 operand is two bf16 terms, so a bf16 x fp32 product (K S^T, Q S^T,
-    the update) is 2 passes and an fp32 x fp32 product (T R, P Delta) keeps 3 of the 4
+    the update) is 2 passes and an fp32 x fp32 product (T'' R', PT'' R') keeps 3 of the 4
     term pairs.  Time at the bf16 peak for this many flops is the kernel's MFMA roof."""
     return tokens * heads * (2 * 6 * d * d + 3 * 2 * c * d)
 
 
 def scan_issued_flops(tokens, heads, d=D, c=CHUNK):
     """Matrix-core flops the scan kernel actually issues (16x16x32 bf16 MFMAs): per 16-row
-    slab and chunk, 32 for K S^T, 32 for Q S^T, 2 x 18 for T R (both key halves form it),
-    18 for P Delta, 32 for the update."""
+    slab and chunk, 32 for K S^T, 32 for Q S^T, 2 x 18 for T'' R' (both key halves form
+    it), 18 for PT'' R', 32 for the update."""
     chunks = tokens // c
     return chunks * heads * (d // 16) * (32 + 32 + 36 + 18 + 32) * 16 * 16 * 32 * 2
 
@@ -267,7 +267,7 @@ def main():
                       "roof_us": round(dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
         "conv": {"us": round(conv_ms * 1e3, 2), "hbm_gbs": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1)},
         "roofline": {
-            "kernel": "scan_kernel<bf16,128>",
+            "kernel": "scan_staged_kernel<bf16,128>",
             "bound": "mfma",
             "achieved": round(achieved_tflops, 2),
             # the bf16 dense peak scaled by algorithmic / pass-weighted flops: the peak of
