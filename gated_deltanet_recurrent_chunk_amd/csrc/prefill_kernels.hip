@@ -157,126 +157,124 @@ __device__ __forceinline__ void row_terms(const RowOp<float>& o, bf16x8 (&t)[NT]
 }  // namespace
 
 // ==================================================================================
-// Pre-pass: one wave per (chunk, value head).
+// Pre-pass: one 4-wave workgroup per (chunk, value head).  Two workgroups fit a compute
+// unit (about 75 KiB of LDS each), so every SIMD runs two of these waves.
+//
+//   P0 (all waves)  key and query rows into LDS; wave 0 forms the gates g, exp(g), b,
+//                   exp(g_n - g) and writes the record's row vectors.
+//   P1 (per wave)   its share of A = strict-lower(b exp(g_t - g_s) K K^T) into LDS (five
+//                   tiles of the ten lower 16 x 16 tiles per wave, counting P's below),
+//                   the P fragments of its own row tile ut = W (kept in registers), and
+//                   K^T fragments.
+//   P2 (per wave)   columns 16 W .. 16 W + 15 of T = (I + A)^-1, block by block of 16
+//                   rows: block i's dependence on the earlier rows is one MFMA product
+//                   U = A[block i, 0 : 16 i] T[0 : 16 i, columns], then 16 rows of forward
+//                   substitution.  Writes those columns of T'' and those rows of T^T.
+//   P3 (per wave)   T'' fragments (a quarter each) and the PT'' fragments of row tile W.
+//
+// The blocked product runs on split bf16 terms like every other product (fp32 class for
+// bf16 inputs: two terms, order <= 1; fp32 inputs: three terms, order <= 2).
 template <typename IO, int D>
-__global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
+struct FactorLds {
   using Cfg = PrefillCfg<IO, D>;
+  static constexpr int KP = row_stride(D), TP = row_stride(CT);
+  static constexpr int KS = Cfg::NTI * CT * KP;  // bf16 elements of the key (or query) planes
+  static constexpr int TT = Cfg::NTF * CT * TP;  // bf16 elements of T^T (or T'') planes
+  static constexpr int QT = KS > TT ? KS : TT;   // query planes, later T''
+};
+
+// The ten lower 16 x 16 tiles of A, dealt 4, 3, 2, 1 to waves 0..3 (P's tiles of row
+// tile ut = W are 1, 2, 3, 4: five tiles per wave).
+__host__ __device__ constexpr int a_tile_mt(int i) { return i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 2 : 3; }
+__host__ __device__ constexpr int a_tile_nt(int i) { return i - (i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 3 : 6); }
+__host__ __device__ constexpr int a_tiles_begin(int w) { return w == 0 ? 0 : w == 1 ? 4 : w == 2 ? 7 : w == 3 ? 9 : 10; }
+
+template <typename IO, int D, int W>
+__device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const int n, uint8_t* rec,
+                                               bf16_bits* Ks, bf16_bits* QT, float (*As)[CT + 4], bf16_bits* Tt,
+                                               float (*Ub)[16], const float* vec) {
+  using Cfg = PrefillCfg<IO, D>;
+  using L = FactorLds<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
-  constexpr int KP = row_stride(D), TP = row_stride(CT);
+  constexpr int KP = L::KP, TP = L::TP;
   constexpr int KSD = (D + 31) / 32, DT = D / 16;
-  constexpr int VEC = 16 / sizeof(IO);
-  constexpr int PER_ROW = D / VEC;
-  constexpr int KS_BYTES = NTI * CT * KP * 2, TL_BYTES = NTF * CT * TP * 2, AS_BYTES = CT * (CT + 4) * 4;
-  constexpr int L0_BYTES = KS_BYTES > TL_BYTES ? KS_BYTES : TL_BYTES;
-  constexpr int L1A = KS_BYTES > AS_BYTES ? KS_BYTES : AS_BYTES;
-  constexpr int L1_BYTES = L1A > TL_BYTES ? L1A : TL_BYTES;
-  // L0: key rows, later T''; L1: query rows, later A, later T^T
-  __shared__ __attribute__((aligned(16))) uint8_t L0[L0_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t L1[L1_BYTES];
-  __shared__ float gl[CT];
-  __shared__ float vec_tmp[4 * CT];
-  __shared__ float vec_lds[2 * CT];
-  bf16_bits* Ks = reinterpret_cast<bf16_bits*>(L0);
-  bf16_bits* Qs = reinterpret_cast<bf16_bits*>(L1);
-  bf16_bits* Tl = reinterpret_cast<bf16_bits*>(L0);
-  bf16_bits* Tt = reinterpret_cast<bf16_bits*>(L1);
-  auto As = reinterpret_cast<float (*)[CT + 4]>(L1);
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const bf16_bits* Qs = QT;
 
-  const int c = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int grp = lane >> 4, col = lane & 15;
-  const ChunkDesc cd = p.chunks[c];
-  const int n = cd.len;
-  const int hk = h / p.group;
-  if constexpr (D < 32) {
-    // the kappa groups past a 16-wide row are contracted: keep them zero
-    zero_lds(L0, L0_BYTES, lane, 64);
-    zero_lds(L1, L1_BYTES, lane, 64);
-  }
-  __syncthreads();
-  // Every row load is issued before any is used: buffer loads whose descriptor ends at
-  // the chunk's last row, so rows past n read as zeros without a branch.
-  constexpr int PER_LANE = CT * PER_ROW / 64;
-  const uint32_t qsb = (uint32_t)p.qk_stride * sizeof(IO);
-  const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
-  const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
-  const rsrc_t ra = make_rsrc(p.a + cd.row * p.Hv + h, (uint32_t)n * p.Hv * 4);
-  const rsrc_t rb = make_rsrc(p.b + cd.row * p.Hv + h, (uint32_t)n * p.Hv * 4);
-  u32x4 kv[PER_LANE], qv[PER_LANE];
+  // ---------------------------------------------------------------- P1
+  // A tiles: acc = K_mt K_nt^T; element (t, s) with t = 16 mt + 4 grp + r, s = 16 nt + col
 #pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) {
-    const int idx = lane + 64 * i;
-    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    const uint32_t off = t * qsb + j0 * sizeof(IO);
-    kv[i] = ld16(rk, off, 0);
-    qv[i] = ld16(rq, off, 0);
-  }
-  const float av = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, lane * p.Hv * 4, 0, 0));
-  const float bb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, lane * p.Hv * 4, 0, 0));
+  for (int ti = a_tiles_begin(W); ti < a_tiles_begin(W + 1); ++ti) {
+    const int mt = a_tile_mt(ti), nt = a_tile_nt(ti);
+    f32x4 acc = zero4();
 #pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) {
-    const int idx = lane + 64 * i;
-    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    const uint4 k4{kv[i][0], kv[i][1], kv[i][2], kv[i][3]}, q4{qv[i][0], qv[i][1], qv[i][2], qv[i][3]};
-    store_row_terms<IO, NTI>(k4, Ks, CT * KP, KP, t, j0);
-    store_row_terms<IO, NTI>(q4, Qs, CT * KP, KP, t, j0);
-  }
-  const float la = lane < n ? __logf(av) : 0.f;  // rows past n: b = 0, log-decay 0
-  const float g = wave_inclusive_scan(la);        // rows past n keep g_{n-1}
-  gl[lane] = g;
-  __syncthreads();
-  uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
-
-  // ---- P fragments.  Tile (ms, mt) of P^T = K Q^T has the C layout "lane (col, grp)
-  //      holds P[16 mt + col][16 ms + 4 grp + r]", i.e. elements 0..3 (ms = 2s) or 4..7
-  //      (ms = 2s + 1) of the A operand of P for (mt, s).  Kept in registers: they are
-  //      the B operands of PT^T = T^T P^T below.
-  bf16x8 Pfr[kFragCombos][NTF];
+    for (int s = 0; s < KSD; ++s) {
+      bf16x8 a[NTI], b[NTI];
+      op_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
+      op_terms<NTI>(Ks, CT * KP, KP, 16 * nt + col, s, grp, b);
+      mma_terms<NTI, NTI, ORD>(acc, a, b);
+    }
+    const int sc = 16 * nt + col;
+    const float gs = vec[sc];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int s = 0; s <= (mt >> 1); ++s) {
-      const bool two = 2 * s + 1 <= mt;  // tile 2s+1 lies above the diagonal otherwise
-      f32x4 acc0 = zero4(), acc1 = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        bf16x8 bq[NTI], a0[NTI], a1[NTI];
-        op_terms<NTI>(Qs, CT * KP, KP, 16 * mt + col, ks, grp, bq);
-        op_terms<NTI>(Ks, CT * KP, KP, 32 * s + col, ks, grp, a0);
-        mma_terms<NTI, NTI, ORD>(acc0, a0, bq);
-        if (two) {
-          op_terms<NTI>(Ks, CT * KP, KP, 32 * s + 16 + col, ks, grp, a1);
-          mma_terms<NTI, NTI, ORD>(acc1, a1, bq);
-        }
-      }
-      const int t = 16 * mt + col;
-      const float gt = gl[t];
-      bf16_bits tt[8][NTF];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sp = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
-        const float dot = e < 4 ? acc0[e] : acc1[e - 4];
-        // the exponent g_t - g_s is <= 0 on the causal side kept by the select; the
-        // other side is computed and discarded
-        float dec = __expf(gt - gl[sp]);
-        asm volatile("" : "+v"(dec));  // computed for every element, see factorize_chunk
-        const float val = (sp <= t && t < n && (e < 4 || two)) ? p.scale * dec * dot : 0.f;
-        split_terms<NTF>(val, tt[e]);
-      }
-#pragma unroll
-      for (int i = 0; i < NTF; ++i) {
-        bf16_bits v8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
-        Pfr[frag_combo(mt, s)][i] = pack8(v8);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * mt + 4 * grp + r;
+      // computed for every element (pinned, so the LDS reads are not moved into a
+      // branch per element) and kept or dropped by the select
+      float dec = __expf(vec[t] - gs), bt = vec[2 * CT + t];
+      asm volatile("" : "+v"(dec), "+v"(bt));
+      As[t][sc] = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
     }
   }
 
-  // ---- K^T fragments: A operand of the state update.  Row col of tile jt is the key
-  //      column the scan keeps at register position (jt, col / 4, col % 4), kcol order;
-  //      contraction over the chunk rows t = kappa(s, grp, e).
+  // P fragments of row tile W: tile (ms, W) of P^T = K Q^T has the C layout "lane (col,
+  // grp) holds P[16 W + col][16 ms + 4 grp + r]", i.e. elements 0..3 (ms = 2s) or 4..7
+  // (ms = 2s + 1) of the A operand of P for (W, s).  They stay in registers: they are the
+  // B operands of PT^T = T^T P^T in P3.
+  constexpr int NPS = (W >> 1) + 1;
+  bf16x8 Pfr[NPS][NTF];
 #pragma unroll
-  for (int jt = 0; jt < DT; ++jt) {
+  for (int s = 0; s < NPS; ++s) {
+    const bool two = 2 * s + 1 <= W;  // tile 2s+1 lies above the diagonal otherwise
+    f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      bf16x8 bq[NTI], a0[NTI], a1[NTI];
+      op_terms<NTI>(Qs, CT * KP, KP, 16 * W + col, ks, grp, bq);
+      op_terms<NTI>(Ks, CT * KP, KP, 32 * s + col, ks, grp, a0);
+      mma_terms<NTI, NTI, ORD>(acc0, a0, bq);
+      if (two) {
+        op_terms<NTI>(Ks, CT * KP, KP, 32 * s + 16 + col, ks, grp, a1);
+        mma_terms<NTI, NTI, ORD>(acc1, a1, bq);
+      }
+    }
+    const int t = 16 * W + col;
+    const float gt = vec[t];
+    bf16_bits tt[8][NTF];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sp = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
+      const float dot = e < 4 ? acc0[e] : acc1[e - 4];
+      // the exponent g_t - g_s is <= 0 on the causal side kept by the select
+      float dec = __expf(gt - vec[sp]);
+      asm volatile("" : "+v"(dec));
+      const float val = (sp <= t && t < n && (e < 4 || two)) ? p.scale * dec * dot : 0.f;
+      split_terms<NTF>(val, tt[e]);
+    }
+#pragma unroll
+    for (int i = 0; i < NTF; ++i) {
+      bf16_bits v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
+      Pfr[s][i] = pack8(v8);
+    }
+  }
+
+  // K^T fragments of state tiles jt = W, W + 4, ...: row col of tile jt is the key column
+  // the scan keeps at register position (jt, col / 4, col % 4) (kcol order); contraction
+  // over the chunk rows t = kappa(s, grp, e)
+#pragma unroll
+  for (int jt = W; jt < DT; jt += 4) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -291,70 +289,241 @@ __global__ __launch_bounds__(64) void factorize_kernel(FactorizeArgs<IO> p) {
       }
     }
   }
+  __syncthreads();  // A complete; the query rows are read
 
-  // ---- row vectors and exp(g_n)
-  {
+  // ---------------------------------------------------------------- P2 (wave 0)
+  // Column j = lane of T, T[t][j] = [t == j] - sum_{s<t} A[t][s] T[s][j], block by block
+  // of 16 rows.  Finished rows overwrite A's rows in place (fp32, for P3) and become rows
+  // of T^T (bf16 terms, the B operands of the later blocks' products and of PT'').
+  if constexpr (W == 0) {
+    const int j = lane;
+    float Tc[CT];
+#pragma unroll
+    for (int i = 0; i < CT / 16; ++i) {
+      float U[16];
+      if (i > 0) {
+        // U = A[16 i + 0..15][0 : 16 i] T[0 : 16 i][0..63], four column tiles: A rows
+        // from LDS (fp32 split into terms; contraction elements at or past 16 i are the
+        // block's own triangle or above it and are dropped), T columns as rows of T^T
+        f32x4 u[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int sp = 0; sp < (16 * i + 31) / 32; ++sp) {
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 4 * grp]);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 16 + 4 * grp]);
+          const bool keep_hi = 32 * sp + 16 < 16 * i;  // the low run is always below 16 i
+          bf16x8 a[NTF];
+          reg_operand<NTF>(lo, keep_hi ? hi : zero4(), a);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            bf16x8 b[NTF];
+            op_terms<NTF>(Tt, CT * TP, TP, 16 * ct + col, sp, grp, b);
+            mma_terms<NTF, NTF, ORD>(u[ct], a, b);
+          }
+        }
+        // lane (col, grp) of tile ct holds U[4 grp + r][16 ct + col]: to lane j through LDS
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) *reinterpret_cast<f32x4*>(&Ub[16 * ct + col][4 * grp]) = u[ct];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&Ub[j][4 * q]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) U[4 * q + r] = v[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) U[r] = 0.f;
+      }
+      // forward substitution over the block's 16 rows (four interleaved partial sums
+      // added in a fixed order).  Coefficients are broadcast LDS reads, requested a group
+      // of four rows ahead of the sums that use them.
+      f32x4 cf[2][16];
+      auto fetch = [&](int g) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 4 * g + rr;
+#pragma unroll
+          for (int s4 = 0; s4 < r; s4 += 4)
+            cf[g & 1][4 * rr + s4 / 4] = *reinterpret_cast<const f32x4*>(&As[16 * i + r][16 * i + s4]);
+        }
+      };
+      fetch(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g + 1 < 4) fetch(g + 1);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 4 * g + rr, t = 16 * i + r;
+          float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < r; ++s) ps[s & 3] = fmaf(cf[g & 1][4 * rr + s / 4][s & 3], Tc[16 * i + s], ps[s & 3]);
+          Tc[t] = ((t == j ? 1.f : 0.f) - U[r]) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+        }
+      }
+      // rows 16 i .. 16 i + 15 of T^T row j (runs of four columns are contiguous in the
+      // swizzled order), and of T in place of A's rows (no longer read)
+#pragma unroll
+      for (int t0 = 16 * i; t0 < 16 * i + 16; t0 += 4) {
+        bf16_bits tt[4][NTF];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_terms<NTF>(Tc[t0 + e], tt[e]);
+#pragma unroll
+        for (int q = 0; q < NTF; ++q)
+          *reinterpret_cast<uint2*>(Tt + q * CT * TP + j * TP + swz(t0)) =
+              uint2{(uint32_t)tt[0][q] | ((uint32_t)tt[1][q] << 16), (uint32_t)tt[2][q] | ((uint32_t)tt[3][q] << 16)};
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) As[16 * i + r][j] = Tc[16 * i + r];
+    }
+  }
+  __syncthreads();  // T (fp32 rows in As) and T^T complete
+
+  // ---------------------------------------------------------------- P3
+  // T'' = diag(exp(g_n - g)) T diag(b) fragments of combos W, W + 4: lane (col, grp) of
+  // combo (mt, s) holds row t = 16 mt + col, columns kappa(s, grp, 0..7)
+#pragma unroll
+  for (int f = W; f < kFragCombos; f += 4) {
+    const int mt = f < 2 ? f : 2 + (f - 2) / 2, s = f < 2 ? 0 : (f - 2) % 2;
+    const int t = 16 * mt + col;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&As[t][32 * s + 4 * grp]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&As[t][32 * s + 16 + 4 * grp]);
+    const f32x4 blo = *reinterpret_cast<const f32x4*>(&vec[2 * CT + 32 * s + 4 * grp]);
+    const f32x4 bhi = *reinterpret_cast<const f32x4*>(&vec[2 * CT + 32 * s + 16 + 4 * grp]);
+    const float et = vec[3 * CT + t];
+    f32x4 v0, v1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v0[r] = (lo[r] * et) * blo[r];
+      v1[r] = (hi[r] * et) * bhi[r];
+    }
+    bf16x8 fr[NTF];
+    reg_operand<NTF>(v0, v1, fr);
+#pragma unroll
+    for (int q = 0; q < NTF; ++q)
+      *reinterpret_cast<bf16x8*>(rec + Cfg::T_OFF + (f * NTF + q) * 1024 + lane * 16) = fr[q];
+  }
+  // PT'' = (scale P) T diag(b) for row tile ut = W, through its transpose: tile (jt, W)
+  // of PT^T = T^T P^T, A = T^T rows (planes Tt), B = P^T, whose B operand at k-step s' is
+  // the A operand of P for (W, s').  Its C layout "lane (col, grp) holds
+  // PT[16 W + col][16 jt + 4 grp + r]" is elements 0..3 (jt = 2s) or 4..7 (jt = 2s + 1)
+  // of the A operand of PT'' for (W, s).  T^T[j][t'] is zero for t' < j and P[u][t'] for
+  // t' > u, so s' runs over jt/2 .. W/2.
+#pragma unroll
+  for (int s = 0; s < NPS; ++s) {
+    f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int jt = 2 * s + h2;
+      if (jt > W) continue;  // above the diagonal: zero
+#pragma unroll
+      for (int sp = jt >> 1; sp < NPS; ++sp) {
+        bf16x8 a[NTF];
+        op_terms<NTF>(Tt, CT * TP, TP, 16 * jt + col, sp, grp, a);
+        mma_terms<NTF, NTF, ORD>(acc[h2], a, Pfr[sp]);
+      }
+    }
+    bf16_bits tt[8][NTF];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float bj = vec[2 * CT + 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3)];
+      split_terms<NTF>(acc[e >> 2][e & 3] * bj, tt[e]);
+    }
+#pragma unroll
+    for (int q = 0; q < NTF; ++q) {
+      bf16_bits v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = tt[e][q];
+      *reinterpret_cast<bf16x8*>(rec + Cfg::P_OFF + (frag_combo(W, s) * NTF + q) * 1024 + lane * 16) = pack8(v8);
+    }
+  }
+}
+
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
+  using Cfg = PrefillCfg<IO, D>;
+  using L = FactorLds<IO, D>;
+  constexpr int NTI = Cfg::NTI;
+  constexpr int KP = L::KP;
+  constexpr int VEC = 16 / sizeof(IO);
+  constexpr int PER_ROW = D / VEC;
+  constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + 255) / 256;
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[L::KS];
+  __shared__ __attribute__((aligned(16))) bf16_bits QT[L::QT];  // query rows, later T''
+  __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
+  __shared__ __attribute__((aligned(16))) bf16_bits Tt[L::TT];
+  __shared__ __attribute__((aligned(16))) float Ub[CT][16];
+  __shared__ __attribute__((aligned(16))) float vec[4 * CT];  // g, exp(g), b, exp(g_n - g)
+
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const ChunkDesc cd = uniform_chunk(p.chunks + c);
+  const int n = cd.len;
+  const int hk = h / p.group;
+  uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
+
+  // The blocked product of P2 contracts rows of T^T beyond the rows written so far (its
+  // A operand is zero there): they must hold zeros, not stale bits.  For d < 32 the kappa
+  // groups past a 16-wide key row are contracted too.
+  zero_lds(Tt, sizeof(Tt), tid, 256);
+  if constexpr (D < 32) {
+    zero_lds(Ks, sizeof(Ks), tid, 256);
+    zero_lds(QT, sizeof(QT), tid, 256);
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- P0
+  // every row load first: buffer loads whose descriptor ends at the chunk's last row, so
+  // rows past n read as zeros without a branch
+  const uint32_t qsb = (uint32_t)p.qk_stride * sizeof(IO);
+  const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
+  const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
+  u32x4 kv[PER_THR], qv[PER_THR];
+#pragma unroll
+  for (int i = 0; i < PER_THR; ++i) {
+    const int idx = tid + 256 * i;
+    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    // pieces past the tile (small d) read past the descriptor's end: zeros, not stored
+    const uint32_t off = idx < PIECES ? t * qsb + j0 * sizeof(IO) : 0xFFFFFFF0u & (n * qsb + 16u);
+    kv[i] = ld16(rk, off, 0);
+    qv[i] = ld16(rq, off, 0);
+  }
+  float av = 1.f, bb = 0.f;
+  if (wave == 0) {
+    const rsrc_t ra = make_rsrc(p.a + cd.row * p.Hv + h, (uint32_t)n * p.Hv * 4);
+    const rsrc_t rb = make_rsrc(p.b + cd.row * p.Hv + h, (uint32_t)n * p.Hv * 4);
+    av = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, lane * p.Hv * 4, 0, 0));
+    bb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, lane * p.Hv * 4, 0, 0));
+  }
+#pragma unroll
+  for (int i = 0; i < PER_THR; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < PIECES) {
+      const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+      const uint4 k4{kv[i][0], kv[i][1], kv[i][2], kv[i][3]}, q4{qv[i][0], qv[i][1], qv[i][2], qv[i][3]};
+      store_row_terms<IO, NTI>(k4, Ks, CT * KP, KP, t, j0);
+      store_row_terms<IO, NTI>(q4, QT, CT * KP, KP, t, j0);
+    }
+  }
+  if (wave == 0) {
+    const float la = lane < n ? __logf(av) : 0.f;  // rows past n: b = 0, log-decay 0
+    const float g = wave_inclusive_scan(la);        // rows past n keep g_{n-1}
     const float gn = __shfl(g, n - 1, 64);
     const float eg = __expf(g);
+    vec[lane] = g;
+    vec[CT + lane] = eg;
+    vec[2 * CT + lane] = bb;
+    vec[3 * CT + lane] = lane < n ? __expf(gn - g) : 0.f;
     float* vo = reinterpret_cast<float*>(rec + Cfg::VEC_OFF);
     vo[Cfg::V_EG * CT + lane] = eg;
     vo[Cfg::V_EGS * CT + lane] = p.scale * eg;
     if (lane == 0) *reinterpret_cast<float*>(rec + Cfg::EGN_OFF) = __expf(gn);
   }
-
-  // ---- T = (I + A)^-1: T'' = diag(exp(g_n - g)) T diag(b) over the key rows, T^T over
-  //      the query rows (both are read by then)
-  factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks, CT * KP, As, n, g, bb, Tl, CT * TP, TP, vec_tmp, vec_lds, Tt);
   __syncthreads();
 
-  // ---- PT'' = (scale P) T diag(b), through its transpose: tile (jt, ut) of
-  //      PT^T = T^T P^T, with A = T^T rows (planes Tt) and B = P^T, whose B operand at
-  //      k-step s' is the A operand of P for (ut, s').  Its C layout "lane (col, grp)
-  //      holds PT[16 ut + col][16 jt + 4 grp + r]" is elements 0..3 (jt = 2s) or 4..7
-  //      (jt = 2s + 1) of the A operand of PT'' for (ut, s).  T^T[j][t'] is zero for
-  //      t' < j and P[u][t'] for t' > u, so s' runs over jt/2 .. ut/2.
-#pragma unroll
-  for (int ut = 0; ut < 4; ++ut) {
-#pragma unroll
-    for (int s = 0; s <= (ut >> 1); ++s) {
-      f32x4 acc[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int jt = 2 * s + h2;
-        if (jt > ut) continue;  // above the diagonal: zero
-#pragma unroll
-        for (int sp = jt >> 1; sp <= (ut >> 1); ++sp) {
-          bf16x8 a[NTF];
-          op_terms<NTF>(Tt, CT * TP, TP, 16 * jt + col, sp, grp, a);
-          mma_terms<NTF, NTF, ORD>(acc[h2], a, Pfr[frag_combo(ut, sp)]);
-        }
-      }
-      bf16_bits tt[8][NTF];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float bj = vec_tmp[2 * CT + 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3)];
-        split_terms<NTF>(acc[e >> 2][e & 3] * bj, tt[e]);
-      }
-#pragma unroll
-      for (int i = 0; i < NTF; ++i) {
-        bf16_bits v8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
-        *reinterpret_cast<bf16x8*>(rec + Cfg::P_OFF + (frag_combo(ut, s) * NTF + i) * 1024 + lane * 16) =
-            pack8(v8);
-      }
-    }
-  }
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int s = 0; s <= (mt >> 1); ++s) {
-#pragma unroll
-      for (int i = 0; i < NTF; ++i) {
-        const bf16x8 v = op_read(Tl + i * CT * TP, TP, 16 * mt + col, s, grp);
-        *reinterpret_cast<bf16x8*>(rec + Cfg::T_OFF + (frag_combo(mt, s) * NTF + i) * 1024 + lane * 16) = v;
-      }
-    }
+  switch (wave) {
+    case 0: factorize_wave<IO, D, 0>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
+    case 1: factorize_wave<IO, D, 1>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
+    case 2: factorize_wave<IO, D, 2>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
+    default: factorize_wave<IO, D, 3>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
   }
 }
 
@@ -1019,7 +1188,7 @@ template <typename IO, int D>
 static hipError_t launch_factorize_t(const FactorizeArgs<IO>& a, int n_chunks, hipStream_t st) {
   if (n_chunks == 0) return hipSuccess;
   dim3 grid(n_chunks, a.Hv);
-  hipLaunchKernelGGL((factorize_kernel<IO, D>), grid, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((factorize_kernel<IO, D>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
