@@ -23,6 +23,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace gdn {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -131,6 +134,22 @@ __device__ __forceinline__ void reg_operand(const f32x4& v0, const f32x4& v1, bf
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{}).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Lane S of each 16-lane row of the wave, broadcast to the whole row (DPP row_newbcast).
+template <int S>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + S, 0xF, 0xF, true));
+}
 
 // Wave-wide inclusive prefix sum (64 lanes), fixed combination order.
 __device__ __forceinline__ float wave_inclusive_scan(float x) {

@@ -166,11 +166,12 @@ __device__ __forceinline__ void row_terms(const RowOp<float>& o, bf16x8 (&t)[NT]
 //                   tiles of the ten lower 16 x 16 tiles per wave, counting P's below),
 //                   the P fragments of its own row tile ut = W (kept in registers), and
 //                   K^T fragments.
-//   P2 (per wave)   columns 16 W .. 16 W + 15 of T = (I + A)^-1, block by block of 16
-//                   rows: block i's dependence on the earlier rows is one MFMA product
-//                   U = A[block i, 0 : 16 i] T[0 : 16 i, columns], then 16 rows of forward
-//                   substitution.  Writes those columns of T'' and those rows of T^T.
-//   P3 (per wave)   T'' fragments (a quarter each) and the PT'' fragments of row tile W.
+//   P2              T = (I + A)^-1 by 16-row blocks: one wave inverts the four 16 x 16
+//                   diagonal blocks at once; then each wave forms block row i of its 16
+//                   columns as T_ii (E_i - U_i), U_i = A[block i, 0 : 16 i] T[0 : 16 i, :],
+//                   both products on MFMA with the earlier blocks kept in registers.
+//                   Writes T^T rows and T'' (bf16 terms).
+//   P3 (per wave)   T'' fragments and the PT'' fragments of row tile W.
 //
 // The blocked product runs on split bf16 terms like every other product (fp32 class for
 // bf16 inputs: two terms, order <= 1; fp32 inputs: three terms, order <= 2).
@@ -192,7 +193,7 @@ __host__ __device__ constexpr int a_tiles_begin(int w) { return w == 0 ? 0 : w =
 template <typename IO, int D, int W>
 __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const int n, uint8_t* rec,
                                                bf16_bits* Ks, bf16_bits* QT, float (*As)[CT + 4], bf16_bits* Tt,
-                                               float (*Ub)[16], const float* vec) {
+                                               float (*Ub)[24], const float* vec, const int p2_wave) {
   using Cfg = PrefillCfg<IO, D>;
   using L = FactorLds<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
@@ -200,6 +201,8 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
   constexpr int KSD = (D + 31) / 32, DT = D / 16;
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
   const bf16_bits* Qs = QT;
+  bf16_bits* Tl = QT;                                 // T'' planes, once P1 has read the query rows
+  bf16_bits* Td = reinterpret_cast<bf16_bits*>(Ub);  // T_ii planes
 
   // ---------------------------------------------------------------- P1
   // A tiles: acc = K_mt K_nt^T; element (t, s) with t = 16 mt + 4 grp + r, s = 16 nt + col
@@ -291,115 +294,104 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
   }
   __syncthreads();  // A complete; the query rows are read
 
-  // ---------------------------------------------------------------- P2 (wave 0)
-  // Column j = lane of T, T[t][j] = [t == j] - sum_{s<t} A[t][s] T[s][j], block by block
-  // of 16 rows.  Finished rows overwrite A's rows in place (fp32, for P3) and become rows
-  // of T^T (bf16 terms, the B operands of the later blocks' products and of PT'').
-  if constexpr (W == 0) {
-    const int j = lane;
-    float Tc[CT];
+  // ---------------------------------------------------------------- P2
+  // T = (I + A)^-1 by blocks of 16 rows.  With A_ii the diagonal blocks and
+  // U_i = A[block i, 0 : 16 i] T[0 : 16 i, :], block row i of T is T_ii (E_i - U_i),
+  // T_ii = (I + A_ii)^-1.
+  //
+  // P2a (one wave; which one rotates with the workgroup): the four T_ii at once, lane
+  // 16 bi + c owning column c of T_bi,bi, forward substitution over 16 rows whose
+  // coefficients A[16 bi + r][16 bi + s] come from lane (bi, s) of the same 16-lane row
+  // (a DPP broadcast within the row).  Written as bf16 terms, row-major, to Td.
+  if (W == p2_wave) {
+    const int bi = lane >> 4, c = lane & 15;
+    float R[16], X[16];
 #pragma unroll
-    for (int i = 0; i < CT / 16; ++i) {
-      float U[16];
-      if (i > 0) {
-        // U = A[16 i + 0..15][0 : 16 i] T[0 : 16 i][0..63], four column tiles: A rows
-        // from LDS (fp32 split into terms; contraction elements at or past 16 i are the
-        // block's own triangle or above it and are dropped), T columns as rows of T^T
-        f32x4 u[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int r = 0; r < 16; ++r) R[r] = As[16 * bi + r][16 * bi + c];
 #pragma unroll
-        for (int sp = 0; sp < (16 * i + 31) / 32; ++sp) {
-          const f32x4 lo = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 4 * grp]);
-          const f32x4 hi = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 16 + 4 * grp]);
-          const bool keep_hi = 32 * sp + 16 < 16 * i;  // the low run is always below 16 i
-          bf16x8 a[NTF];
-          reg_operand<NTF>(lo, keep_hi ? hi : zero4(), a);
+    for (int r = 0; r < 16; ++r) {
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      static_for<16>([&](auto sc) {
+        constexpr int sv = decltype(sc)::value;
+        if (sv < r) ps[sv & 3] = fmaf(row_bcast<sv>(R[r]), X[sv], ps[sv & 3]);
+      });
+      X[r] = (r == c ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    }
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            bf16x8 b[NTF];
-            op_terms<NTF>(Tt, CT * TP, TP, 16 * ct + col, sp, grp, b);
-            mma_terms<NTF, NTF, ORD>(u[ct], a, b);
-          }
-        }
-        // lane (col, grp) of tile ct holds U[4 grp + r][16 ct + col]: to lane j through LDS
+    for (int r = 0; r < 16; ++r) {
+      bf16_bits tt[NTF];
+      split_terms<NTF>(X[r], tt);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) *reinterpret_cast<f32x4*>(&Ub[16 * ct + col][4 * grp]) = u[ct];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(&Ub[j][4 * q]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) U[4 * q + r] = v[r];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) U[r] = 0.f;
-      }
-      // forward substitution over the block's 16 rows (four interleaved partial sums
-      // added in a fixed order).  Coefficients are broadcast LDS reads, requested a group
-      // of four rows ahead of the sums that use them.
-      f32x4 cf[2][16];
-      auto fetch = [&](int g) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 4 * g + rr;
-#pragma unroll
-          for (int s4 = 0; s4 < r; s4 += 4)
-            cf[g & 1][4 * rr + s4 / 4] = *reinterpret_cast<const f32x4*>(&As[16 * i + r][16 * i + s4]);
-        }
-      };
-      fetch(0);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g + 1 < 4) fetch(g + 1);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 4 * g + rr, t = 16 * i + r;
-          float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < r; ++s) ps[s & 3] = fmaf(cf[g & 1][4 * rr + s / 4][s & 3], Tc[16 * i + s], ps[s & 3]);
-          Tc[t] = ((t == j ? 1.f : 0.f) - U[r]) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-        }
-      }
-      // rows 16 i .. 16 i + 15 of T^T row j (runs of four columns are contiguous in the
-      // swizzled order), and of T in place of A's rows (no longer read)
-#pragma unroll
-      for (int t0 = 16 * i; t0 < 16 * i + 16; t0 += 4) {
-        bf16_bits tt[4][NTF];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_terms<NTF>(Tc[t0 + e], tt[e]);
-#pragma unroll
-        for (int q = 0; q < NTF; ++q)
-          *reinterpret_cast<uint2*>(Tt + q * CT * TP + j * TP + swz(t0)) =
-              uint2{(uint32_t)tt[0][q] | ((uint32_t)tt[1][q] << 16), (uint32_t)tt[2][q] | ((uint32_t)tt[3][q] << 16)};
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) As[16 * i + r][j] = Tc[16 * i + r];
+      for (int q = 0; q < NTF; ++q) Td[((q * 4 + bi) * 16 + r) * 16 + c] = tt[q];
     }
   }
-  __syncthreads();  // T (fp32 rows in As) and T^T complete
+  __syncthreads();  // T_ii complete
+
+  // P2b (every wave, column tile W): block rows of T in MFMA C layout, lane (col, grp)
+  // holding T[16 i + 4 grp + r][16 W + col].  A C-layout tile is directly elements 0..3
+  // of the B operand over its 16 rows, so the earlier blocks feed U_i and E_i - U_i
+  // feeds the product by T_ii without leaving registers.
+  {
+    f32x4 Tb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 u = zero4();
+#pragma unroll
+      for (int sp = 0; sp < (16 * i + 31) / 32; ++sp) {
+        // A rows 16 i + col (fp32, split into terms); contraction elements at or past
+        // 16 i are the block's own triangle or above it and are dropped
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 4 * grp]);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 16 + 4 * grp]);
+        const bool keep_hi = 32 * sp + 16 < 16 * i;
+        bf16x8 a[NTF], b[NTF];
+        reg_operand<NTF>(lo, keep_hi ? hi : zero4(), a);
+        reg_operand<NTF>(Tb[2 * sp], keep_hi ? Tb[2 * sp + 1] : zero4(), b);
+        mma_terms<NTF, NTF, ORD>(u, a, b);
+      }
+      f32x4 em;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) em[r] = (16 * i + 4 * grp + r == 16 * W + col ? 1.f : 0.f) - u[r];
+      bf16x8 tii[NTF], e_op[NTF];
+#pragma unroll
+      for (int q = 0; q < NTF; ++q) {
+        // A operand of T_ii: row col, columns 4 grp .. + 3 (contraction past 16 is zero)
+        const uint2 w = *reinterpret_cast<const uint2*>(&Td[((q * 4 + i) * 16 + col) * 16 + 4 * grp]);
+        tii[q] = __builtin_bit_cast(bf16x8, u32x4{w.x, w.y, 0u, 0u});
+      }
+      reg_operand<NTF>(em, zero4(), e_op);
+      Tb[i] = zero4();
+      mma_terms<NTF, NTF, ORD>(Tb[i], tii, e_op);
+      // row 16 W + col of T^T (columns 16 i + 4 grp .. + 3, contiguous in the swizzled
+      // order), and T''[t][j] = exp(g_n - g_t) T[t][j] b_j into the T'' planes
+      bf16_bits tt[4][NTF];
+      const float bj = vec[2 * CT + 16 * W + col];
+      const int pc = swz(16 * W + col);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) split_terms<NTF>(Tb[i][r], tt[r]);
+#pragma unroll
+      for (int q = 0; q < NTF; ++q)
+        *reinterpret_cast<uint2*>(Tt + q * CT * TP + (16 * W + col) * TP + swz(16 * i + 4 * grp)) =
+            uint2{(uint32_t)tt[0][q] | ((uint32_t)tt[1][q] << 16), (uint32_t)tt[2][q] | ((uint32_t)tt[3][q] << 16)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * i + 4 * grp + r;
+        bf16_bits t2[NTF];
+        split_terms<NTF>((Tb[i][r] * vec[3 * CT + t]) * bj, t2);
+#pragma unroll
+        for (int q = 0; q < NTF; ++q) Tl[q * CT * TP + t * TP + pc] = t2[q];
+      }
+    }
+  }
+  __syncthreads();  // T'' and T^T complete
 
   // ---------------------------------------------------------------- P3
-  // T'' = diag(exp(g_n - g)) T diag(b) fragments of combos W, W + 4: lane (col, grp) of
-  // combo (mt, s) holds row t = 16 mt + col, columns kappa(s, grp, 0..7)
+  // T'' fragments: combo f, term q for items W, W + 4, ...
 #pragma unroll
-  for (int f = W; f < kFragCombos; f += 4) {
+  for (int it = W; it < kFragCombos * NTF; it += 4) {
+    const int f = it / NTF, q = it % NTF;
     const int mt = f < 2 ? f : 2 + (f - 2) / 2, s = f < 2 ? 0 : (f - 2) % 2;
-    const int t = 16 * mt + col;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(&As[t][32 * s + 4 * grp]);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(&As[t][32 * s + 16 + 4 * grp]);
-    const f32x4 blo = *reinterpret_cast<const f32x4*>(&vec[2 * CT + 32 * s + 4 * grp]);
-    const f32x4 bhi = *reinterpret_cast<const f32x4*>(&vec[2 * CT + 32 * s + 16 + 4 * grp]);
-    const float et = vec[3 * CT + t];
-    f32x4 v0, v1;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v0[r] = (lo[r] * et) * blo[r];
-      v1[r] = (hi[r] * et) * bhi[r];
-    }
-    bf16x8 fr[NTF];
-    reg_operand<NTF>(v0, v1, fr);
-#pragma unroll
-    for (int q = 0; q < NTF; ++q)
-      *reinterpret_cast<bf16x8*>(rec + Cfg::T_OFF + (f * NTF + q) * 1024 + lane * 16) = fr[q];
+    const bf16x8 v = op_read(Tl + q * CT * TP, TP, 16 * mt + col, s, grp);
+    *reinterpret_cast<bf16x8*>(rec + Cfg::T_OFF + it * 1024 + lane * 16) = v;
   }
   // PT'' = (scale P) T diag(b) for row tile ut = W, through its transpose: tile (jt, W)
   // of PT^T = T^T P^T, A = T^T rows (planes Tt), B = P^T, whose B operand at k-step s' is
@@ -450,7 +442,7 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   __shared__ __attribute__((aligned(16))) bf16_bits QT[L::QT];  // query rows, later T''
   __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
   __shared__ __attribute__((aligned(16))) bf16_bits Tt[L::TT];
-  __shared__ __attribute__((aligned(16))) float Ub[CT][16];
+  __shared__ __attribute__((aligned(16))) float Ub[CT][24];  // T_ii planes (bf16 terms)
   __shared__ __attribute__((aligned(16))) float vec[4 * CT];  // g, exp(g), b, exp(g_n - g)
 
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
@@ -460,15 +452,12 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   const int hk = h / p.group;
   uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
 
-  // The blocked product of P2 contracts rows of T^T beyond the rows written so far (its
-  // A operand is zero there): they must hold zeros, not stale bits.  For d < 32 the kappa
-  // groups past a 16-wide key row are contracted too.
-  zero_lds(Tt, sizeof(Tt), tid, 256);
+  // For d < 32 the kappa groups past a 16-wide key row are contracted: keep them zero.
   if constexpr (D < 32) {
     zero_lds(Ks, sizeof(Ks), tid, 256);
     zero_lds(QT, sizeof(QT), tid, 256);
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---------------------------------------------------------------- P0
   // every row load first: buffer loads whose descriptor ends at the chunk's last row, so
@@ -519,11 +508,12 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   }
   __syncthreads();
 
+  const int p2_wave = (blockIdx.x + blockIdx.y) & 3;
   switch (wave) {
-    case 0: factorize_wave<IO, D, 0>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
-    case 1: factorize_wave<IO, D, 1>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
-    case 2: factorize_wave<IO, D, 2>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
-    default: factorize_wave<IO, D, 3>(p, n, rec, Ks, QT, As, Tt, Ub, vec); break;
+    case 0: factorize_wave<IO, D, 0>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
+    case 1: factorize_wave<IO, D, 1>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
+    case 2: factorize_wave<IO, D, 2>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
+    default: factorize_wave<IO, D, 3>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
   }
 }
 
