@@ -818,7 +818,15 @@ struct ScanStaged {
   static constexpr int NS = D / 16, NSP = 2, SP = 2, NW = SP * NSP, NG = NS / SP;
 };
 
-__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, uint32_t voff) {
+// LDS addresses of the staged scan are kept in the LDS address space: a generic pointer
+// converted back costs a null check per copy.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_u8* p) {
+  return *(const __attribute__((address_space(3))) T*)p;
+}
+
+__device__ __forceinline__ void dma16(rsrc_t r, lds_u8* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
 }
 
@@ -826,8 +834,8 @@ __device__ __forceinline__ void dma16(rsrc_t r, const void* lds, uint32_t voff) 
 // Q % 2), compiled once per wave index so that every register index and every copy
 // assignment is a constant.
 template <typename IO, int D, int Q>
-__device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const int u, const int sg, uint8_t* stage0,
-                                                 uint8_t* stage1, uint8_t* kqs, f32x4* xch) {
+__device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const int u, const int sg, lds_u8* stage0,
+                                                 lds_u8* stage1, lds_u8* kqs, f32x4* xch) {
   using Cfg = PrefillCfg<IO, D>;
   using Shp = ScanStaged<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
@@ -914,7 +922,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   //      bounds of both descriptors are in the per-lane offset: lanes past the record
   //      or past the chunk's last row write zeros.
   const IO* v_pair = p.v + (int64_t)h * D + 16 * SP * sg;
-  auto stage_chunk = [&](const ChunkDesc& cd, int c, const uint8_t* B) {
+  auto stage_chunk = [&](const ChunkDesc& cd, int c, lds_u8* B) {
     const rsrc_t rr = make_rsrc(p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
     const rsrc_t rv = make_rsrc(v_pair + cd.row * p.v_stride, (uint32_t)cd.len * vsb);
 #pragma unroll
@@ -949,15 +957,15 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       for (int mt = 0; mt < 4; ++mt) {
         const int r = 16 * mt + col;
         const int off = r * RB + 16 * ((grp + 4 * (s0 + s)) ^ (r % PPR));
-        Kop[mt][s].v = *reinterpret_cast<const bf16x8*>(kqs + off);
-        Qop[mt][s].v = *reinterpret_cast<const bf16x8*>(kqs + 64 * RB + off);
+        Kop[mt][s].v = lds_load<bf16x8>(kqs + off);
+        Qop[mt][s].v = lds_load<bf16x8>(kqs + 64 * RB + off);
       }
   };
-  auto frag = [&](const uint8_t* B, int off, int f) {
-    return *reinterpret_cast<const bf16x8*>(B + off + 1024 * f + 16 * lane);
+  auto frag = [&](const lds_u8* B, int off, int f) {
+    return lds_load<bf16x8>(B + off + 1024 * f + 16 * lane);
   };
-  auto vrow4 = [&](const uint8_t* B, int plane, int mt) {  // rows 16 mt + 4 grp .. + 3 of a vector plane
-    return *reinterpret_cast<const f32x4*>(B + Cfg::VEC_OFF + plane * CT * 4 + 64 * mt + 16 * grp);
+  auto vrow4 = [&](const lds_u8* B, int plane, int mt) {  // rows 16 mt + 4 grp .. + 3 of a vector plane
+    return lds_load<f32x4>(B + Cfg::VEC_OFF + plane * CT * 4 + 64 * mt + 16 * grp);
   };
   auto issue_point = [] { __builtin_amdgcn_sched_barrier(0); };
 
@@ -966,38 +974,21 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   stage_chunk(cur, cb, stage0);
   stage_kq(cur);
 
-  auto step = [&](const int c, const uint8_t* Bc, const uint8_t* Bn) {
+  auto step = [&](const int c, const lds_u8* Bc, lds_u8* Bn) {
     const bool more = c + 1 < ce;
     const ChunkDesc nxt = to_desc(nxt_raw);
-    {
-      // wait for this wave's copies into Bc and kqs (the compiler counts LDS DMA per
-      // LDS object)
-      const float probe = *(const __attribute__((address_space(3))) float*)(Bc + 16 * lane);
-      const float probe_kq = *(const __attribute__((address_space(3))) float*)(kqs + 16 * lane);
-      asm volatile("" ::"v"(probe), "v"(probe_kq));
-    }
-    lds_barrier();
+    // Every wave's copies of this chunk (into Bc and kqs) have landed once each wave has
+    // waited for all of its own vector memory operations and passed the barrier.  The
+    // wait is explicit: the compiler's own count of outstanding LDS DMA follows the
+    // data a wave reads itself, not the copies its partners read.  The copies were
+    // issued most of a chunk earlier, so the wait rarely stalls.
+    full_barrier();
     // (the last chunk stages itself again: every path issues the same copies, so the
     // compiler's counts of outstanding loads stay exact)
     stage_chunk(nxt, more ? c + 1 : c, Bn);
     nxt_raw = chunk_raw(c + 2 < ce ? c + 2 : c + 1 - (more ? 0 : 1));
 
     read_kq();
-    // ---- operands of phase B
-    float Vv[4][4];
-    f32x4 veg[4];
-    bf16x8 Tf[kFragCombos][NTF];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Vv[mt][r] = bf16_to_f32(*reinterpret_cast<const bf16_bits*>(Bc + v_rd + (16 * mt + 4 * grp + r) * VRB));
-      veg[mt] = vrow4(Bc, Cfg::V_EG, mt);
-    }
-#pragma unroll
-    for (int f = 0; f < kFragCombos; ++f)
-#pragma unroll
-      for (int i = 0; i < NTF; ++i) Tf[f][i] = frag(Bc, Cfg::T_OFF, f * NTF + i);
     issue_point();
 
     // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains
@@ -1020,6 +1011,9 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     issue_point();
     // add the partner's partial sums: X for all rows, Y for this wave's output rows
     f32x4 Ym[MR];
+    float Vv[4][4];
+    f32x4 veg[4];
+    bf16x8 Tf[kFragCombos][NTF];
     {
       f32x4* mine = xch + ((jj * NSP + w) * 6) * 64 + lane;
       const f32x4* other = xch + ((jj * NSP + (w ^ 1)) * 6) * 64 + lane;
@@ -1027,6 +1021,18 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       for (int mt = 0; mt < 4; ++mt) mine[mt * 64] = X[mt];
 #pragma unroll
       for (int i = 0; i < MR; ++i) mine[(4 + i) * 64] = Y[MR * (w ^ 1) + i];
+      // operands of phase B, requested here: the barrier's wait covers their latency
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Vv[mt][r] = bf16_to_f32(lds_load<bf16_bits>(Bc + v_rd + (16 * mt + 4 * grp + r) * VRB));
+        veg[mt] = vrow4(Bc, Cfg::V_EG, mt);
+      }
+#pragma unroll
+      for (int f = 0; f < kFragCombos; ++f)
+#pragma unroll
+        for (int i = 0; i < NTF; ++i) Tf[f][i] = frag(Bc, Cfg::T_OFF, f * NTF + i);
       lds_barrier();
       // every wave has read this chunk's key and query rows: copy the next chunk's
       // (the last chunk copies its own again, so that every path issues the same copies)
@@ -1045,21 +1051,6 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       }
     }
 
-    // ---- operands of phase C
-    f32x4 vegs[MR];
-    bf16x8 Pf[MR][2][NTF];
-#pragma unroll
-    for (int i = 0; i < MR; ++i) {
-      const int mt = mt0 + i;
-      vegs[i] = vrow4(Bc, Cfg::V_EGS, mt);
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        if (s <= (mt >> 1))
-#pragma unroll
-          for (int t = 0; t < NTF; ++t) Pf[i][s][t] = frag(Bc, Cfg::P_OFF, frag_combo(mt, s) * NTF + t);
-    }
-    issue_point();
-
     // ---- B: R' = V - exp(g) X, Dt = T'' R' over the nonzero k-steps
     f32x4 R[4];
 #pragma unroll
@@ -1077,15 +1068,19 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
 #pragma unroll
       for (int mt = 2 * s; mt < 4; ++mt) mma_terms<NTF, NTF, ORD>(Dt[mt], Tf[frag_combo(mt, s)], Rop[s]);
 
-    // ---- operands of phase D
-    bf16x8 KTf[DTH][2][NTI];
+    // ---- operands of phase C, requested while the products above run
+    f32x4 vegs[MR];
+    bf16x8 Pf[MR][2][NTF];
 #pragma unroll
-    for (int j = 0; j < DTH; ++j)
+    for (int i = 0; i < MR; ++i) {
+      const int mt = mt0 + i;
+      vegs[i] = vrow4(Bc, Cfg::V_EGS, mt);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
+        if (s <= (mt >> 1))
 #pragma unroll
-        for (int i = 0; i < NTI; ++i) KTf[j][s][i] = frag(Bc, Cfg::KT_OFF, ((jt0 + j) * 2 + s) * NTI + i);
-    const float egn = *reinterpret_cast<const float*>(Bc + Cfg::EGN_OFF);
+          for (int t = 0; t < NTF; ++t) Pf[i][s][t] = frag(Bc, Cfg::P_OFF, frag_combo(mt, s) * NTF + t);
+    }
     issue_point();
 
     // ---- C: O = scale exp(g) Y + PT'' R' for this wave's row tiles
@@ -1104,6 +1099,17 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
         for (int r = 0; r < 4; ++r) st4(ro, o_off[r] + 16 * mt * osb, acc[r]);
       }
     }
+
+    // ---- operands of phase D, requested while the products above run
+    bf16x8 KTf[DTH][2][NTI];
+#pragma unroll
+    for (int j = 0; j < DTH; ++j)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < NTI; ++i) KTf[j][s][i] = frag(Bc, Cfg::KT_OFF, ((jt0 + j) * 2 + s) * NTI + i);
+    const float egn = lds_load<float>(Bc + Cfg::EGN_OFF);
+    issue_point();
 
     // ---- D: S^T <- exp(g_n) S^T + K^T Dt for this wave's tiles
     {
@@ -1165,10 +1171,10 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   const int sg = (blk >> 3) % NG;
   if (u >= p.n_seqs * p.Hv) return;
   switch (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))) {
-    case 0: scan_staged_wave<IO, D, 0>(p, u, sg, stage0, stage1, kqs, xch); break;
-    case 1: scan_staged_wave<IO, D, 1>(p, u, sg, stage0, stage1, kqs, xch); break;
-    case 2: scan_staged_wave<IO, D, 2>(p, u, sg, stage0, stage1, kqs, xch); break;
-    default: scan_staged_wave<IO, D, 3>(p, u, sg, stage0, stage1, kqs, xch); break;
+    case 0: scan_staged_wave<IO, D, 0>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
+    case 1: scan_staged_wave<IO, D, 1>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
+    case 2: scan_staged_wave<IO, D, 2>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
+    default: scan_staged_wave<IO, D, 3>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
   }
 }
 
