@@ -844,19 +844,20 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   constexpr int KSH = KSD / NSP, DTH = DT / NSP, MR = 4 / NSP;
   constexpr int ESZ = sizeof(IO);
   // staged chunk: the factor record (its last 1 KiB granule partial), then 64 value
-  // rows of the pair's 32 columns; 16-byte pieces of a value row are permuted by an
-  // XOR with (row / 4) % 4, so that the four row groups of one read hit distinct banks
+  // rows of the workgroup's 16 SP columns; 16-byte pieces of a value row are permuted by
+  // an XOR with (row / 4) % VNP, so that the four row groups of one read hit distinct
+  // banks
   constexpr int RG = (Cfg::REC_BYTES + 1023) / 1024;
   constexpr int VRB = SP * 16 * ESZ, VNP = VRB / 16, VG = 64 * VRB / 1024;
   constexpr int V_OFF = RG * 1024, G = RG + VG;
   constexpr int GPW = (G + NW - 1) / NW;  // copies per wave; granules past G are padding
   constexpr int BUF = GPW * NW * 1024;
-  constexpr int XCH = SP * NSP * 6 * 64;  // f32x4 exchange slots
+  constexpr int XCH = NSP == 2 ? SP * NSP * 6 * 64 : 1;  // f32x4 exchange slots
   // key and query rows of a chunk (one buffer, refilled once every wave has read
   // them): rows of RB bytes whose 16-byte pieces are permuted by an XOR with the row
   // index, so that the 16 rows of one operand read land in distinct banks
   constexpr int RB = D * ESZ, PPR = RB / 16, RPG = 1024 / RB, KQG = 64 / RPG, KQPW = 2 * KQG / NW;
-  static_assert(KSH * NSP == KSD && DTH * NSP == DT && VNP == 4 && VG * 1024 == 64 * VRB, "shape");
+  static_assert(KSH * NSP == KSD && DTH * NSP == DT && (VNP == 4 || VNP == 8) && VG * 1024 == 64 * VRB, "shape");
   static_assert(RPG * RB == 1024 && KQPW * NW == 2 * KQG, "key/query staging");
   static_assert(2 * BUF + 16 * XCH + 2 * 64 * RB <= 160 * 1024, "LDS budget");
   const int seq = u / p.Hv, h = u - seq * p.Hv;
@@ -900,8 +901,10 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   }
   // this lane's value column in a staged row (row t adds t * VRB); (t / 4) % 4 = grp
   // for every row the lane reads
+  // this lane's value column in a staged row t = 16 mt + 4 grp + r (row t adds t * VRB;
+  // (t / 4) % VNP depends on mt and grp only)
   const int v_byte = (16 * jj + col) * ESZ;
-  const int v_rd = V_OFF + 16 * ((v_byte >> 4) ^ grp) + (v_byte & 15);
+  auto v_rd = [&](int mt) { return V_OFF + 16 * ((v_byte >> 4) ^ ((4 * mt + grp) & (VNP - 1))) + (v_byte & 15); };
 
   // chunk descriptors: one vector load (every lane the same 16 bytes) a chunk ahead;
   // a scalar load would make every wait on LDS reads a wait for all of them
@@ -929,7 +932,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     for (int gi = 0; gi < GPW; ++gi) {
       const int g = q + gi * NW;  // wave-uniform
       const bool is_v = g >= RG && g < G;
-      const uint32_t t = 16u * (uint32_t)(g - RG) + (uint32_t)lane / VNP;
+      const uint32_t t = (64u / VNP) * (uint32_t)(g - RG) + (uint32_t)lane / VNP;
       const uint32_t lp = ((uint32_t)lane % VNP) ^ ((t >> 2) & (VNP - 1));
       const uint32_t voff = g < RG ? 1024u * g + 16u * lane : is_v ? t * vsb + 16u * lp : (uint32_t)Cfg::REC_BYTES;
       dma16(is_v ? rv : rr, B + 1024 * g, voff);
@@ -950,16 +953,14 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   };
   // this wave's A operands of X and Y: row 16 mt + col, key columns 32 (s0 + s) + 8 grp ..
   RowOp<IO> Kop[4][KSH], Qop[4][KSH];
-  auto read_kq = [&]() {
+  auto read_kq = [&](int s) {  // k-step s0 + s
 #pragma unroll
-    for (int s = 0; s < KSH; ++s)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int r = 16 * mt + col;
-        const int off = r * RB + 16 * ((grp + 4 * (s0 + s)) ^ (r % PPR));
-        Kop[mt][s].v = lds_load<bf16x8>(kqs + off);
-        Qop[mt][s].v = lds_load<bf16x8>(kqs + 64 * RB + off);
-      }
+    for (int mt = 0; mt < 4; ++mt) {
+      const int r = 16 * mt + col;
+      const int off = r * RB + 16 * ((grp + 4 * (s0 + s)) ^ (r % PPR));
+      Kop[mt][s].v = lds_load<bf16x8>(kqs + off);
+      Qop[mt][s].v = lds_load<bf16x8>(kqs + 64 * RB + off);
+    }
   };
   auto frag = [&](const lds_u8* B, int off, int f) {
     return lds_load<bf16x8>(B + off + 1024 * f + 16 * lane);
@@ -988,15 +989,18 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     stage_chunk(nxt, more ? c + 1 : c, Bn);
     nxt_raw = chunk_raw(c + 2 < ce ? c + 2 : c + 1 - (more ? 0 : 1));
 
-    read_kq();
+    read_kq(0);
     issue_point();
 
-    // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains
+    // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains;
+    //      each k-step's key and query operands are requested one k-step ahead
     f32x4 X[4], Y[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) X[mt] = Y[mt] = zero4();
 #pragma unroll
     for (int s = 0; s < KSH; ++s) {
+      if (s + 1 < KSH) read_kq(s + 1);
+      issue_point();
       bf16x8 sop[NTF];
       reg_operand<NTF>(S[2 * s], (2 * s + 1 < DTH) ? S[2 * s + 1] : zero4(), sop);
 #pragma unroll
@@ -1009,30 +1013,33 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       }
     }
     issue_point();
-    // add the partner's partial sums: X for all rows, Y for this wave's output rows
+    // with two waves per slab, add the partner's partial sums (X for all rows, Y for
+    // this wave's output rows) through LDS
     f32x4 Ym[MR];
     float Vv[4][4];
     f32x4 veg[4];
     bf16x8 Tf[kFragCombos][NTF];
-    {
-      f32x4* mine = xch + ((jj * NSP + w) * 6) * 64 + lane;
-      const f32x4* other = xch + ((jj * NSP + (w ^ 1)) * 6) * 64 + lane;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) mine[mt * 64] = X[mt];
-#pragma unroll
-      for (int i = 0; i < MR; ++i) mine[(4 + i) * 64] = Y[MR * (w ^ 1) + i];
-      // operands of phase B, requested here: the barrier's wait covers their latency
+    auto read_b = [&]() {  // operands of phase B
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          Vv[mt][r] = bf16_to_f32(lds_load<bf16_bits>(Bc + v_rd + (16 * mt + 4 * grp + r) * VRB));
+          Vv[mt][r] = bf16_to_f32(lds_load<bf16_bits>(Bc + v_rd(mt) + (16 * mt + 4 * grp + r) * VRB));
         veg[mt] = vrow4(Bc, Cfg::V_EG, mt);
       }
 #pragma unroll
       for (int f = 0; f < kFragCombos; ++f)
 #pragma unroll
         for (int i = 0; i < NTF; ++i) Tf[f][i] = frag(Bc, Cfg::T_OFF, f * NTF + i);
+    };
+    if constexpr (NSP == 2) {
+      f32x4* mine = xch + ((jj * NSP + w) * 6) * 64 + lane;
+      const f32x4* other = xch + ((jj * NSP + (w ^ 1)) * 6) * 64 + lane;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) mine[mt * 64] = X[mt];
+#pragma unroll
+      for (int i = 0; i < MR; ++i) mine[(4 + i) * 64] = Y[MR * (w ^ 1) + i];
+      read_b();  // requested here: the barrier's wait covers their latency
       lds_barrier();
       // every wave has read this chunk's key and query rows: copy the next chunk's
       // (the last chunk copies its own again, so that every path issues the same copies)
@@ -1049,6 +1056,14 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ym[i][r] = Y[mt0 + i][r] + yo[r];
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MR; ++i) Ym[i] = Y[mt0 + i];
+      read_b();
+      lds_barrier();
+      // every wave has read this chunk's key and query rows: copy the next chunk's (the
+      // last chunk copies its own again, so that every path issues the same copies)
+      stage_kq(more ? nxt : cur);
     }
 
     // ---- B: R' = V - exp(g) X, Dt = T'' R' over the nonzero k-steps
@@ -1150,7 +1165,7 @@ struct StagedLds {
   static constexpr int RG = (Cfg::REC_BYTES + 1023) / 1024;
   static constexpr int G = RG + 64 * Shp::SP * 16 * (int)sizeof(IO) / 1024;
   static constexpr int BUF = (G + Shp::NW - 1) / Shp::NW * Shp::NW * 1024;
-  static constexpr int XCH = Shp::SP * Shp::NSP * 6 * 64;
+  static constexpr int XCH = Shp::NSP == 2 ? Shp::SP * Shp::NSP * 6 * 64 : 1;
   static constexpr int KQ = 2 * 64 * D * (int)sizeof(IO);
 };
 
