@@ -36,7 +36,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
   __shared__ __attribute__((aligned(16))) float vec[4 * CT];
   __shared__ float vec_tmp[2 * CT];
 
-  const int r_ = blockIdx.x, h = blockIdx.y;
+  // head-major grid: consecutive workgroups take consecutive heads of one request, so
+  // they sweep that request's contiguous state block in address order
+  const int h = blockIdx.x, r_ = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int slot = p.slot_ids[r_];
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
 template <typename IO, int D>
 static hipError_t launch_flush_t(const FlushArgs<IO>& a, int n_req, int ct, hipStream_t st) {
   if (n_req == 0) return hipSuccess;
-  dim3 grid(n_req, a.Hv);
+  dim3 grid(a.Hv, n_req);
   if (ct <= 32)
     hipLaunchKernelGGL((flush_kernel<IO, D, 32>), grid, dim3(64 * (D / 16)), 0, st, a);
   else

@@ -91,7 +91,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
   constexpr int RPP = NTH / LPR;
   constexpr int NP = D / RPP;
   constexpr int HALF = D / 2;
-  const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  // head-major grid: consecutive workgroups take consecutive heads of one request, so
+  // they sweep that request's contiguous state block in address order
+  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int slot = p.slot_ids[r];
   if (slot < -1 || slot >= p.n_slots) {
     if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
@@ -305,7 +307,7 @@ static hipError_t launch_decode_t(const DecodeArgs<IO>& a, int n_req, hipStream_
   if (n_req == 0) return hipSuccess;
   constexpr int LPR = D / 8;
   constexpr int NTH = (D * LPR < 256) ? D * LPR : 256;
-  hipLaunchKernelGGL((decode_kernel<IO, D>), dim3(n_req, a.Hv), dim3(NTH), 0, st, a);
+  hipLaunchKernelGGL((decode_kernel<IO, D>), dim3(a.Hv, n_req), dim3(NTH), 0, st, a);
   return hipGetLastError();
 }
 
