@@ -193,9 +193,13 @@ template <typename IO, bool SILU>
 __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int TR = kConvTile;
-  const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * VEC;
+  // channel group fastest: consecutive workgroups cover one tile's rows across all
+  // channels, sweeping whole rows in address order
+  const int ng = (int)((p.channels / VEC + 255) / 256);
+  const int tix = (int)(blockIdx.x / ng), cg = (int)(blockIdx.x % ng);
+  const int64_t c0 = ((int64_t)cg * 256 + threadIdx.x) * VEC;
   if (c0 >= p.channels) return;
-  const ConvTile tile = p.tiles[blockIdx.x];
+  const ConvTile tile = p.tiles[tix];
   const ConvSeq sq = p.seqs[tile.seq];
   const int64_t C = p.channels;
   const int64_t rel0 = tile.row - sq.row0;
@@ -335,7 +339,9 @@ static hipError_t launch_conv_t(const ConvArgs<IO>& a, int n_tiles, hipStream_t 
   if (n_tiles == 0) return hipSuccess;
   constexpr int VEC = 16 / sizeof(IO);
   const int64_t groups = a.channels / VEC;
-  dim3 grid((unsigned)n_tiles, (unsigned)((groups + 255) / 256));
+  const int64_t blocks = (int64_t)n_tiles * ((groups + 255) / 256);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks);
   if (a.act == GDN_ACT_SILU)
     hipLaunchKernelGGL((conv_kernel<IO, true>), grid, dim3(256), 0, st, a);
   else
