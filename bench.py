@@ -2,9 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 
-Step = one pass of the prefill hot path over one 27B-shaped layer: the causal conv
-update over the packed q|k|v channels (18,432 bf16 channels, 8,192 tokens) and the
-chunked prefill of the gated delta rule (48 heads, 128 x 128 fp32 state per head,
+Step = one pass of the prefill hot path over one 27B-shaped layer, as two library
+calls: the causal conv update over the packed q|k|v channels (18,432 bf16 channels,
+8,192 tokens) and the chunked prefill (pre-pass and scan in one call) of the gated delta rule (48 heads, 128 x 128 fp32 state per head,
 bf16 q/k/v, fp32 o, 64-token chunks) writing a checkpoint page at each of the nine
 896-token block boundaries.  `value` is prefill tokens per second per layer over the
 K timed steps (inputs resident in HBM, synthetic, seeded).
@@ -146,8 +146,8 @@ def main():
 
     def step():
         g.conv_update(layer, x, w, [("zero", None, tail)], cu, sp, y, ckpt=pool, page_ids=page_ids, workspace=cws)
-        g.prefill_factorize(layer, q, k, a, b, cu, sp, BLOCK, ws)
-        g.prefill_scan(layer, q, k, v, cu, sp, [("zero", None, S)], o, ws, ckpt=pool, page_ids=page_ids)
+        g.chunk_prefill(layer, q, k, v, a, b, cu, sp, [("zero", None, S)], o, ckpt=pool, page_ids=page_ids,
+                        workspace=ws)
 
     for _ in range(args.warmup):
         step()

@@ -8,7 +8,10 @@
 // first use and kept): a table is copied into the ring and an asynchronous copy is
 // enqueued on the caller's stream, followed by an event; a ring region is reused only
 // after the event that last covered it has completed.  This keeps every call
-// asynchronous with respect to the host.
+// asynchronous with respect to the host.  The events skip the system-scope fence: they
+// only tell the host that a copy has finished reading the ring, and the fence's cache
+// writeback and invalidation would delay the kernel that follows and start it with cold
+// caches.  Completed events are kept and reused.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -35,6 +38,7 @@ struct StagingRing {
     hipEvent_t ev;
   };
   std::deque<Seg> live;
+  std::vector<hipEvent_t> spare;
 };
 StagingRing g_ring;
 
@@ -65,18 +69,23 @@ hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) 
       ++it;
       continue;
     }
-    hipEventDestroy(it->ev);
+    g_ring.spare.push_back(it->ev);
     it = g_ring.live.erase(it);
   }
   std::memcpy(g_ring.base + off, src, bytes);
   hipError_t e = hipMemcpyAsync(dst, g_ring.base + off, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return e;
   hipEvent_t ev;
-  e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-  if (e != hipSuccess) return e;
+  if (!g_ring.spare.empty()) {
+    ev = g_ring.spare.back();
+    g_ring.spare.pop_back();
+  } else {
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
+    if (e != hipSuccess) return e;
+  }
   e = hipEventRecord(ev, stream);
   if (e != hipSuccess) {
-    hipEventDestroy(ev);
+    g_ring.spare.push_back(ev);
     return e;
   }
   g_ring.live.push_back({off, bytes, ev});
