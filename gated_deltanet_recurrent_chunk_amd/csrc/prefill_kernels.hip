@@ -181,8 +181,24 @@ struct FactorLds {
   static constexpr int KP = row_stride(D), TP = row_stride(CT);
   static constexpr int KS = Cfg::NTI * CT * KP;  // bf16 elements of the key (or query) planes
   static constexpr int TT = Cfg::NTF * CT * TP;  // bf16 elements of T^T (or T'') planes
-  static constexpr int QT = KS > TT ? KS : TT;   // query planes, later T''
+  static constexpr int QT = KS > TT ? KS : TT;   // query planes, later T''; key planes, later T^T
+  // The T_ii planes (NTF terms x 16 bf16 per row of a diagonal block) fit in the
+  // diagonal 16 x 16 fp32 blocks of A for NTF <= 2; A is not read there once they exist.
+  static constexpr bool TD_IN_A = Cfg::NTF <= 2;
 };
+
+// Row vectors of the chunk (k = 0: g, 1: exp(g), 2: b, 3: exp(g_n - g)) live in the four
+// padding columns of A's rows: element t of vector k is A[t][CT + k].
+__device__ __forceinline__ float& rowvec(float (*As)[CT + 4], int k, int t) { return As[t][CT + k]; }
+
+// Row r of the T_ii plane for term q of diagonal block bi (16 bf16).
+template <bool IN_A>
+__device__ __forceinline__ bf16_bits* td_row(float (*As)[CT + 4], float (*Ub)[24], int q, int bi, int r) {
+  if constexpr (IN_A)
+    return reinterpret_cast<bf16_bits*>(&As[16 * bi + r][16 * bi + 8 * q]);
+  else
+    return reinterpret_cast<bf16_bits*>(&Ub[0][0]) + ((q * 4 + bi) * 16 + r) * 16;
+}
 
 // The ten lower 16 x 16 tiles of A, dealt 4, 3, 2, 1 to waves 0..3 (P's tiles of row
 // tile ut = W are 1, 2, 3, 4: five tiles per wave).
@@ -192,17 +208,18 @@ __host__ __device__ constexpr int a_tiles_begin(int w) { return w == 0 ? 0 : w =
 
 template <typename IO, int D, int W>
 __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const int n, uint8_t* rec,
-                                               bf16_bits* Ks, bf16_bits* QT, float (*As)[CT + 4], bf16_bits* Tt,
-                                               float (*Ub)[24], const float* vec, const int p2_wave) {
+                                               bf16_bits* Ks, bf16_bits* QT, float (*As)[CT + 4], float (*Ub)[24],
+                                               const int p2_wave) {
   using Cfg = PrefillCfg<IO, D>;
   using L = FactorLds<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
   constexpr int KP = L::KP, TP = L::TP;
   constexpr int KSD = (D + 31) / 32, DT = D / 16;
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  constexpr bool TDA = L::TD_IN_A;
   const bf16_bits* Qs = QT;
-  bf16_bits* Tl = QT;                                 // T'' planes, once P1 has read the query rows
-  bf16_bits* Td = reinterpret_cast<bf16_bits*>(Ub);  // T_ii planes
+  bf16_bits* Tl = QT;  // T'' planes, once P1 has read the query rows
+  bf16_bits* Tt = Ks;  // T^T planes, once P1 has read the key rows
 
   // ---------------------------------------------------------------- P1
   // A tiles: acc = K_mt K_nt^T; element (t, s) with t = 16 mt + 4 grp + r, s = 16 nt + col
@@ -218,13 +235,13 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       mma_terms<NTI, NTI, ORD>(acc, a, b);
     }
     const int sc = 16 * nt + col;
-    const float gs = vec[sc];
+    const float gs = rowvec(As, 0, sc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * mt + 4 * grp + r;
       // computed for every element (pinned, so the LDS reads are not moved into a
       // branch per element) and kept or dropped by the select
-      float dec = __expf(vec[t] - gs), bt = vec[2 * CT + t];
+      float dec = __expf(rowvec(As, 0, t) - gs), bt = rowvec(As, 2, t);
       asm volatile("" : "+v"(dec), "+v"(bt));
       As[t][sc] = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
     }
@@ -252,14 +269,14 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       }
     }
     const int t = 16 * W + col;
-    const float gt = vec[t];
+    const float gt = rowvec(As, 0, t);
     bf16_bits tt[8][NTF];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sp = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
       const float dot = e < 4 ? acc0[e] : acc1[e - 4];
       // the exponent g_t - g_s is <= 0 on the causal side kept by the select
-      float dec = __expf(gt - vec[sp]);
+      float dec = __expf(gt - rowvec(As, 0, sp));
       asm volatile("" : "+v"(dec));
       const float val = (sp <= t && t < n && (e < 4 || two)) ? p.scale * dec * dot : 0.f;
       split_terms<NTF>(val, tt[e]);
@@ -322,7 +339,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       bf16_bits tt[NTF];
       split_terms<NTF>(X[r], tt);
 #pragma unroll
-      for (int q = 0; q < NTF; ++q) Td[((q * 4 + bi) * 16 + r) * 16 + c] = tt[q];
+      for (int q = 0; q < NTF; ++q) td_row<TDA>(As, Ub, q, bi, r)[c] = tt[q];
     }
   }
   __syncthreads();  // T_ii complete
@@ -355,7 +372,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
 #pragma unroll
       for (int q = 0; q < NTF; ++q) {
         // A operand of T_ii: row col, columns 4 grp .. + 3 (contraction past 16 is zero)
-        const uint2 w = *reinterpret_cast<const uint2*>(&Td[((q * 4 + i) * 16 + col) * 16 + 4 * grp]);
+        const uint2 w = *reinterpret_cast<const uint2*>(td_row<TDA>(As, Ub, q, i, col) + 4 * grp);
         tii[q] = __builtin_bit_cast(bf16x8, u32x4{w.x, w.y, 0u, 0u});
       }
       reg_operand<NTF>(em, zero4(), e_op);
@@ -364,7 +381,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       // row 16 W + col of T^T (columns 16 i + 4 grp .. + 3, contiguous in the swizzled
       // order), and T''[t][j] = exp(g_n - g_t) T[t][j] b_j into the T'' planes
       bf16_bits tt[4][NTF];
-      const float bj = vec[2 * CT + 16 * W + col];
+      const float bj = rowvec(As, 2, 16 * W + col);
       const int pc = swz(16 * W + col);
 #pragma unroll
       for (int r = 0; r < 4; ++r) split_terms<NTF>(Tb[i][r], tt[r]);
@@ -376,7 +393,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * i + 4 * grp + r;
         bf16_bits t2[NTF];
-        split_terms<NTF>((Tb[i][r] * vec[3 * CT + t]) * bj, t2);
+        split_terms<NTF>((Tb[i][r] * rowvec(As, 3, t)) * bj, t2);
 #pragma unroll
         for (int q = 0; q < NTF; ++q) Tl[q * CT * TP + t * TP + pc] = t2[q];
       }
@@ -416,7 +433,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
     bf16_bits tt[8][NTF];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float bj = vec[2 * CT + 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3)];
+      const float bj = rowvec(As, 2, 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3));
       split_terms<NTF>(acc[e >> 2][e & 3] * bj, tt[e]);
     }
 #pragma unroll
@@ -438,12 +455,12 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int PER_ROW = D / VEC;
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + 255) / 256;
-  __shared__ __attribute__((aligned(16))) bf16_bits Ks[L::KS];
+  // 54,272 bytes at d = 128 with bf16 inputs: three workgroups per CU
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[L::QT];  // key rows, later T^T
   __shared__ __attribute__((aligned(16))) bf16_bits QT[L::QT];  // query rows, later T''
+  // A; its diagonal blocks later hold the T_ii planes, its padding columns the row vectors
   __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
-  __shared__ __attribute__((aligned(16))) bf16_bits Tt[L::TT];
-  __shared__ __attribute__((aligned(16))) float Ub[CT][24];  // T_ii planes (bf16 terms)
-  __shared__ __attribute__((aligned(16))) float vec[4 * CT];  // g, exp(g), b, exp(g_n - g)
+  __shared__ __attribute__((aligned(16))) float Ub[L::TD_IN_A ? 1 : CT][24];  // T_ii planes otherwise
 
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -497,10 +514,10 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
     const float g = wave_inclusive_scan(la);        // rows past n keep g_{n-1}
     const float gn = __shfl(g, n - 1, 64);
     const float eg = __expf(g);
-    vec[lane] = g;
-    vec[CT + lane] = eg;
-    vec[2 * CT + lane] = bb;
-    vec[3 * CT + lane] = lane < n ? __expf(gn - g) : 0.f;
+    rowvec(As, 0, lane) = g;
+    rowvec(As, 1, lane) = eg;
+    rowvec(As, 2, lane) = bb;
+    rowvec(As, 3, lane) = lane < n ? __expf(gn - g) : 0.f;
     float* vo = reinterpret_cast<float*>(rec + Cfg::VEC_OFF);
     vo[Cfg::V_EG * CT + lane] = eg;
     vo[Cfg::V_EGS * CT + lane] = p.scale * eg;
@@ -510,10 +527,10 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
 
   const int p2_wave = (blockIdx.x + blockIdx.y) & 3;
   switch (wave) {
-    case 0: factorize_wave<IO, D, 0>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
-    case 1: factorize_wave<IO, D, 1>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
-    case 2: factorize_wave<IO, D, 2>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
-    default: factorize_wave<IO, D, 3>(p, n, rec, Ks, QT, As, Tt, Ub, vec, p2_wave); break;
+    case 0: factorize_wave<IO, D, 0>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
+    case 1: factorize_wave<IO, D, 1>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
+    case 2: factorize_wave<IO, D, 2>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
+    default: factorize_wave<IO, D, 3>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
   }
 }
 
