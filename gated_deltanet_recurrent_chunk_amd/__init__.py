@@ -88,12 +88,14 @@ _decl("gdn_prefill_scan", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i
                                  _P(_Ckpt), _vp, _vp, _sz])
 _decl("gdn_decode_step", _i32, [_P(_Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp])
 _decl("gdn_replay_flush", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp])
+_decl("gdn_replay_forward", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                   _i32, _vp, _vp])
 
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_state_bytes", "gdn_conv_tail_bytes",
             "gdn_checkpoint_bytes", "gdn_conv_channels", "gdn_cached_prefix_tokens", "gdn_floor_chunk",
             "gdn_count_boundaries", "gdn_block_size_for_state", "gdn_prefill_workspace_bytes",
             "gdn_conv_workspace_bytes", "gdn_conv_update", "gdn_chunk_prefill", "gdn_prefill_factorize",
-            "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush")
+            "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush", "gdn_replay_forward")
 
 
 class GdnError(RuntimeError):
@@ -409,6 +411,37 @@ def replay_flush(layer: Layer, state_pool, slot_ids, buf_k, buf_v, buf_a, buf_b,
                                int(state_pool.shape[0]), _ptr(slot_ids), _ptr(buf_k), _ptr(buf_v), _ptr(buf_a),
                                _ptr(buf_b), int(buf_k.shape[1]), _ptr(n_accepted), _ptr(status))
     _check(st, "gdn_replay_flush")
+
+
+def replay_forward(layer: Layer, state_pool, slot_ids, buf_k, buf_v, buf_a, buf_b, n_logged, n_new, q_new, o,
+                   status=None, stream=None):
+    """ReplaySSM verification outputs (gdn_replay_forward): o[r, i] = scale * S q_new[r, i]
+    after log rows 0 .. n_logged[r] + i of request r's slot, from the slot's state, for
+    i < n_new[r].  Neither the state nor the log is written.  buf_*: [n_slots, buf_rows,
+    heads, ...]; q_new: [n_req, max_new, n_qk_heads, d]; o: [n_req, max_new, n_v_heads, d]
+    fp32."""
+    n_req = int(slot_ids.numel())
+    D, Hv, Hqk = layer.head_dim, layer.n_v_heads, layer.n_qk_heads
+    n_slots = int(state_pool.shape[0])
+    _need(slot_ids.dtype == torch.int32 and n_logged.dtype == torch.int32 and n_new.dtype == torch.int32,
+          "int32 slot_ids / n_logged / n_new")
+    _need(n_logged.numel() >= n_req and n_new.numel() >= n_req, "n_logged / n_new too short")
+    _need(state_pool.dtype == torch.float32 and state_pool.is_contiguous()
+          and tuple(state_pool.shape[1:]) == (Hv, D, D), "state_pool must be fp32 [slots, Hv, d, d]")
+    rows = int(buf_k.shape[1])
+    _rows_ok(buf_k, n_slots * rows, Hqk * D, layer.io_dtype, "buf_k")
+    _rows_ok(buf_v, n_slots * rows, Hv * D, layer.io_dtype, "buf_v")
+    _rows_ok(buf_a, n_slots * rows, Hv, torch.float32, "buf_a")
+    _rows_ok(buf_b, n_slots * rows, Hv, torch.float32, "buf_b")
+    max_new = int(q_new.shape[1]) if q_new.dim() >= 2 else 0
+    _need(q_new.shape[0] >= n_req, "q_new: one row block per request")
+    _rows_ok(q_new, q_new.shape[0] * max_new, Hqk * D, layer.io_dtype, "q_new")
+    _need(tuple(o.shape[:2]) == (q_new.shape[0], max_new), "o: [n_req, max_new, n_v_heads, d]")
+    _rows_ok(o, o.shape[0] * max_new, Hv * D, torch.float32, "o")
+    st = _lib.gdn_replay_forward(ctypes.byref(layer.c()), _stream(stream), n_req, _ptr(state_pool), n_slots,
+                                 _ptr(slot_ids), _ptr(buf_k), _ptr(buf_v), _ptr(buf_a), _ptr(buf_b), rows,
+                                 _ptr(n_logged), _ptr(n_new), _ptr(q_new), max_new, _ptr(o), _ptr(status))
+    _check(st, "gdn_replay_forward")
 
 
 def lib_handle():

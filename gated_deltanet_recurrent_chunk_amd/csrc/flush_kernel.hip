@@ -1,8 +1,11 @@
-// flush_kernel.hip -- the replay flush ("Caching less to serve more requests", section
-// "What we changed"): each request keeps one state plus a log of its per-token inputs
-// since it; the flush folds the first n accepted rows of the log into the state as one
-// block of the chunked gated delta rule (chunk_common.h), one launch for all requests.
-// The state is read once and written once; logged rows at or past n are never read.
+// flush_kernel.hip -- the ReplaySSM kernels ("Caching less to serve more requests",
+// section "What we changed"): each request keeps one state plus a log of its per-token
+// inputs since it.
+//   flush:   folds the first n accepted rows of the log into the state as one block of
+//            the chunked gated delta rule (chunk_common.h), one launch for all requests.
+//            The state is read once and written once; rows at or past n are never read.
+//   replay:  the outputs of new rows appended behind the logged ones, computed from the
+//            state and the log as one block of the same rule; nothing is written back.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.h"
@@ -147,6 +150,221 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
       mma_terms<NTI, NTF, ORD>(acc, a, Dtop[s]);
     }
     *reinterpret_cast<f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp) = acc;
+  }
+}
+
+// ==================================================================================
+// Replay outputs: one workgroup per (request, value head), one wave per 16-row slab of
+// the state.  With L = m + n rows (m logged, n new), S_0 the slot's state, g the running
+// log-decay and T = (I + A)^-1 from the rows' keys and gates (wave 0), the block form of
+// the rule gives
+//   Delta = T diag(b) (V - diag(e^g) K S_0^T)            (the rows' corrected updates)
+//   O     = scale (diag(e^g) Q S_0^T + P Delta),  P[t][s] = e^(g_t - g_s) q_t.k_s, s <= t
+// whose row t is scale * S_t q_t, the output after row t.  Rows t < m carry no query:
+// their outputs are zero and not stored.
+template <typename IO, int D, int CT>
+__global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p) {
+  constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
+  constexpr int NW = D / 16, NTH = 64 * NW;
+  constexpr int KP = row_stride(D), TP = row_stride(CT), VP = D + 4;
+  constexpr int DT = D / 16, KSD = (D + 31) / 32;
+  constexpr int MT = CT / 16, KST = (MT + 1) / 2;
+  constexpr int VEC = 16 / sizeof(IO);
+  constexpr int PER_ROW = D / VEC;
+  // P tiles formed: (mt, nt) with nt <= mt | 1, which covers every tile the output
+  // products read (tiles above the diagonal come out zero)
+  constexpr int NPT = MT == 4 ? 12 : MT == 2 ? 4 : 1;
+
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
+  __shared__ __attribute__((aligned(16))) bf16_bits Qs[NTI * CT * KP];
+  __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
+  __shared__ float As[CT][CT + 4];
+  __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
+  __shared__ __attribute__((aligned(16))) bf16_bits Ps[NTF * CT * TP];
+  __shared__ __attribute__((aligned(16))) float vec[4 * CT];
+  __shared__ float vec_tmp[2 * CT];
+
+  // head-major grid, as for the flush
+  const int h = blockIdx.x, r_ = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int slot = p.slot_ids[r_];
+  const int m = p.n_logged[r_], n = p.n_new[r_];
+  if (slot < -1 || slot >= p.n_slots || m < 0 || n < 0 || m + n > p.buf_rows || n > p.max_new) {
+    if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
+    return;
+  }
+  if (slot < 0 || n == 0) return;  // padding or no new rows: nothing written
+  const int L = m + n;
+
+  const int hk = h / p.group;
+  const int my_row = wave * 16 + col;
+  const float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
+  f32x4 S[DT];
+#pragma unroll
+  for (int jt = 0; jt < DT; ++jt)
+    S[jt] = *reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp);
+
+  if constexpr (D < 32) {
+    zero_lds(Ks, sizeof(Ks), tid, NTH);
+    zero_lds(Qs, sizeof(Qs), tid, NTH);
+  }
+  __syncthreads();
+  // log rows 0 .. L-1 of this slot (keys, values), and the queries of the new rows
+  const size_t row0 = (size_t)slot * p.buf_rows;
+  const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
+  const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
+  const IO* qb = p.q_new + (size_t)r_ * p.max_new * p.Hqk * D + (size_t)hk * D;
+  for (int idx = tid; idx < CT * PER_ROW; idx += NTH) {
+    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    uint4 kv = load16(kb + (size_t)t * p.Hqk * D + j0, t < L);
+    store_row_terms<IO, NTI>(kv, Ks, CT * KP, KP, t, j0);
+    uint4 qv = load16(qb + (size_t)(t >= m ? t - m : 0) * p.Hqk * D + j0, t >= m && t < L);
+    store_row_terms<IO, NTI>(qv, Qs, CT * KP, KP, t, j0);
+    uint4 vv = load16(vb + (size_t)t * p.Hv * D + j0, t < L);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv, e);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float la = 0.f, bb = 0.f;
+    if (lane < L) {
+      const size_t ai = (row0 + lane) * p.Hv + h;
+      la = __logf(p.buf_a[ai]);
+      bb = p.buf_b[ai];
+    }
+    const float g = wave_inclusive_scan(la);
+    factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
+  } else {
+    // match the barriers inside factorize_chunk
+    __syncthreads();
+    __syncthreads();
+  }
+  __syncthreads();
+
+  // P tiles, dealt round robin to the waves, as NTF bf16 term planes (row t, column s)
+  for (int ti = wave; ti < NPT; ti += NW) {
+    const int mt = MT == 4 ? (ti < 2 ? 0 : ti < 4 ? 1 : ti < 8 ? 2 : 3) : MT == 2 ? ti >> 1 : 0;
+    const int nt = MT == 4 ? (ti < 4 ? ti & 1 : (ti - 4) & 3) : MT == 2 ? ti & 1 : 0;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      bf16x8 a[NTI], b[NTI];
+      op_terms<NTI>(Qs, CT * KP, KP, 16 * mt + col, s, grp, a);
+      op_terms<NTI>(Ks, CT * KP, KP, 16 * nt + col, s, grp, b);
+      mma_terms<NTI, NTI, ORD>(acc, a, b);
+    }
+    const int sc = 16 * nt + col;
+    const float gs = vec[sc];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * mt + 4 * grp + r;
+      // the exponent g_t - g_s is <= 0 on the causal side kept by the select
+      float dec = __expf(vec[t] - gs);
+      asm volatile("" : "+v"(dec));
+      const float val = (sc <= t && t < L) ? dec * acc[r] : 0.f;
+      bf16_bits tt[NTF];
+      split_terms<NTF>(val, tt);
+#pragma unroll
+      for (int q = 0; q < NTF; ++q) Ps[q * CT * TP + t * TP + swz(sc)] = tt[q];
+    }
+  }
+  __syncthreads();
+
+  // X = K S_0^T and Y = Q S_0^T for this wave's slab
+  bf16x8 Sop[KSD][NTF];
+#pragma unroll
+  for (int s = 0; s < KSD; ++s) reg_operand<NTF>(S[2 * s], (2 * s + 1 < DT) ? S[2 * s + 1] : zero4(), Sop[s]);
+  f32x4 R[2 * KST], Y[2 * KST];
+#pragma unroll
+  for (int mt = 0; mt < 2 * KST; ++mt) {
+    R[mt] = zero4();
+    Y[mt] = zero4();
+    if (mt >= MT) continue;
+    f32x4 acc = zero4(), accy = zero4();
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      bf16x8 a[NTI], aq[NTI];
+      op_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
+      op_terms<NTI>(Qs, CT * KP, KP, 16 * mt + col, s, grp, aq);
+      mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
+      mma_terms<NTI, NTF, ORD>(accy, aq, Sop[s]);
+    }
+    Y[mt] = accy;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * mt + 4 * grp + r;
+      float val = 0.f;
+      if (t < L) val = vec[2 * CT + t] * (Vs[t * VP + my_row] - vec[CT + t] * acc[r]);
+      R[mt][r] = val;
+    }
+  }
+  // Delta = T R
+  bf16x8 Rop[KST][NTF];
+#pragma unroll
+  for (int s = 0; s < KST; ++s) reg_operand<NTF>(R[2 * s], R[2 * s + 1], Rop[s]);
+  f32x4 Dl[2 * KST];
+#pragma unroll
+  for (int mt = 0; mt < 2 * KST; ++mt) {
+    Dl[mt] = zero4();
+    if (mt >= MT) continue;
+#pragma unroll
+    for (int s = 0; s <= (mt >> 1); ++s) {
+      bf16x8 a[NTF];
+      op_terms<NTF>(Ts, CT * TP, TP, 16 * mt + col, s, grp, a);
+      mma_terms<NTF, NTF, ORD>(Dl[mt], a, Rop[s]);
+    }
+  }
+  // O = scale (e^g Y + P Delta); rows m .. L-1 stored
+  bf16x8 Dop[KST][NTF];
+#pragma unroll
+  for (int s = 0; s < KST; ++s) reg_operand<NTF>(Dl[2 * s], Dl[2 * s + 1], Dop[s]);
+  float* ob = p.o + (size_t)r_ * p.max_new * p.Hv * D + (size_t)h * D + my_row;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    f32x4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = vec[CT + 16 * mt + 4 * grp + r] * Y[mt][r];
+#pragma unroll
+    for (int s = 0; s <= (mt >> 1); ++s) {
+      bf16x8 a[NTF];
+      op_terms<NTF>(Ps, CT * TP, TP, 16 * mt + col, s, grp, a);
+      mma_terms<NTF, NTF, ORD>(acc, a, Dop[s]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * mt + 4 * grp + r;
+      if (t >= m && t < L) ob[(size_t)(t - m) * p.Hv * D] = p.scale * acc[r];
+    }
+  }
+}
+
+template <typename IO, int D>
+static hipError_t launch_replay_t(const ReplayArgs<IO>& a, int n_req, int ct, hipStream_t st) {
+  if (n_req == 0) return hipSuccess;
+  dim3 grid(a.Hv, n_req);
+  if (ct <= 32)
+    hipLaunchKernelGGL((replay_kernel<IO, D, 32>), grid, dim3(64 * (D / 16)), 0, st, a);
+  else
+    hipLaunchKernelGGL((replay_kernel<IO, D, 64>), grid, dim3(64 * (D / 16)), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_replay(const ReplayArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_replay_t<bf16_bits, 16>(a, n_req, ct, st);
+    case 32: return launch_replay_t<bf16_bits, 32>(a, n_req, ct, st);
+    case 64: return launch_replay_t<bf16_bits, 64>(a, n_req, ct, st);
+    case 128: return launch_replay_t<bf16_bits, 128>(a, n_req, ct, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+hipError_t launch_replay(const ReplayArgs<float>& a, int D, int n_req, int ct, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_replay_t<float, 16>(a, n_req, ct, st);
+    case 32: return launch_replay_t<float, 32>(a, n_req, ct, st);
+    case 64: return launch_replay_t<float, 64>(a, n_req, ct, st);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -497,4 +497,52 @@ gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t 
   return hip_status(launch_flush(fa, L.D, n_req, ct, stream));
 }
 
+gdn_status gdn_replay_forward(const gdn_layer* layer, hipStream_t stream, int32_t n_req, const float* state_pool,
+                              int64_t n_slots, const int32_t* slot_ids, const void* buf_k, const void* buf_v,
+                              const float* buf_a, const float* buf_b, int32_t buf_rows, const int32_t* n_logged,
+                              const int32_t* n_new, const void* q_new, int32_t max_new, float* o, int32_t* status) {
+  LayerInfo L;
+  gdn_status s = check_layer(layer, &L);
+  if (s != GDN_OK) return s;
+  if (n_req < 0 || n_slots < 0 || max_new < 0) return GDN_ERR_BAD_SHAPE;
+  if (buf_rows < 1 || buf_rows > kMaxBufRows) return GDN_ERR_CAPACITY;
+  if (L.io == GDN_F32 && L.D > 64) return GDN_ERR_BAD_SHAPE;
+  if (n_req == 0 || max_new == 0) return GDN_OK;
+  if (!state_pool || !slot_ids || !buf_k || !buf_v || !buf_a || !buf_b || !n_logged || !n_new || !q_new || !o)
+    return GDN_ERR_NULL_ARG;
+  if (!aligned(state_pool, 16) || !aligned(buf_k, 16) || !aligned(buf_v, 16) || !aligned(q_new, 16))
+    return GDN_ERR_BAD_SHAPE;
+  if (n_req > 65535) return GDN_ERR_CAPACITY;
+  const int ct = buf_rows <= 32 ? 32 : 64;
+  auto fill = [&](auto& ra, auto tag) {
+    using IO = decltype(tag);
+    ra.state_pool = state_pool;
+    ra.slot_ids = slot_ids;
+    ra.n_logged = n_logged;
+    ra.n_new = n_new;
+    ra.buf_k = static_cast<const IO*>(buf_k);
+    ra.buf_v = static_cast<const IO*>(buf_v);
+    ra.buf_a = buf_a;
+    ra.buf_b = buf_b;
+    ra.q_new = static_cast<const IO*>(q_new);
+    ra.o = o;
+    ra.status = status;
+    ra.n_slots = n_slots;
+    ra.buf_rows = buf_rows;
+    ra.max_new = max_new;
+    ra.Hqk = L.Hqk;
+    ra.Hv = L.Hv;
+    ra.group = L.Hv / L.Hqk;
+    ra.scale = L.scale;
+  };
+  if (L.io == GDN_BF16) {
+    ReplayArgs<bf16_bits> ra;
+    fill(ra, bf16_bits{});
+    return hip_status(launch_replay(ra, L.D, n_req, ct, stream));
+  }
+  ReplayArgs<float> ra;
+  fill(ra, float{});
+  return hip_status(launch_replay(ra, L.D, n_req, ct, stream));
+}
+
 }  // extern "C"

@@ -64,6 +64,28 @@ struct FlushArgs {
 };
 
 template <typename IO>
+struct ReplayArgs {
+  const float* state_pool;
+  const int32_t* slot_ids;
+  const int32_t* n_logged;
+  const int32_t* n_new;
+  const IO* buf_k;
+  const IO* buf_v;
+  const float* buf_a;
+  const float* buf_b;
+  const IO* q_new;
+  float* o;
+  int32_t* status;
+  int64_t n_slots;
+  int32_t buf_rows;
+  int32_t max_new;
+  int32_t Hqk;
+  int32_t Hv;
+  int32_t group;
+  float scale;
+};
+
+template <typename IO>
 struct DecodeArgs {
   const IO* q;
   const IO* k;
@@ -103,6 +125,8 @@ hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, hipStream_t st);
 hipError_t launch_scan(const ScanArgs<float>& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st);
 hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, int ct, hipStream_t st);
+hipError_t launch_replay(const ReplayArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st);
+hipError_t launch_replay(const ReplayArgs<float>& a, int D, int n_req, int ct, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs<bf16_bits>& a, int D, int n_req, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs<float>& a, int D, int n_req, hipStream_t st);
 hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st);

@@ -273,6 +273,28 @@ gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t 
                             const float* buf_b, int32_t buf_rows, const int32_t* n_accepted,
                             int32_t* status);
 
+/* ReplaySSM verification outputs ("Caching less to serve more requests", section "What
+ * we changed": each request keeps one state and a log of the per-token inputs since it,
+ * and a layer's output is computed from the two).  Request r has m = n_logged[r] rows
+ * in the log of slot slot_ids[r] and n = n_new[r] new rows written behind them by the
+ * caller (log rows m .. m + n - 1).  The gated delta rule runs from the slot's state
+ * over log rows 0 .. m + n - 1, and o[r][i] = scale * S_{m+i} q_new[r][i] for i < n,
+ * with S_t the state after log row t.  Nothing is written to the state or the log: a
+ * later gdn_replay_flush accepts rows, a smaller count rolls them back.
+ *   state_pool, buf_k, buf_v, buf_a, buf_b, buf_rows (<= 64) as for gdn_replay_flush.
+ *   q_new [n_req][max_new][n_qk_heads][d] io_dtype; o [n_req][max_new][n_v_heads][d]
+ *   fp32, rows at or past n_new[r] not written.  n_logged, n_new [n_req] int32
+ *   (device).  Slot -1 or n = 0 writes nothing.  m < 0, n < 0, m + n > buf_rows,
+ *   n > max_new or a slot outside [-1, n_slots) writes nothing for that request and
+ *   sets GDN_ERR_CAPACITY in *status (device int32, may be NULL).  All device pointers;
+ *   libgdn allocates nothing. */
+gdn_status gdn_replay_forward(const gdn_layer* layer, hipStream_t stream, int32_t n_req,
+                              const float* state_pool, int64_t n_slots, const int32_t* slot_ids,
+                              const void* buf_k, const void* buf_v, const float* buf_a,
+                              const float* buf_b, int32_t buf_rows, const int32_t* n_logged,
+                              const int32_t* n_new, const void* q_new, int32_t max_new, float* o,
+                              int32_t* status);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,6 +129,29 @@ def recurrence(q, k, v, a, b, scale=1.0, S0=None, p0=0, block=0, want_o=True, th
     return o, S_out, ck
 
 
+def replay_outputs(S0, k, v, a, b, m, q_new, scale=1.0):
+    """ReplaySSM verification outputs ("Caching less to serve more requests", section
+    "What we changed": one state per request plus a log of the per-token inputs since
+    it, and a layer's output computed from the two).
+
+    S0: [Hv, dv, dk] (the request's state); k: [L, Hqk, dk], v: [L, Hv, dv], a, b:
+    [L, Hv] the log rows 0 .. L-1 with L = m + n; q_new: [n, Hqk, dk] the queries of log
+    rows m .. L-1.  Returns o [n, Hv, dv]: o[i] = scale * S_{m+i} q_new[i], with S_t the
+    state after log row t of the gated delta rule run from S0.  Written as the token
+    recurrence over all L rows with zero queries on the first m (whose outputs are
+    dropped).
+    """
+    q_new = _f64(q_new)
+    n = q_new.shape[0]
+    L = m + n
+    k = _f64(k)[:L]
+    assert k.shape[0] == L
+    q = np.zeros_like(k)
+    q[m:] = q_new
+    o, _, _ = recurrence(q, k, _f64(v)[:L], _f64(a)[:L], _f64(b)[:L], scale, S0)
+    return o[m:]
+
+
 def conv(x, w, tail=None, act=1, p0=0, block=0, threads=0):
     """Causal depthwise conv of width W = w.shape[1].
 

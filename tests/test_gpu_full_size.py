@@ -220,6 +220,35 @@ def test_flush_4b_full_size_all_heads(g, counts):
         assert rel_l2(f64(out[r + 1]), S_ref) <= TOL[torch.bfloat16], r
 
 
+def test_replay_4b_full_size_all_heads(g):
+    """Replay outputs at the flush workload's shape: 16 requests x 32 heads, a 32-slot log
+    holding the accepted rows (1..16 per request) and 16 new rows behind them."""
+    w = gi.FLUSH_4B
+    n_req, H, D, rows = w["n_req"], w["n_heads"], w["head_dim"], w["buf_rows"]
+    n_new = 16
+    layer = g.Layer(16, H, D, torch.bfloat16)
+    logged = gi.accepted_counts(n_req, w["seed"])
+    say(f"full-size replay logged={logged.tolist()} new={n_new}")
+    pool = gi.states(n_req, H, D, seed=w["seed"])
+    _, bk, bv, ba, bb = gi.qkvab(n_req * rows, 16, H, D, torch.bfloat16, seed=w["seed"])
+    bk, bv = bk.view(n_req, rows, 16, D), bv.view(n_req, rows, H, D)
+    ba, bb = ba.view(n_req, rows, H), bb.view(n_req, rows, H)
+    qn, _, _, _, _ = gi.qkvab(n_req * n_new, 16, H, D, torch.bfloat16, seed=w["seed"] + 1)
+    qn = qn.view(n_req, n_new, 16, D)
+    pd = pool.cuda()
+    o = torch.empty(n_req, n_new, H, D, device="cuda")
+    slots = torch.arange(n_req, dtype=torch.int32)
+    g.replay_forward(layer, pd, slots.cuda(), bk.cuda(), bv.cuda(), ba.cuda(), bb.cuda(), logged.cuda(),
+                     torch.full((n_req,), n_new, dtype=torch.int32).cuda(), qn.cuda(), o)
+    torch.cuda.synchronize()
+    assert torch.equal(pd.cpu(), pool)
+    out = o.cpu()
+    for r in range(n_req):
+        m = int(logged[r])
+        o_ref = oracle.replay_outputs(f64(pool[r]), f64(bk[r]), f64(bv[r]), f64(ba[r]), f64(bb[r]), m, f64(qn[r]))
+        assert rel_l2(f64(out[r]), o_ref) <= TOL[torch.bfloat16], r
+
+
 def test_long_27b_prefill_then_decode(g):
     """229,376 tokens at the 27B layer (256 checkpoints), then 256 concurrent decode
     requests.  The oracle checks one head of the prefill over every token and boundary,

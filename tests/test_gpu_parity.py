@@ -269,6 +269,83 @@ def test_flush_rejects_bad_count_on_device(g):
     assert same_bits(pool, before)
 
 
+# ------------------------------------------------------------------------- replay outputs
+
+REPLAY_CASES = [
+    # D, dtype, buf_rows, per request (slot, logged, new); slot -1 is padding
+    (128, torch.bfloat16, 32, [(4, 16, 16), (0, 0, 17), (2, 15, 1), (5, 3, 0), (-1, 2, 5), (1, 15, 17), (3, 7, 9)]),
+    (16, torch.float32, 32, [(1, 5, 11), (0, 0, 1), (3, 31, 1), (2, 12, 17)]),
+    (64, torch.bfloat16, 64, [(0, 40, 17), (2, 0, 3), (1, 63, 1), (3, 47, 17)]),
+    (32, torch.float32, 64, [(3, 30, 17), (0, 1, 16), (2, 0, 0)]),
+]
+
+
+@pytest.mark.parametrize("D,dtype,rows,reqs", REPLAY_CASES)
+def test_replay_forward_matches_oracle(g, D, dtype, rows, reqs):
+    """Outputs of the new rows from the slot's state and its log; the state, the log, the
+    rows past each request's count and the padding requests' outputs are untouched."""
+    Hqk, Hv, n_slots, max_new = 2, 4, 6, 17
+    layer = g.Layer(Hqk, Hv, D, dtype, scale=0.5)
+    say(f"replay D={D} {dtype} rows={rows} reqs={reqs}")
+    n_req = len(reqs)
+    pool = gi.states(n_slots, Hv, D, seed=91).cuda()
+    kk, vv, aa, bb = [], [], [], []
+    for s in range(n_slots):
+        _, k, v, a, b = gi.qkvab(rows, Hqk, Hv, D, dtype, seed=92 + s)
+        kk.append(k), vv.append(v), aa.append(a), bb.append(b)
+    buf_k, buf_v = torch.stack(kk).cuda(), torch.stack(vv).cuda()
+    buf_a, buf_b = torch.stack(aa).cuda(), torch.stack(bb).cuda()
+    qn, _, _, _, _ = gi.qkvab(n_req * max_new, Hqk, Hv, D, dtype, seed=99)
+    q_new = qn.view(n_req, max_new, Hqk, D).cuda()
+    # log rows past m + n and queries past n hold NaN: they must never be read
+    for r, (s, m, n) in enumerate(reqs):
+        if s >= 0:
+            nan_fill_(buf_k[s, m + n:]), nan_fill_(buf_v[s, m + n:])
+            nan_fill_(buf_a[s, m + n:]), nan_fill_(buf_b[s, m + n:])
+        nan_fill_(q_new[r, n:])
+    o = torch.full((n_req, max_new, Hv, D), 1234.5, device="cuda")
+    o_before = o.clone()
+    before = pool.clone()
+    logs = [t.clone() for t in (buf_k, buf_v, buf_a, buf_b)]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    i32 = lambda xs: torch.tensor(xs, dtype=torch.int32, device="cuda")
+    g.replay_forward(layer, pool, i32([x[0] for x in reqs]), buf_k, buf_v, buf_a, buf_b, i32([x[1] for x in reqs]),
+                     i32([x[2] for x in reqs]), q_new, o, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert same_bits(pool, before)
+    for t0, t1 in zip(logs, (buf_k, buf_v, buf_a, buf_b)):
+        assert same_bits(t0, t1)
+    for r, (s, m, n) in enumerate(reqs):
+        assert same_bits(o[r, n:], o_before[r, n:]), r
+        if s < 0 or n == 0:
+            assert same_bits(o[r], o_before[r]), r
+            continue
+        o_ref = oracle.replay_outputs(f64(before[s]), f64(buf_k[s]), f64(buf_v[s]), f64(buf_a[s]), f64(buf_b[s]), m,
+                                      f64(q_new[r, :n]), 0.5)
+        assert rel_l2(f64(o[r, :n]), o_ref) <= TOL[dtype], (r, s, m, n)
+
+
+def test_replay_forward_rejects_bad_counts_on_device(g):
+    D, H, rows, max_new = 32, 2, 32, 8
+    layer = g.Layer(H, H, D, torch.bfloat16)
+    pool = gi.states(2, H, D, seed=101).cuda()
+    buf = torch.zeros(2, rows, H, D, dtype=torch.bfloat16, device="cuda")
+    ab = torch.full((2, rows, H), 0.5, device="cuda")
+    q_new = torch.zeros(4, max_new, H, D, dtype=torch.bfloat16, device="cuda")
+    o = torch.full((4, max_new, H, D), 7.0, device="cuda")
+    o_before = o.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    i32 = lambda xs: torch.tensor(xs, dtype=torch.int32, device="cuda")
+    say("replay bad counts")
+    # logged + new past the log, new past max_new, a negative count, a slot out of range
+    g.replay_forward(layer, pool, i32([0, 1, 0, 5]), buf, buf, ab, ab, i32([30, 0, -1, 0]), i32([3, 9, 2, 1]),
+                     q_new, o, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1 << 8
+    assert same_bits(o, o_before)
+
+
 # ------------------------------------------------------------------------- conv
 
 @pytest.mark.parametrize("dtype,act", [(torch.bfloat16, 1), (torch.float32, 1), (torch.bfloat16, 0)])

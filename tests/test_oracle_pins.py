@@ -229,6 +229,51 @@ def test_flush_equals_sequential_application_and_ignores_rejected_rows():
     assert np.isfinite(Sf).all()
 
 
+def test_replay_outputs_fold_the_log_then_read_the_new_rows():
+    """Replay outputs from (state, log of m rows, n new rows) equal folding the m logged
+    rows into the state first and then running the n new rows with their queries; log
+    rows past m + n are never read."""
+    m, n, rows, Hqk, Hv, d = 6, 4, 13, 1, 2, 5
+    q, k, v, a, b = _inputs(rows, Hqk, Hv, d, 24)
+    k[m + n:] = np.nan
+    v[m + n:] = np.nan
+    a[m + n:] = np.nan
+    b[m + n:] = np.nan
+    S = rng(25).standard_normal((Hv, d, d))
+    o = oracle.replay_outputs(S, k, v, a, b, m, q[m:m + n], 0.7)
+    _, Sm, _ = oracle.recurrence(None, k[:m], v[:m], a[:m], b[:m], 1.0, S, want_o=False)
+    o2, _, _ = oracle.recurrence(q[m:m + n], k[m:m + n], v[m:m + n], a[m:m + n], b[m:m + n], 0.7, Sm)
+    assert o.shape == (n, Hv, d)
+    assert np.array_equal(o, o2)
+    assert np.isfinite(o).all()
+
+
+def test_replay_outputs_overwrite_closed_form():
+    """a = b = 1 with one-hot keys: each row replaces one column of the state with its
+    value (S <- S + (v - S k) k^T), so after log row t the state is S0 with the columns
+    of rows 0..t overwritten in order; the output of new row i is scale times that
+    state applied to its query."""
+    m, n, d, scale = 3, 3, 6, 0.5
+    cols = [4, 1, 4, 0, 2, 1]   # column 4 and column 1 are written twice
+    r = rng(26)
+    S0 = r.standard_normal((1, d, d))
+    k = np.zeros((m + n, 1, d))
+    for t, c in enumerate(cols):
+        k[t, 0, c] = 1.0
+    v = r.standard_normal((m + n, 1, d))
+    a = np.ones((m + n, 1))
+    b = np.ones((m + n, 1))
+    qn = r.standard_normal((n, 1, d))
+    o = oracle.replay_outputs(S0, k, v, a, b, m, qn, scale)
+    St = S0[0].copy()
+    want = []
+    for t, c in enumerate(cols):
+        St[:, c] = v[t, 0]
+        if t >= m:
+            want.append(scale * St @ qn[t - m, 0])
+    assert np.allclose(o[:, 0], np.array(want), rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- conv
 
 def test_conv_identity_taps():
