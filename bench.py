@@ -13,6 +13,8 @@ Reported beside it, each timed with HIP events on the stream the kernels run on:
   * the replay flush at the 4B-shaped layer (16 requests, 32 value heads x 128 x 128
     fp32 state, a 32-slot log, accepted rows uniform in 1..16, plus all-16 and all-17),
     rotating over enough state pools that every launch streams from HBM;
+  * the replay outputs at the same layer: 16 new rows behind each request's accepted
+    rows in the log, outputs of the new rows from the state and the log;
   * the decode step for 256 requests at the 27B shape;
   * the conv update alone;
   * the roofline of the dominant kernel (the chunk scan);
@@ -91,6 +93,15 @@ def flush_bytes(n_acc, heads=32, qk_heads=16, d=D):
     state = heads * d * d * 4
     row = qk_heads * d * 2 + heads * d * 2 + 2 * heads * 4
     return sum(2 * state + n * row for n in n_acc if n > 0)
+
+
+def replay_bytes(n_logged, n_new, heads=32, qk_heads=16, d=D):
+    """HBM bytes one replay launch must move: each request's state read once, its logged
+    and new log rows (bf16 k, v; fp32 a, b) and the new rows' queries read once, the new
+    rows' fp32 outputs written once."""
+    state = heads * d * d * 4
+    row = qk_heads * d * 2 + heads * d * 2 + 2 * heads * 4
+    return sum(state + (m + n_new) * row + n_new * (qk_heads * d * 2 + heads * d * 4) for m in n_logged)
 
 
 def main():
@@ -221,6 +232,26 @@ def main():
     flush_17 = time_flush(torch.full((n_req,), 17), reps)
     fb_u = flush_bytes(acc_u.tolist())
 
+    # ------------------------------------------------------------ replay outputs (4B layer)
+    # the verify step of the pages' drafts: 16 new rows behind each request's accepted
+    # rows (uniform in 1..16) in the same 32-slot log, outputs of the 16 new rows
+    n_new = 16
+    rq_new = gi.qkvab(n_req * n_new, 16, 32, D, torch.bfloat16, seed=1004)[0].view(n_req, n_new, 16, D).to(dev)
+    r_out = torch.empty(n_req, n_new, 32, D, dtype=torch.float32, device=dev)
+    logged_d = acc_u.to(torch.int32).to(dev)
+    new_d = torch.full((n_req,), n_new, dtype=torch.int32, device=dev)
+    for i in range(3):
+        g.replay_forward(fl_layer, fpools[i % n_pools], slots, bk, bv, ba, bb, logged_d, new_d, rq_new, r_out)
+    torch.cuda.synchronize()
+    ev = events(2)
+    ev[0].record()
+    for r in range(reps):
+        g.replay_forward(fl_layer, fpools[r % n_pools], slots, bk, bv, ba, bb, logged_d, new_d, rq_new, r_out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    replay_us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    rb = replay_bytes(acc_u.tolist(), n_new)
+
     # ------------------------------------------------------------ decode (27B layer, 256 requests)
     n_dec = 256
     dpool = gi.states(n_dec, H, D, seed=1005).to(dev)
@@ -262,6 +293,10 @@ def main():
                                "workload": "flush_4b_16req_H32_d128_32slots",
                                "hbm_gbs_u1_16": round(fb_u / (flush_u * 1e-6) / 1e9, 1),
                                "roof_us_u1_16": round(fb_u / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
+        "replay_forward_us": {"value": round(replay_us, 2),
+                              "workload": "replay_4b_16req_H32_d128_32slots_logged_u1_16_new16",
+                              "hbm_gbs": round(rb / (replay_us * 1e-6) / 1e9, 1),
+                              "roof_us": round(rb / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
         "decode_us": {"value": round(decode_us, 2), "workload": "decode_27b_256req_H48_d128",
                       "hbm_gbs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
                       "roof_us": round(dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
