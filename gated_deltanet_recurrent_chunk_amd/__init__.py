@@ -32,6 +32,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 GDN_F32, GDN_BF16 = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
+CONV_QK_L2NORM = 0x100  # OR into Layer.conv_act: unit L2 norm per q / k head after the conv
 SRC_ZERO, SRC_SLOT, SRC_CHECKPOINT = 0, 1, 2
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_BAD_DTYPE",
                 4: "GDN_ERR_BAD_VARLEN", 5: "GDN_ERR_OFF_BOUNDARY", 6: "GDN_ERR_PAGE_TOO_SMALL",
@@ -88,6 +89,8 @@ _decl("gdn_prefill_scan", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i
                                  _P(_Ckpt), _vp, _vp, _sz])
 _decl("gdn_decode_step", _i32, [_P(_Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp])
 _decl("gdn_replay_flush", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp])
+_decl("gdn_gates", _i32, [_P(_Layer), _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp])
+_decl("gdn_gated_norm", _i32, [_P(_Layer), _vp, _i64, _vp, _vp, _i64, _vp, ctypes.c_float, _vp])
 _decl("gdn_replay_forward", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                    _i32, _vp, _vp])
 
@@ -95,7 +98,8 @@ EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_state_bytes", "gdn_conv
             "gdn_checkpoint_bytes", "gdn_conv_channels", "gdn_cached_prefix_tokens", "gdn_floor_chunk",
             "gdn_count_boundaries", "gdn_block_size_for_state", "gdn_prefill_workspace_bytes",
             "gdn_conv_workspace_bytes", "gdn_conv_update", "gdn_chunk_prefill", "gdn_prefill_factorize",
-            "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush", "gdn_replay_forward")
+            "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush", "gdn_replay_forward",
+            "gdn_gates", "gdn_gated_norm")
 
 
 class GdnError(RuntimeError):
@@ -411,6 +415,40 @@ def replay_flush(layer: Layer, state_pool, slot_ids, buf_k, buf_v, buf_a, buf_b,
                                int(state_pool.shape[0]), _ptr(slot_ids), _ptr(buf_k), _ptr(buf_v), _ptr(buf_a),
                                _ptr(buf_b), int(buf_k.shape[1]), _ptr(n_accepted), _ptr(status))
     _check(st, "gdn_replay_flush")
+
+
+def gates(layer: Layer, ba, A_log, dt_bias, a, b, stream=None):
+    """Packed-core gates (gdn_gates): b = sigmoid(ba[:, :Hv]), a = exp(-exp(A_log) *
+    softplus(ba[:, Hv:2Hv] + dt_bias)).  ba: [tokens, >= 2 Hv] io dtype (rows may be wider);
+    A_log fp32 [Hv]; dt_bias io dtype [Hv]; a, b fp32 [tokens, Hv]."""
+    Hv = layer.n_v_heads
+    n = int(ba.shape[0])
+    _need(ba.dim() == 2 and ba.shape[1] >= 2 * Hv and ba.stride(1) == 1, "ba: [tokens, >= 2 Hv], unit column stride")
+    _need(ba.dtype == layer.io_dtype, "ba: io dtype")
+    _need(A_log.dtype == torch.float32 and A_log.numel() == Hv, "A_log: fp32 [Hv]")
+    _need(dt_bias.dtype == layer.io_dtype and dt_bias.numel() == Hv, "dt_bias: io dtype [Hv]")
+    _rows_ok(a, n, Hv, torch.float32, "a")
+    _rows_ok(b, n, Hv, torch.float32, "b")
+    st = _lib.gdn_gates(ctypes.byref(layer.c()), _stream(stream), n, _ptr(ba), int(ba.stride(0)), _ptr(A_log),
+                        _ptr(dt_bias), _ptr(a), _ptr(b))
+    _check(st, "gdn_gates")
+
+
+def gated_norm(layer: Layer, o, z, weight, out, eps=1e-6, stream=None):
+    """Gated RMSNorm of the output rows (gdn_gated_norm): out = o * rsqrt(mean(o^2) + eps)
+    * weight * silu(z) per (token, value head) row.  o fp32 [tokens, Hv, d]; z io dtype
+    [tokens, >= Hv*d] rows (or [tokens, Hv, d]); weight io dtype [d]; out io dtype."""
+    Hv, D = layer.n_v_heads, layer.head_dim
+    n = int(o.shape[0])
+    _rows_ok(o, n, Hv * D, torch.float32, "o")
+    z2 = z.reshape(z.shape[0], -1) if z.dim() == 3 and z.is_contiguous() else z
+    _need(z2.dim() == 2 and z2.shape[0] >= n and z2.shape[1] >= Hv * D and z2.stride(1) == 1, "z rows")
+    _need(z2.dtype == layer.io_dtype, "z: io dtype")
+    _need(weight.dtype == layer.io_dtype and weight.numel() == D and weight.is_contiguous(), "weight: io dtype [d]")
+    _rows_ok(out, n, Hv * D, layer.io_dtype, "out")
+    st = _lib.gdn_gated_norm(ctypes.byref(layer.c()), _stream(stream), n, _ptr(o), _ptr(z2), int(z2.stride(0)),
+                             _ptr(weight), float(eps), _ptr(out))
+    _check(st, "gdn_gated_norm")
 
 
 def replay_forward(layer: Layer, state_pool, slot_ids, buf_k, buf_v, buf_a, buf_b, n_logged, n_new, q_new, o,

@@ -427,6 +427,8 @@ gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn
     ca.page_bytes = (size_t)ckpt->page_bytes;
     ca.tail_offset = (size_t)L.state_bytes;
     ca.channels = L.channels;
+    ca.qk_channels = 2 * (int64_t)L.Hqk * L.D;
+    ca.head_dim = L.D;
     ca.block = ckpt->block;
     ca.act = L.act;
     return hip_status(launch_conv(ca, (int)tiles.size(), stream));
@@ -442,6 +444,8 @@ gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn
   ca.page_bytes = (size_t)ckpt->page_bytes;
   ca.tail_offset = (size_t)L.state_bytes;
   ca.channels = L.channels;
+  ca.qk_channels = 2 * (int64_t)L.Hqk * L.D;
+  ca.head_dim = L.D;
   ca.block = ckpt->block;
   ca.act = L.act;
   return hip_status(launch_conv(ca, (int)tiles.size(), stream));
@@ -495,6 +499,44 @@ gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t 
                       static_cast<const float*>(buf_v), buf_a, buf_b, status, n_slots, buf_rows, L.Hqk, L.Hv,
                       L.Hv / L.Hqk};
   return hip_status(launch_flush(fa, L.D, n_req, ct, stream));
+}
+
+gdn_status gdn_gates(const gdn_layer* layer, hipStream_t stream, int64_t n_tokens, const void* ba,
+                     int64_t ba_stride, const float* A_log, const void* dt_bias, float* a, float* b) {
+  LayerInfo L;
+  gdn_status s = check_layer(layer, &L);
+  if (s != GDN_OK) return s;
+  if (n_tokens < 0 || ba_stride < 2 * (int64_t)L.Hv) return GDN_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return GDN_OK;
+  if (!ba || !A_log || !dt_bias || !a || !b) return GDN_ERR_NULL_ARG;
+  if (L.io == GDN_BF16) {
+    GateArgs<bf16_bits> ga{static_cast<const bf16_bits*>(ba), A_log, static_cast<const bf16_bits*>(dt_bias), a, b,
+                           n_tokens, ba_stride, L.Hv};
+    return hip_status(launch_gates(ga, stream));
+  }
+  GateArgs<float> ga{static_cast<const float*>(ba), A_log, static_cast<const float*>(dt_bias), a, b, n_tokens,
+                     ba_stride, L.Hv};
+  return hip_status(launch_gates(ga, stream));
+}
+
+gdn_status gdn_gated_norm(const gdn_layer* layer, hipStream_t stream, int64_t n_tokens, const float* o,
+                          const void* z, int64_t z_stride, const void* weight, float eps, void* out) {
+  LayerInfo L;
+  gdn_status s = check_layer(layer, &L);
+  if (s != GDN_OK) return s;
+  // z rows are read 16 bytes at a time: a stride of whole 8-element groups
+  if (n_tokens < 0 || z_stride < (int64_t)L.Hv * L.D || z_stride % 8 != 0 || !(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return GDN_OK;
+  if (!o || !z || !weight || !out) return GDN_ERR_NULL_ARG;
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(weight, 16) || !aligned(out, 16)) return GDN_ERR_BAD_SHAPE;
+  if (L.io == GDN_BF16) {
+    NormArgs<bf16_bits> na{o, static_cast<const bf16_bits*>(z), static_cast<const bf16_bits*>(weight),
+                           static_cast<bf16_bits*>(out), n_tokens * L.Hv, z_stride, L.Hv, eps};
+    return hip_status(launch_gated_norm(na, L.D, stream));
+  }
+  NormArgs<float> na{o, static_cast<const float*>(z), static_cast<const float*>(weight), static_cast<float*>(out),
+                     n_tokens * L.Hv, z_stride, L.Hv, eps};
+  return hip_status(launch_gated_norm(na, L.D, stream));
 }
 
 gdn_status gdn_replay_forward(const gdn_layer* layer, hipStream_t stream, int32_t n_req, const float* state_pool,

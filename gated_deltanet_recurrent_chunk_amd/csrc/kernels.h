@@ -115,10 +115,40 @@ struct ConvArgs {
   size_t page_bytes;
   size_t tail_offset;  // byte offset of the conv tail inside a page
   int64_t channels;
+  int64_t qk_channels;  // 2 * Hqk * head_dim: the channels normalized per head (flag)
+  int32_t head_dim;
   int32_t block;
-  int32_t act;
+  int32_t act;          // gdn_act, optionally | GDN_CONV_QK_L2NORM
 };
 
+template <typename IO>
+struct GateArgs {
+  const IO* ba;          // [tokens][ba_stride]: b part at columns 0..Hv-1, a part at Hv..2Hv-1
+  const float* A_log;    // [Hv]
+  const IO* dt_bias;     // [Hv]
+  float* a;              // [tokens][Hv]
+  float* b;              // [tokens][Hv]
+  int64_t n_tokens;
+  int64_t ba_stride;
+  int32_t Hv;
+};
+
+template <typename IO>
+struct NormArgs {
+  const float* o;        // [rows][D] (rows = tokens * Hv)
+  const IO* z;           // token t: z + t * z_stride, heads [Hv][D]
+  const IO* w;           // [D]
+  IO* out;               // [rows][D]
+  int64_t n_rows;
+  int64_t z_stride;
+  int32_t Hv;
+  float eps;
+};
+
+hipError_t launch_gates(const GateArgs<bf16_bits>& a, hipStream_t st);
+hipError_t launch_gates(const GateArgs<float>& a, hipStream_t st);
+hipError_t launch_gated_norm(const NormArgs<bf16_bits>& a, int D, hipStream_t st);
+hipError_t launch_gated_norm(const NormArgs<float>& a, int D, hipStream_t st);
 hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, int n_chunks, hipStream_t st);
 hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, int n_chunks, hipStream_t st);
 hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, hipStream_t st);

@@ -10,7 +10,8 @@ gdn_status check_layer(const gdn_layer* layer, LayerInfo* out) {
   if (!layer) return GDN_ERR_NULL_ARG;
   const gdn_layer& l = *layer;
   if (l.io_dtype != GDN_F32 && l.io_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  if (l.conv_act != GDN_ACT_NONE && l.conv_act != GDN_ACT_SILU) return GDN_ERR_BAD_DTYPE;
+  const int32_t act = l.conv_act & ~GDN_CONV_QK_L2NORM;
+  if (act != GDN_ACT_NONE && act != GDN_ACT_SILU) return GDN_ERR_BAD_DTYPE;
   if (l.n_qk_heads <= 0 || l.n_v_heads <= 0) return GDN_ERR_BAD_SHAPE;
   // value heads share query/key heads in equal groups; a count that does not divide is
   // refused ("Hybrid linear attention (gated DeltaNet)", "Packed-core traces")

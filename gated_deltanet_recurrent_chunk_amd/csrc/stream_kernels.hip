@@ -189,7 +189,7 @@ __device__ __forceinline__ void unpack_row(const uint4& v, float (&out)[16 / siz
   }
 }
 
-template <typename IO, bool SILU>
+template <typename IO, bool SILU, bool NORM>
 __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int TR = kConvTile;
@@ -270,6 +270,20 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
       if constexpr (SILU) acc = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));
       yv[e] = acc;
     }
+    if constexpr (NORM) {
+      // unit L2 norm per q / k head: the head's values sit in head_dim / VEC consecutive
+      // lanes of one wave (heads start on such a lane group), summed by an xor butterfly
+      // (every lane ends with the same bits)
+      if (c0 < p.qk_channels) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ss = fmaf(yv[e], yv[e], ss);
+        for (int off = 1; off < p.head_dim / VEC; off <<= 1) ss += __shfl_xor(ss, off);
+        const float inv = rsqrtf(ss + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) yv[e] *= inv;
+      }
+    }
     store_vec<IO, VEC>(p.y + (tile.row + t) * C + c0, yv);
     if (bmask & (1u << t)) {
       {
@@ -342,10 +356,15 @@ static hipError_t launch_conv_t(const ConvArgs<IO>& a, int n_tiles, hipStream_t 
   const int64_t blocks = (int64_t)n_tiles * ((groups + 255) / 256);
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks);
-  if (a.act == GDN_ACT_SILU)
-    hipLaunchKernelGGL((conv_kernel<IO, true>), grid, dim3(256), 0, st, a);
+  const bool silu = (a.act & ~GDN_CONV_QK_L2NORM) == GDN_ACT_SILU, norm = (a.act & GDN_CONV_QK_L2NORM) != 0;
+  if (silu && norm)
+    hipLaunchKernelGGL((conv_kernel<IO, true, true>), grid, dim3(256), 0, st, a);
+  else if (silu)
+    hipLaunchKernelGGL((conv_kernel<IO, true, false>), grid, dim3(256), 0, st, a);
+  else if (norm)
+    hipLaunchKernelGGL((conv_kernel<IO, false, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((conv_kernel<IO, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((conv_kernel<IO, false, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st) {
@@ -354,5 +373,89 @@ hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st
 hipError_t launch_conv(const ConvArgs<float>& a, int n_tiles, hipStream_t st) {
   return launch_conv_t<float>(a, n_tiles, st);
 }
+
+// ==================================================================================
+// Gates of the packed core ("Hybrid linear attention (gated DeltaNet)", "Packed-core
+// traces": the core owns dt_bias and an fp32 A_log and takes the "ba" projection):
+//   b = sigmoid(ba_b),   a = exp(-exp(A_log) * softplus(ba_a + dt_bias))
+// per (token, value head), in fp32.  a is kept at or above the smallest normal float
+// so that its logarithm (the prefill's log-decay) stays finite.
+template <typename IO>
+__global__ __launch_bounds__(256) void gates_kernel(GateArgs<IO> p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.n_tokens * p.Hv) return;
+  const int64_t t = i / p.Hv;
+  const int h = (int)(i - t * p.Hv);
+  const IO* row = p.ba + t * p.ba_stride;
+  const float bx = to_f32(row[h]), ax = to_f32(row[p.Hv + h]);
+  const float x = ax + to_f32(p.dt_bias[h]);
+  // softplus(x) = log(1 + e^x), = x once e^-x is below fp32 resolution
+  const float sp = x > 20.f ? x : log1pf(expf(x));
+  p.a[i] = fmaxf(expf(-expf(p.A_log[h]) * sp), 1.17549435e-38f);
+  p.b[i] = 1.f / (1.f + expf(-bx));
+}
+
+// Gated RMSNorm of the output rows (the packed core's output is "gated-normalized value
+// rows", with a norm scale replicated over heads):
+//   out = o * (mean(o^2) + eps)^(-1/2) * w * silu(z)
+// per (token, value head) row of D values; D / 8 lanes per row, 8 values per lane, the
+// mean by an xor butterfly inside the lane group.
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void gated_norm_kernel(NormArgs<IO> p) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int j0 = (threadIdx.x % LPR) * 8;
+  if (row >= p.n_rows) return;  // whole lane groups leave together
+  const int64_t t = row / p.Hv;
+  const int h = (int)(row - t * p.Hv);
+  float ov[8], zv[8], wv[8];
+  load_vec<float, 8>(p.o + row * D + j0, ov);
+  load_vec<IO, 8>(p.z + t * p.z_stride + (int64_t)h * D + j0, zv);
+  load_vec<IO, 8>(p.w + j0, wv);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(ov[e], ov[e], ss);
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off);
+  const float r = rsqrtf(ss * (1.f / D) + p.eps);
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (ov[e] * r) * wv[e] * (zv[e] / (1.f + __expf(-zv[e])));
+  store_vec<IO, 8>(p.out + row * D + j0, y);
+}
+
+template <typename IO>
+static hipError_t launch_gates_t(const GateArgs<IO>& a, hipStream_t st) {
+  const int64_t n = a.n_tokens * a.Hv;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gates_kernel<IO>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_gates(const GateArgs<bf16_bits>& a, hipStream_t st) { return launch_gates_t(a, st); }
+hipError_t launch_gates(const GateArgs<float>& a, hipStream_t st) { return launch_gates_t(a, st); }
+
+template <typename IO, int D>
+static hipError_t launch_norm_t(const NormArgs<IO>& a, hipStream_t st) {
+  if (a.n_rows == 0) return hipSuccess;
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t blocks = (a.n_rows + RPB - 1) / RPB;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gated_norm_kernel<IO, D>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+template <typename IO>
+static hipError_t launch_norm_d(const NormArgs<IO>& a, int D, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_norm_t<IO, 16>(a, st);
+    case 32: return launch_norm_t<IO, 32>(a, st);
+    case 64: return launch_norm_t<IO, 64>(a, st);
+    case 128: return launch_norm_t<IO, 128>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+hipError_t launch_gated_norm(const NormArgs<bf16_bits>& a, int D, hipStream_t st) { return launch_norm_d(a, D, st); }
+hipError_t launch_gated_norm(const NormArgs<float>& a, int D, hipStream_t st) { return launch_norm_d(a, D, st); }
 
 }  // namespace gdn

@@ -150,6 +150,21 @@ def conv_inputs(T: int, channels: int, width: int = 4, io_dtype=torch.bfloat16, 
     return x, w
 
 
+def core_inputs(T: int, n_v_heads: int, head_dim: int, io_dtype=torch.bfloat16, seed: int = 0):
+    """Inputs of the packed core's gate and output-norm steps: the "ba" projection rows
+    [T, 2 Hv] (io dtype, N(0, 2)), A_log [Hv] (fp32, log of U[1, 16]), dt_bias [Hv] (io
+    dtype, N(0, 1)), an output o [T, Hv, d] (fp32, N(0, 1)), the gate rows z [T, Hv, d]
+    (io dtype, N(0, 1)) and the norm scale [d] (io dtype, 1 + 0.1 N(0, 1))."""
+    g = _gen(seed, 40_000)
+    ba = (2.0 * torch.randn(T, 2 * n_v_heads, generator=g)).to(io_dtype)
+    A_log = torch.log(1.0 + 15.0 * torch.rand(n_v_heads, generator=g)).to(torch.float32)
+    dt_bias = torch.randn(n_v_heads, generator=g).to(io_dtype)
+    o = torch.randn(T, n_v_heads, head_dim, generator=g).to(torch.float32)
+    z = torch.randn(T, n_v_heads, head_dim, generator=g).to(io_dtype)
+    weight = (1.0 + 0.1 * torch.randn(head_dim, generator=g)).to(io_dtype)
+    return ba, A_log, dt_bias, o, z, weight
+
+
 def conv_tail(n: int, channels: int, width: int = 4, io_dtype=torch.bfloat16, seed: int = 0):
     """Draw n conv tails [n, width - 1, C]."""
     g = _gen(seed, 30_000)

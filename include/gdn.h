@@ -73,6 +73,12 @@ typedef enum gdn_status {
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 typedef enum gdn_act { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_act;
+/* Flag OR-ed into gdn_layer.conv_act: after the activation, every q and k head of a
+ * conv output row (channels [0, 2 * n_qk_heads * head_dim), head_dim values each) is
+ * scaled to unit L2 norm, y <- y * (sum y^2 + 1e-6)^(-1/2): the post-conv step of the
+ * packed core ("Hybrid linear attention (gated DeltaNet)", "Packed-core traces"), done
+ * inside the conv pass.  Value channels and the stored tails are unaffected. */
+#define GDN_CONV_QK_L2NORM 0x100
 
 /* Layer descriptor.  head_dim is d_k = d_v and must be 16, 32, 64 or 128.
  * n_v_heads must be a positive multiple of n_qk_heads: invalid dimensions and head
@@ -272,6 +278,29 @@ gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t 
                             const void* buf_k, const void* buf_v, const float* buf_a,
                             const float* buf_b, int32_t buf_rows, const int32_t* n_accepted,
                             int32_t* status);
+
+/* Gates of the packed core ("Hybrid linear attention (gated DeltaNet)", "Packed-core
+ * traces": the core owns dt_bias and a float32 A_log and takes the "ba" projection).
+ * For each token t and value head h, in fp32:
+ *   b[t][h] = sigmoid(ba[t][h]),
+ *   a[t][h] = exp(-exp(A_log[h]) * softplus(ba[t][Hv + h] + dt_bias[h])),
+ * a kept at or above the smallest normal float (its log is the prefill's log-decay).
+ *   ba: token t at ba + t * ba_stride (ba_stride >= 2 * n_v_heads elements), io_dtype;
+ *   A_log [n_v_heads] fp32; dt_bias [n_v_heads] io_dtype; a, b [n_tokens][n_v_heads]
+ *   fp32, the decay and write strength gdn_chunk_prefill and gdn_decode_step take. */
+gdn_status gdn_gates(const gdn_layer* layer, hipStream_t stream, int64_t n_tokens, const void* ba,
+                     int64_t ba_stride, const float* A_log, const void* dt_bias, float* a, float* b);
+
+/* Gated RMSNorm of the output rows (the packed core's output is "gated-normalized value
+ * rows", with one norm scale replicated over the heads; same page and section).  For
+ * each token t, value head h and channel j:
+ *   out[t][h][j] = o[t][h][j] * (mean_j o[t][h][j]^2 + eps)^(-1/2) * weight[j] * silu(z[t][h][j]).
+ *   o [n_tokens][n_v_heads][d] fp32 (the prefill or decode output); z: token t at
+ *   z + t * z_stride, [n_v_heads][d] io_dtype (z_stride a multiple of 8 elements, at
+ *   least n_v_heads * d); weight [d] io_dtype; out [n_tokens][n_v_heads][d] io_dtype.
+ *   o, z, weight, out 16-byte aligned; eps >= 0. */
+gdn_status gdn_gated_norm(const gdn_layer* layer, hipStream_t stream, int64_t n_tokens, const float* o,
+                          const void* z, int64_t z_stride, const void* weight, float eps, void* out);
 
 /* ReplaySSM verification outputs ("Caching less to serve more requests", section "What
  * we changed": each request keeps one state and a log of the per-token inputs since it,

@@ -179,6 +179,48 @@ def conv(x, w, tail=None, act=1, p0=0, block=0, threads=0):
     return y, tail_out, ck
 
 
+# ---------------------------------------------------------------- packed-core steps
+# "Hybrid linear attention (gated DeltaNet)", "Packed-core traces": the packed core
+# takes qkvz plus the "ba" projection, owns the conv, dt_bias, an fp32 A_log and a norm
+# scale replicated over heads, and returns gated-normalized value rows.  The page names
+# the steps without formulas; the readings below are the standard gated DeltaNet ones.
+
+def l2norm_qk_heads(y, n_qk_heads: int, head_dim: int, eps: float = 1e-6):
+    """The post-conv step: each q and k head of a conv output row (channels
+    [0, 2 * n_qk_heads * head_dim), head_dim values per head) scaled to unit L2 norm,
+    y / sqrt(sum y^2 + eps); the value channels pass unchanged.  y: [L, C]."""
+    y = _f64(y).copy()
+    L = y.shape[0]
+    qk = 2 * n_qk_heads * head_dim
+    heads = y[:, :qk].reshape(L, 2 * n_qk_heads, head_dim)
+    ss = (heads * heads).sum(axis=2, keepdims=True)
+    y[:, :qk] = (heads / np.sqrt(ss + eps)).reshape(L, qk)
+    return y
+
+
+def gates(ba, A_log, dt_bias, n_v_heads: int):
+    """The gates from the "ba" projection: b = sigmoid(ba[:, :Hv]) and
+    a = exp(-exp(A_log) * softplus(ba[:, Hv:2Hv] + dt_bias)), a kept at or above 2^-126
+    (the smallest normal fp32 value, so that the fp32 decay the prefill takes has a
+    finite logarithm).  Returns (a, b), [L, Hv]."""
+    ba = _f64(ba)
+    Hv = n_v_heads
+    x = ba[:, Hv:2 * Hv] + _f64(dt_bias)[None, :]
+    softplus = np.logaddexp(0.0, x)
+    a = np.maximum(np.exp(-np.exp(_f64(A_log))[None, :] * softplus), 2.0 ** -126)
+    b = 1.0 / (1.0 + np.exp(-ba[:, :Hv]))
+    return a, b
+
+
+def gated_norm(o, z, weight, eps: float = 1e-6):
+    """Gated RMSNorm of output rows: o * (mean(o^2) + eps)^(-1/2) * weight * silu(z) over
+    the last axis (one row per token and value head).  o, z: [..., d]; weight: [d]."""
+    o = _f64(o)
+    z = _f64(z)
+    r = 1.0 / np.sqrt((o * o).mean(axis=-1, keepdims=True) + eps)
+    return o * r * _f64(weight) * (z / (1.0 + np.exp(-z)))
+
+
 def cached_prefix_tokens(shared: int, block: int) -> int:
     return int(_load().gdn_oracle_cached_prefix_tokens(shared, block))
 

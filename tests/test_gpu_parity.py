@@ -269,6 +269,82 @@ def test_flush_rejects_bad_count_on_device(g):
     assert same_bits(pool, before)
 
 
+# ------------------------------------------------------------------------- packed-core steps
+
+@pytest.mark.parametrize("Hqk,Hv,D,dtype", [(2, 4, 128, torch.bfloat16), (1, 2, 16, torch.float32),
+                                            (3, 3, 32, torch.bfloat16), (2, 2, 64, torch.float32)])
+def test_conv_with_qk_l2norm_matches_oracle(g, Hqk, Hv, D, dtype):
+    """The conv with the post-conv step fused: q and k heads of every output row at unit
+    norm, value channels and tails as without it."""
+    block = 16
+    layer = g.Layer(Hqk, Hv, D, dtype, conv_act=g.ACT_SILU | g.CONV_QK_L2NORM)
+    C = layer.conv_channels
+    lens, starts = [37, 70, 5], [0, 32, 7]
+    say(f"conv+l2norm Hqk={Hqk} Hv={Hv} D={D} {dtype}")
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    x, w = gi.conv_inputs(cu[-1], C, 4, dtype, seed=111)
+    tails0 = gi.conv_tail(len(lens), C, 4, dtype, seed=112)
+    n_b = [oracle.count_boundaries(s_, L, block) for s_, L in zip(starts, lens)]
+    pool = make_pool(g, layer, sum(n_b) + 1, block)
+    td = tails0.cuda()
+    out_t = nan_fill_(torch.empty(len(lens), 3, C, dtype=dtype, device="cuda"))
+    refs = [("zero", None, out_t[0]), ("slot", td[1], out_t[1]), ("slot", td[2], out_t[2])]
+    y = nan_fill_(torch.empty(cu[-1], C, dtype=dtype, device="cuda"))
+    g.conv_update(layer, x.cuda(), w.cuda(), refs, cu, starts, y, ckpt=pool, page_ids=list(range(sum(n_b))))
+    torch.cuda.synchronize()
+    for i, (s_, L) in enumerate(zip(starts, lens)):
+        r0 = cu[i]
+        y_ref, t_ref, _ = oracle.conv(f64(x[r0:r0 + L]), f64(w), None if i == 0 else f64(tails0[i]), 1, s_, block)
+        y_ref = oracle.l2norm_qk_heads(y_ref, Hqk, D)
+        if dtype == torch.bfloat16:
+            assert rel_l2(f64(y[r0:r0 + L]), oracle.bf16_round(y_ref)) <= 1e-3, i
+        else:
+            assert rel_l2(f64(y[r0:r0 + L]), y_ref) <= 1e-5, i
+        assert np.array_equal(f64(out_t[i]), t_ref), i
+    qk = 2 * Hqk * D
+    heads = f64(y[:, :qk]).reshape(cu[-1], 2 * Hqk, D)
+    assert np.allclose(np.linalg.norm(heads, axis=2), 1.0, atol=1e-2 if dtype == torch.bfloat16 else 1e-5)
+
+
+@pytest.mark.parametrize("Hv,dtype", [(48, torch.bfloat16), (32, torch.float32), (5, torch.bfloat16)])
+def test_gates_match_oracle(g, Hv, dtype):
+    T = 301
+    layer = g.Layer(Hv, Hv, 16, dtype)
+    ba, A_log, dt_bias, _, _, _ = gi.core_inputs(T, Hv, 16, dtype, seed=121)
+    say(f"gates Hv={Hv} {dtype}")
+    # ba rows inside a wider packed row (stride 2 Hv + 6)
+    wide = torch.zeros(T, 2 * Hv + 6, dtype=dtype)
+    wide[:, :2 * Hv] = ba
+    a = torch.full((T, Hv), float("nan"), device="cuda")
+    b = torch.full((T, Hv), float("nan"), device="cuda")
+    g.gates(layer, wide.cuda(), A_log.cuda(), dt_bias.cuda(), a, b)
+    torch.cuda.synchronize()
+    a_ref, b_ref = oracle.gates(f64(ba), f64(A_log), f64(dt_bias), Hv)
+    # the decay is compared as the log-decay the prefill takes: fp32 evaluation of
+    # exp(-E) carries a relative error of about E * 1e-7
+    ga, g_ref = np.log(f64(a)), np.log(a_ref)
+    assert np.max(np.abs(ga - g_ref) / np.maximum(np.abs(g_ref), 1.0)) <= 1e-5
+    assert np.max(np.abs(f64(b) - b_ref) / b_ref) <= 1e-5
+    assert (f64(a) >= 2.0 ** -126).all() and (f64(a) <= 1).all()
+
+
+@pytest.mark.parametrize("Hv,D,dtype", [(48, 128, torch.bfloat16), (4, 16, torch.float32), (3, 64, torch.bfloat16),
+                                        (2, 32, torch.float32)])
+def test_gated_norm_matches_oracle(g, Hv, D, dtype):
+    T = 77
+    layer = g.Layer(Hv, Hv, D, dtype)
+    _, _, _, o, z, wgt = gi.core_inputs(T, Hv, D, dtype, seed=131)
+    say(f"gated norm Hv={Hv} D={D} {dtype}")
+    out = nan_fill_(torch.empty(T, Hv, D, dtype=dtype, device="cuda"))
+    g.gated_norm(layer, o.cuda(), z.cuda(), wgt.cuda(), out, eps=1e-6)
+    torch.cuda.synchronize()
+    ref = oracle.gated_norm(f64(o), f64(z), f64(wgt), 1e-6)
+    if dtype == torch.bfloat16:
+        assert rel_l2(f64(out), oracle.bf16_round(ref)) <= 1e-3
+    else:
+        assert rel_l2(f64(out), ref) <= 1e-5
+
+
 # ------------------------------------------------------------------------- replay outputs
 
 REPLAY_CASES = [

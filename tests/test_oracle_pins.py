@@ -274,6 +274,65 @@ def test_replay_outputs_overwrite_closed_form():
     assert np.allclose(o[:, 0], np.array(want), rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- packed-core steps
+
+def test_l2norm_qk_heads_hand_values():
+    """A 3-4-5 head becomes (0.6, 0.8); value channels pass unchanged; a zero head stays 0."""
+    y = np.array([[3.0, 4.0, 0.0, -2.5, 7.0, -2.0]])     # Hqk = 1, d = 2: q, k heads, then v
+    out = oracle.l2norm_qk_heads(y, 1, 2, eps=0.0)
+    assert np.array_equal(out[0, :4], [0.6, 0.8, 0.0, -1.0])
+    assert np.array_equal(out[0, 4:], [7.0, -2.0])
+    y[0, 2:4] = 0.0
+    out = oracle.l2norm_qk_heads(y, 1, 2, eps=1e-6)
+    assert np.array_equal(out[0, 2:4], [0.0, 0.0])
+    assert abs(out[0, 0] - 3.0 / np.sqrt(25.0 + 1e-6)) == 0.0
+
+
+def test_l2norm_qk_heads_unit_norm_and_direction():
+    r = rng(27)
+    y = r.standard_normal((5, 2 * 3 * 8 + 16)) * 4.0
+    out = oracle.l2norm_qk_heads(y, 3, 8)
+    h = out[:, :48].reshape(5, 6, 8)
+    assert np.allclose(np.linalg.norm(h, axis=2), 1.0, atol=1e-7)
+    hy = y[:, :48].reshape(5, 6, 8)
+    cos = (h * hy).sum(axis=2) / np.linalg.norm(hy, axis=2)
+    assert np.allclose(cos, 1.0, atol=1e-12)
+    assert np.array_equal(out[:, 48:], y[:, 48:])
+
+
+def test_gates_hand_values():
+    """At zero inputs softplus is log 2: a = exp(-log 2) = 1/2 and b = sigmoid(0) = 1/2;
+    with A_log = log 2 the decay doubles in log space, a = 1/4; large negative inputs
+    give no decay and large positive b inputs full write strength."""
+    Hv = 2
+    ba = np.zeros((1, 2 * Hv))
+    a, b = oracle.gates(ba, np.array([0.0, np.log(2.0)]), np.zeros(Hv), Hv)
+    assert np.allclose(a, [[0.5, 0.25]], rtol=1e-15, atol=0) and np.array_equal(b, [[0.5, 0.5]])
+    ba = np.array([[40.0, -3.0, -60.0, 1.5]])
+    a, b = oracle.gates(ba, np.array([0.0, 0.0]), np.array([0.0, -1.5]), Hv)
+    assert a[0, 0] == 1.0 and np.isclose(a[0, 1], 0.5, rtol=1e-15)   # softplus(0) for head 1
+    assert b[0, 0] == 1.0 and np.isclose(b[0, 1], 1.0 / (1.0 + np.exp(3.0)), rtol=1e-15)
+    # a decay past fp32's normal range stops at 2^-126: exp(-16 * 10) ~ 1e-70
+    a, _ = oracle.gates(np.array([[0.0, 10.0]]), np.array([np.log(16.0)]), np.zeros(1), 1)
+    assert a[0, 0] == 2.0 ** -126
+
+
+def test_gated_norm_hand_values_and_scale_invariance():
+    """o = (3, 4): mean square 12.5, so the normalized row is (3, 4) / sqrt(12.5); a zero
+    gate input gives silu(0) = 0; scaling o leaves the output unchanged (eps = 0)."""
+    o = np.array([[3.0, 4.0]])
+    z = np.array([[1.0, 0.0]])
+    w = np.array([2.0, 5.0])
+    out = oracle.gated_norm(o, z, w, eps=0.0)
+    silu1 = 1.0 / (1.0 + np.exp(-1.0))
+    assert np.isclose(out[0, 0], 3.0 / np.sqrt(12.5) * 2.0 * silu1, rtol=1e-15) and out[0, 1] == 0.0
+    r = rng(28)
+    o = r.standard_normal((4, 3, 16))
+    z = r.standard_normal((4, 3, 16))
+    w = r.standard_normal(16)
+    assert np.allclose(oracle.gated_norm(7.0 * o, z, w, eps=0.0), oracle.gated_norm(o, z, w, eps=0.0), rtol=1e-13)
+
+
 # ---------------------------------------------------------------- conv
 
 def test_conv_identity_taps():
