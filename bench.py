@@ -16,7 +16,9 @@ Reported beside it, each timed with HIP events on the stream the kernels run on:
   * the replay outputs at the same layer: 16 new rows behind each request's accepted
     rows in the log, outputs of the new rows from the state and the log;
   * the decode step for 256 requests at the 27B shape;
-  * the conv update alone;
+  * the conv update alone, and the packed-core steps at the same layer: the conv with
+    the per-head q/k L2 norm fused, the gates from the "ba" projection, the gated RMSNorm
+    of the output rows;
   * the roofline of the dominant kernel (the chunk scan);
   * the fp64 CPU oracle timed on a bounded sample of the same workload.
 Prints one JSON line.
@@ -191,6 +193,20 @@ def main():
     fact_ms = time_stage(lambda: g.prefill_factorize(layer, q, k, a, b, cu, sp, BLOCK, ws), kreps)
     scan_ms = time_stage(lambda: g.prefill_scan(layer, q, k, v, cu, sp, [("zero", None, S)], o, ws, ckpt=pool,
                                                 page_ids=page_ids), kreps)
+    # packed-core steps at the same layer: the conv with the per-head q/k L2 norm fused,
+    # the gates from the "ba" projection, the gated RMSNorm of the output rows
+    nlayer = g.Layer(H, H, D, torch.bfloat16, scale=1.0, conv_act=g.ACT_SILU | g.CONV_QK_L2NORM)
+    conv_norm_ms = time_stage(lambda: g.conv_update(nlayer, x, w, [("zero", None, tail)], cu, sp, y, ckpt=pool,
+                                                    page_ids=page_ids, workspace=cws), kreps)
+    ba, A_log, dt_bias, _, zc, wn = gi.core_inputs(T, H, D, torch.bfloat16, seed=1006)
+    ba, A_log, dt_bias, zc, wn = (t_.to(dev) for t_ in (ba, A_log, dt_bias, zc, wn))
+    ga, gb = torch.empty(T, H, device=dev), torch.empty(T, H, device=dev)
+    gates_ms = time_stage(lambda: g.gates(layer, ba, A_log, dt_bias, ga, gb), kreps)
+    onorm = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    norm_ms = time_stage(lambda: g.gated_norm(layer, o, zc, wn, onorm), kreps)
+    norm_bytes = T * H * D * (4 + 2 + 2)
+    gate_bytes = T * 2 * H * 2 + 2 * T * H * 4
+
     alg = scan_algorithmic_flops(T, H)
     passes = scan_pass_flops(T, H)
     achieved_tflops = alg / (scan_ms * 1e-3) / 1e12
@@ -301,6 +317,11 @@ def main():
                       "hbm_gbs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
                       "roof_us": round(dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
         "conv": {"us": round(conv_ms * 1e3, 2), "hbm_gbs": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1)},
+        "core_steps_us": {"conv_with_qk_l2norm": round(conv_norm_ms * 1e3, 2), "gates": round(gates_ms * 1e3, 2),
+                          "gated_norm": round(norm_ms * 1e3, 2),
+                          "gated_norm_hbm_gbs": round(norm_bytes / (norm_ms * 1e-3) / 1e9, 1),
+                          "gates_hbm_gbs": round(gate_bytes / (gates_ms * 1e-3) / 1e9, 1),
+                          "workload": "27b layer, 8192 tokens x 48 heads x 128"},
         "roofline": {
             "kernel": "scan_staged_kernel<bf16,128>",
             "bound": "mfma",
