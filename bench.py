@@ -11,7 +11,8 @@ K timed steps (inputs resident in HBM, synthetic, seeded).
 
 Reported beside it, each timed with HIP events on the stream the kernels run on:
   * the replay flush at the 4B-shaped layer (16 requests, 32 value heads x 128 x 128
-    fp32 state, a 32-slot log, accepted rows uniform in 1..16, plus all-16 and all-17),
+    fp32 state, a 32-slot log, accepted rows uniform in 1..16, plus all-16 and all-17;
+    and long drafts in a 64-slot log, all-32 and all-33),
     rotating over enough state pools that every launch streams from HBM;
   * the replay outputs at the same layer: 16 new rows behind each request's accepted
     rows in the log, outputs of the new rows from the state and the log;
@@ -247,6 +248,27 @@ def main():
     flush_16 = time_flush(torch.full((n_req,), 16), reps)
     flush_17 = time_flush(torch.full((n_req,), 17), reps)
     fb_u = flush_bytes(acc_u.tolist())
+    # long drafts: a 64-slot log, 32 accepted rows per request (and 33: no cliff past a block)
+    rows64 = 64
+    _, lk, lv, la, lb = gi.qkvab(n_req * rows64, 16, 32, D, torch.bfloat16, seed=1007)
+    lk, lv = lk.view(n_req, rows64, 16, D).to(dev), lv.view(n_req, rows64, 32, D).to(dev)
+    la, lb = la.view(n_req, rows64, 32).to(dev), lb.view(n_req, rows64, 32).to(dev)
+
+    def time_flush64(acc, reps):
+        acc_d = acc.to(torch.int32).to(dev)
+        for i in range(3):
+            g.replay_flush(fl_layer, fpools[i % n_pools], slots, lk, lv, la, lb, acc_d)
+        torch.cuda.synchronize()
+        ev = events(2)
+        ev[0].record()
+        for r in range(reps):
+            g.replay_flush(fl_layer, fpools[r % n_pools], slots, lk, lv, la, lb, acc_d)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    flush_32 = time_flush64(torch.full((n_req,), 32), reps)
+    flush_33 = time_flush64(torch.full((n_req,), 33), reps)
 
     # ------------------------------------------------------------ replay outputs (4B layer)
     # the verify step of the pages' drafts: 16 new rows behind each request's accepted
@@ -306,6 +328,8 @@ def main():
         "kernel_ms": {"conv": round(conv_ms, 4), "factorize": round(fact_ms, 4), "scan": round(scan_ms, 4)},
         "flush_us_per_layer": {"accepted_u1_16": round(flush_u, 2), "all_16": round(flush_16, 2),
                                "all_17": round(flush_17, 2),
+                               "log64_all_32": round(flush_32, 2), "log64_all_33": round(flush_33, 2),
+                               "hbm_gbs_log64_all_32": round(flush_bytes([32] * n_req) / (flush_32 * 1e-6) / 1e9, 1),
                                "workload": "flush_4b_16req_H32_d128_32slots",
                                "hbm_gbs_u1_16": round(fb_u / (flush_u * 1e-6) / 1e9, 1),
                                "roof_us_u1_16": round(fb_u / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
