@@ -89,6 +89,8 @@ _decl("gdn_prefill_scan", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i
                                  _P(_Ckpt), _vp, _vp, _sz])
 _decl("gdn_decode_step", _i32, [_P(_Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp])
 _decl("gdn_replay_flush", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp])
+_decl("gdn_decode_mixed", _i32, [_P(_Layer), _vp, _i32, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp,
+                                 _vp, _vp, _vp])
 _decl("gdn_gates", _i32, [_P(_Layer), _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp])
 _decl("gdn_gated_norm", _i32, [_P(_Layer), _vp, _i64, _vp, _vp, _i64, _vp, ctypes.c_float, _vp])
 _decl("gdn_replay_forward", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
@@ -99,7 +101,7 @@ EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_state_bytes", "gdn_conv
             "gdn_count_boundaries", "gdn_block_size_for_state", "gdn_prefill_workspace_bytes",
             "gdn_conv_workspace_bytes", "gdn_conv_update", "gdn_chunk_prefill", "gdn_prefill_factorize",
             "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush", "gdn_replay_forward",
-            "gdn_gates", "gdn_gated_norm")
+            "gdn_gates", "gdn_gated_norm", "gdn_decode_mixed")
 
 
 class GdnError(RuntimeError):
@@ -415,6 +417,33 @@ def replay_flush(layer: Layer, state_pool, slot_ids, buf_k, buf_v, buf_a, buf_b,
                                int(state_pool.shape[0]), _ptr(slot_ids), _ptr(buf_k), _ptr(buf_v), _ptr(buf_a),
                                _ptr(buf_b), int(buf_k.shape[1]), _ptr(n_accepted), _ptr(status))
     _check(st, "gdn_replay_flush")
+
+
+def decode_mixed(layer: Layer, q, k, v, a, b, state_pool, slot_ids, rows, o, status=None, stream=None,
+                 qk_stride=None, v_stride=None):
+    """Decode tokens of a mixed batch (gdn_decode_mixed): request r's token is row rows[r] of
+    the packed token arrays q, k [n_rows, (row of qk_stride)], v, a, b [n_rows, Hv], o
+    [n_rows, Hv, d] that the batch's prefill sequences share."""
+    n_req = int(slot_ids.numel())
+    D, Hv, Hqk = layer.head_dim, layer.n_v_heads, layer.n_qk_heads
+    qs = qk_stride if qk_stride is not None else Hqk * D
+    vs = v_stride if v_stride is not None else Hv * D
+    n_rows = int(o.shape[0])
+    _need(slot_ids.dtype == torch.int32 and rows.dtype == torch.int32 and rows.numel() >= n_req,
+          "int32 slot_ids / rows")
+    _need(state_pool.dtype == torch.float32 and state_pool.is_contiguous()
+          and tuple(state_pool.shape[1:]) == (Hv, D, D), "state_pool must be fp32 [slots, Hv, d, d]")
+    for t_, st_, heads, name in ((q, qs, Hqk, "q"), (k, qs, Hqk, "k"), (v, vs, Hv, "v")):
+        _need(t_.dtype == layer.io_dtype, f"{name}: io dtype")
+        span = t_.untyped_storage().nbytes() // t_.element_size() - t_.storage_offset()
+        _need(n_rows == 0 or span >= (n_rows - 1) * st_ + heads * D, f"{name}: storage too small for {n_rows} rows")
+    _rows_ok(a, n_rows, Hv, torch.float32, "a")
+    _rows_ok(b, n_rows, Hv, torch.float32, "b")
+    _rows_ok(o, n_rows, Hv * D, torch.float32, "o")
+    st = _lib.gdn_decode_mixed(ctypes.byref(layer.c()), _stream(stream), n_req, n_rows, _ptr(q), _ptr(k), _ptr(v),
+                               qs, vs, _ptr(a), _ptr(b), _ptr(state_pool), int(state_pool.shape[0]), _ptr(slot_ids),
+                               _ptr(rows), _ptr(o), _ptr(status))
+    _check(st, "gdn_decode_mixed")
 
 
 def gates(layer: Layer, ba, A_log, dt_bias, a, b, stream=None):

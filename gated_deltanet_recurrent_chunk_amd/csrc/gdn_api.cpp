@@ -218,6 +218,42 @@ gdn_status check_states(const PrefillPrep& P, const gdn_state_ref* states, int32
   return GDN_OK;
 }
 
+// Decode launch shared by the dense and the mixed-batch entry points.
+gdn_status decode_rows(const LayerInfo& L, hipStream_t stream, int32_t n_req, int64_t n_rows, const void* q,
+                       const void* k, const void* v, int64_t qk_stride, int64_t v_stride, const float* a,
+                       const float* b, float* state_pool, int64_t n_slots, const int32_t* slot_ids,
+                       const int32_t* rows, float* o, int32_t* status) {
+  auto fill = [&](auto& da, auto tag) {
+    using IO = decltype(tag);
+    da.q = static_cast<const IO*>(q);
+    da.k = static_cast<const IO*>(k);
+    da.v = static_cast<const IO*>(v);
+    da.a = a;
+    da.b = b;
+    da.state_pool = state_pool;
+    da.slot_ids = slot_ids;
+    da.o = o;
+    da.status = status;
+    da.n_slots = n_slots;
+    da.Hqk = L.Hqk;
+    da.Hv = L.Hv;
+    da.group = L.Hv / L.Hqk;
+    da.scale = L.scale;
+    da.rows = rows;
+    da.n_rows = n_rows;
+    da.qk_stride = qk_stride;
+    da.v_stride = v_stride;
+  };
+  if (L.io == GDN_BF16) {
+    DecodeArgs<bf16_bits> da;
+    fill(da, bf16_bits{});
+    return hip_status(launch_decode(da, L.D, n_req, stream));
+  }
+  DecodeArgs<float> da;
+  fill(da, float{});
+  return hip_status(launch_decode(da, L.D, n_req, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -463,15 +499,25 @@ gdn_status gdn_decode_step(const gdn_layer* layer, hipStream_t stream, int32_t n
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state_pool, 16)) return GDN_ERR_BAD_SHAPE;
   if (L.io == GDN_F32 && (!aligned(q, 16) || !aligned(k, 16))) return GDN_ERR_BAD_SHAPE;
   if (n_req > 65535) return GDN_ERR_CAPACITY;
-  if (L.io == GDN_BF16) {
-    DecodeArgs<bf16_bits> da{static_cast<const bf16_bits*>(q), static_cast<const bf16_bits*>(k),
-                             static_cast<const bf16_bits*>(v), a, b, state_pool, slot_ids, o, status, n_slots,
-                             L.Hqk, L.Hv, L.Hv / L.Hqk, L.scale};
-    return hip_status(launch_decode(da, L.D, n_req, stream));
-  }
-  DecodeArgs<float> da{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-                       a, b, state_pool, slot_ids, o, status, n_slots, L.Hqk, L.Hv, L.Hv / L.Hqk, L.scale};
-  return hip_status(launch_decode(da, L.D, n_req, stream));
+  return decode_rows(L, stream, n_req, n_req, q, k, v, (int64_t)L.Hqk * L.D, (int64_t)L.Hv * L.D, a, b,
+                     state_pool, n_slots, slot_ids, nullptr, o, status);
+}
+
+gdn_status gdn_decode_mixed(const gdn_layer* layer, hipStream_t stream, int32_t n_req, int64_t n_rows,
+                            const void* q, const void* k, const void* v, int64_t qk_stride, int64_t v_stride,
+                            const float* a, const float* b, float* state_pool, int64_t n_slots,
+                            const int32_t* slot_ids, const int32_t* rows, float* o, int32_t* status) {
+  LayerInfo L;
+  gdn_status s = check_layer(layer, &L);
+  if (s != GDN_OK) return s;
+  if (n_req < 0 || n_slots < 0 || n_rows < 0) return GDN_ERR_BAD_SHAPE;
+  if (n_req == 0) return GDN_OK;
+  if (!q || !k || !v || !a || !b || !state_pool || !slot_ids || !rows || !o) return GDN_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state_pool, 16)) return GDN_ERR_BAD_SHAPE;
+  if (qk_stride < (int64_t)L.Hqk * L.D || v_stride < (int64_t)L.Hv * L.D) return GDN_ERR_BAD_SHAPE;
+  if (n_req > 65535) return GDN_ERR_CAPACITY;
+  return decode_rows(L, stream, n_req, n_rows, q, k, v, qk_stride, v_stride, a, b, state_pool, n_slots, slot_ids,
+                     rows, o, status);
 }
 
 gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t n_req, float* state_pool,

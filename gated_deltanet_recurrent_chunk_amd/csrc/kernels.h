@@ -101,6 +101,10 @@ struct DecodeArgs {
   int32_t Hv;
   int32_t group;
   float scale;
+  const int32_t* rows;  // token row of each request (nullptr: row r)
+  int64_t n_rows;       // rows in the token arrays
+  int64_t qk_stride;    // elements per q / k row
+  int64_t v_stride;     // elements per v row
 };
 
 template <typename IO>

@@ -95,7 +95,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
   // they sweep that request's contiguous state block in address order
   const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int slot = p.slot_ids[r];
-  if (slot < -1 || slot >= p.n_slots) {
+  // the request's token row: its own index, or (a mixed batch) a row of the packed
+  // token arrays it shares with prefill sequences
+  const int64_t row = p.rows ? (int64_t)p.rows[r] : (int64_t)r;
+  if (slot < -1 || slot >= p.n_slots || (slot >= 0 && (row < 0 || row >= p.n_rows))) {
     if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
     return;
   }
@@ -114,8 +117,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
   }
   float k[8], q[8];
   {
-    const IO* kr = p.k + ((size_t)r * p.Hqk + hk) * D;
-    const IO* qr = p.q + ((size_t)r * p.Hqk + hk) * D;
+    const IO* kr = p.k + row * p.qk_stride + (int64_t)hk * D;
+    const IO* qr = p.q + row * p.qk_stride + (int64_t)hk * D;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       k[e] = to_f32(kr[j0 + e]);
@@ -124,9 +127,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
       q[4 + e] = to_f32(qr[j1 + e]);
     }
   }
-  const float a = p.a[(size_t)r * p.Hv + h];
-  const float b = p.b[(size_t)r * p.Hv + h];
-  const IO* vrow = p.v + ((size_t)r * p.Hv + h) * D;
+  const float a = p.a[row * p.Hv + h];
+  const float b = p.b[row * p.Hv + h];
+  const IO* vrow = p.v + row * p.v_stride + (int64_t)h * D;
   float vi[NP];
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) vi[pp] = to_f32(vrow[pp * RPP + rowi]);
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<IO> p) {
   for (int e = 0; e < 8; ++e) kq = fmaf(k[e], q[e], kq);
   kq = group_sum<LPR>(kq);
 
-  float* orow = p.o + ((size_t)r * p.Hv + h) * D;
+  float* orow = p.o + (row * p.Hv + h) * D;
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
     const int i = pp * RPP + rowi;

@@ -261,6 +261,22 @@ gdn_status gdn_decode_step(const gdn_layer* layer, hipStream_t stream, int32_t n
                            const float* b, float* state_pool, int64_t n_slots,
                            const int32_t* slot_ids, float* o, int32_t* status);
 
+/* The decode tokens of a mixed batch ("Hybrid linear attention (gated DeltaNet)", "The
+ * part that is easy to get wrong": in the mixed regime gdn_decode_mixed runs beside the
+ * prefill kernels).  As gdn_decode_step, but request r's token is row rows[r] of packed
+ * token arrays that the batch's prefill sequences share (their rows go to
+ * gdn_chunk_prefill, the decode rows here; the conv covers all of them as sequences):
+ *   q, k: row t at q + t * qk_stride ([n_qk_heads][d] at the row's start); v: row t at
+ *   v + t * v_stride; a, b [n_rows][n_v_heads] fp32; o [n_rows][n_v_heads][d] fp32.
+ *   rows [n_req] int32 (device).  A row outside [0, n_rows) for a request with a slot
+ *   writes nothing for it and sets GDN_ERR_CAPACITY in *status.  Slot rules as for
+ *   gdn_decode_step. */
+gdn_status gdn_decode_mixed(const gdn_layer* layer, hipStream_t stream, int32_t n_req, int64_t n_rows,
+                            const void* q, const void* k, const void* v, int64_t qk_stride,
+                            int64_t v_stride, const float* a, const float* b, float* state_pool,
+                            int64_t n_slots, const int32_t* slot_ids, const int32_t* rows, float* o,
+                            int32_t* status);
+
 /* ReplaySSM flush ("Caching less to serve more requests", section "What we changed"):
  * each request keeps one state plus a log of per-token inputs since it; the flush
  * folds the first n_accepted[r] logged rows of request r into its state as one

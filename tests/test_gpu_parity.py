@@ -345,6 +345,83 @@ def test_gated_norm_matches_oracle(g, Hv, D, dtype):
         assert rel_l2(f64(out), ref) <= 1e-5
 
 
+# ------------------------------------------------------------------------- mixed batches
+
+@pytest.mark.parametrize("Hqk,Hv,D,dtype", [(2, 4, 128, torch.bfloat16), (1, 2, 32, torch.float32)])
+def test_mixed_batch_decode_rows_and_prefill(g, Hqk, Hv, D, dtype):
+    """One packed batch: 5 decode tokens (rows 0..4, in permuted order, one padding slot)
+    and two prefill sequences behind them.  The decode tokens go to decode_mixed, the
+    prefill rows to chunk_prefill; each result against the oracle, and decode_mixed
+    bit-identical to decode_step on the same tokens gathered densely."""
+    layer = g.Layer(Hqk, Hv, D, dtype, scale=0.5)
+    n_dec, lens = 5, [130, 70]
+    T = n_dec + sum(lens)
+    say(f"mixed batch Hqk={Hqk} Hv={Hv} D={D} {dtype}")
+    q, k, v, a, b = gi.qkvab(T, Hqk, Hv, D, dtype, seed=141)
+    n_slots = 7
+    pool0 = gi.states(n_slots, Hv, D, seed=142)
+    slots = [2, 0, -1, 5, 1]
+    rows = [3, 0, 4, 1, 2]
+    qd, kd, vd, ad, bd = _dev(q, k, v, a, b)
+    pool = pool0.cuda()
+    o = torch.full((T, Hv, D), 777.0, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    i32 = lambda xs: torch.tensor(xs, dtype=torch.int32, device="cuda")
+    g.decode_mixed(layer, qd, kd, vd, ad, bd, pool, i32(slots), i32(rows), o, status=status)
+    # the prefill rows: sequence A from zero, sequence B from the state in slot 6
+    SA = torch.empty(Hv, D, D, device="cuda")
+    SB = torch.empty(Hv, D, D, device="cuda")
+    cu = [0, lens[0], lens[0] + lens[1]]
+    pre = slice(n_dec, T)
+    g.chunk_prefill(layer, qd[pre], kd[pre], vd[pre], ad[pre], bd[pre], cu, [0, 40],
+                    [("zero", None, SA), ("slot", pool[6].clone(), SB)], o[pre], ckpt=g.no_checkpoints())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    out, pl = f64(o), f64(pool)
+    for r, (s_, row) in enumerate(zip(slots, rows)):
+        if s_ < 0:
+            assert np.all(out[row] == 777.0)
+            continue
+        o_ref, S_ref, _ = oracle.recurrence(f64(q[row:row + 1]), f64(k[row:row + 1]), f64(v[row:row + 1]),
+                                            f64(a[row:row + 1]), f64(b[row:row + 1]), 0.5, f64(pool0[s_]))
+        assert rel_l2(out[row:row + 1], o_ref) <= TOL[dtype], r
+        assert rel_l2(pl[s_], S_ref) <= TOL[dtype], r
+    for s_ in (3, 4, 6):
+        assert np.array_equal(pl[s_], f64(pool0[s_]))
+    for i, (src, Sg) in enumerate(((None, SA), (f64(pool0[6]), SB))):
+        r0 = n_dec + cu[i]
+        sl_ = slice(r0, r0 + lens[i])
+        o_ref, S_ref, _ = oracle.recurrence(f64(q[sl_]), f64(k[sl_]), f64(v[sl_]), f64(a[sl_]), f64(b[sl_]), 0.5, src)
+        assert rel_l2(out[sl_], o_ref) <= TOL[dtype], i
+        assert rel_l2(f64(Sg), S_ref) <= TOL[dtype], i
+    # the same tokens, gathered densely, through decode_step: identical bits
+    pool2 = pool0.cuda()
+    idx = torch.tensor(rows, device="cuda")
+    o2 = torch.full((n_dec, Hv, D), 777.0, device="cuda")
+    g.decode_step(layer, qd[idx].contiguous(), kd[idx].contiguous(), vd[idx].contiguous(), ad[idx].contiguous(),
+                  bd[idx].contiguous(), pool2, i32(slots), o2)
+    torch.cuda.synchronize()
+    assert same_bits(pool2, pool)
+    assert same_bits(o2, o[idx])
+
+
+def test_mixed_batch_rejects_rows_outside_the_arrays(g):
+    D, H = 32, 2
+    layer = g.Layer(H, H, D, torch.bfloat16)
+    q, k, v, a, b = _dev(*gi.qkvab(4, H, H, D, torch.bfloat16, seed=151))
+    pool = gi.states(2, H, D, seed=152).cuda()
+    before = pool.clone()
+    o = torch.zeros(4, H, D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("mixed batch bad rows")
+    g.decode_mixed(layer, q, k, v, a, b, pool, torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+                   torch.tensor([4, -1], dtype=torch.int32, device="cuda"), o, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1 << 8
+    assert same_bits(pool, before)
+    assert torch.count_nonzero(o) == 0
+
+
 # ------------------------------------------------------------------------- replay outputs
 
 REPLAY_CASES = [
