@@ -16,7 +16,9 @@ Reported beside it, each timed with HIP events on the stream the kernels run on:
     rotating over enough state pools that every launch streams from HBM;
   * the replay outputs at the same layer: 16 new rows behind each request's accepted
     rows in the log, outputs of the new rows from the state and the log;
-  * the decode step for 256 requests at the 27B shape;
+  * the decode step for 256 requests at the 27B shape, and a mixed step: those 256 decode
+    tokens and the 8,192-token prefill in one packed batch (conv over all sequences,
+    prefill over its rows, the decode rows through decode_mixed);
   * the conv update alone, and the packed-core steps at the same layer: the conv with
     the per-head q/k L2 norm fused, the gates from the "ba" projection, the gated RMSNorm
     of the output rows;
@@ -291,6 +293,7 @@ def main():
     rb = replay_bytes(acc_u.tolist(), n_new)
 
     # ------------------------------------------------------------ decode (27B layer, 256 requests)
+    # (the mixed-batch step, below, needs the prefill inputs and the decode pool)
     n_dec = 256
     dpool = gi.states(n_dec, H, D, seed=1005).to(dev)
     dq, dk, dv, da, db = (t.to(dev) for t in gi.qkvab(n_dec, H, H, D, torch.bfloat16, seed=1005))
@@ -307,6 +310,43 @@ def main():
     torch.cuda.synchronize()
     decode_us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
     dec_bytes = n_dec * (2 * H * D * D * 4 + 3 * H * D * 2 + 2 * H * 4 + H * D * 4)
+
+    # ------------------------------------------------------------ mixed batch (27B layer)
+    # one packed batch: 256 decode tokens (rows 0..255) and the 8,192-token prefill behind
+    # them; the conv runs over all 257 sequences, the prefill over its rows, the decode
+    # tokens through decode_mixed
+    mT = n_dec + T
+    mx = torch.cat([gi.conv_inputs(n_dec, C, 4, torch.bfloat16, seed=1008)[0].to(dev), x])
+    my = torch.empty_like(mx)
+    mq, mk, mv = (torch.cat([d_, p_]) for d_, p_ in ((dq, q), (dk, k), (dv, v)))
+    ma, mb = torch.cat([da, a]), torch.cat([db, b])
+    mo = torch.empty(mT, H, D, dtype=torch.float32, device=dev)
+    mtails = torch.zeros(n_dec, 3, C, dtype=torch.bfloat16, device=dev)
+    m_cu = list(range(n_dec + 1)) + [n_dec + T]
+    m_sp = [100] * n_dec + [0]
+    m_refs = [("slot", mtails[i], mtails[i]) for i in range(n_dec)] + [("zero", None, tail)]
+    m_pages = list(range(n_ck))
+    mcws = torch.empty(g.conv_workspace_bytes(layer, m_cu, m_sp, BLOCK), dtype=torch.uint8, device=dev)
+    mrows = torch.arange(n_dec, dtype=torch.int32, device=dev)
+    pre = slice(n_dec, mT)
+
+    def mixed_step():
+        g.conv_update(layer, mx, w, m_refs, m_cu, m_sp, my, ckpt=pool, page_ids=m_pages, workspace=mcws)
+        g.chunk_prefill(layer, mq[pre], mk[pre], mv[pre], ma[pre], mb[pre], cu, sp, [("zero", None, S)], mo[pre],
+                        ckpt=pool, page_ids=page_ids, workspace=ws)
+        g.decode_mixed(layer, mq, mk, mv, ma, mb, dpool, dslots, mrows, mo)
+
+    def time_steps(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / args.steps
+
+    mixed_ms = time_steps(mixed_step)
 
     conv_bytes = 2 * T * C * 2
     result = {
@@ -337,6 +377,9 @@ def main():
                               "workload": "replay_4b_16req_H32_d128_32slots_logged_u1_16_new16",
                               "hbm_gbs": round(rb / (replay_us * 1e-6) / 1e9, 1),
                               "roof_us": round(rb / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
+        "mixed_step": {"ms": round(mixed_ms, 4), "prefill_tokens": T, "decode_tokens": n_dec,
+                       "tokens_per_s": round((T + n_dec) / (mixed_ms * 1e-3), 1),
+                       "workload": "27b layer: 256 decode tokens + the 8192-token prefill in one packed batch"},
         "decode_us": {"value": round(decode_us, 2), "workload": "decode_27b_256req_H48_d128",
                       "hbm_gbs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
                       "roof_us": round(dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
