@@ -462,12 +462,12 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
   __shared__ __attribute__((aligned(16))) float Ub[L::TD_IN_A ? 1 : CT][24];  // T_ii planes otherwise
 
-  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int h = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const ChunkDesc cd = uniform_chunk(p.chunks + c);
   const int n = cd.len;
   const int hk = h / p.group;
-  uint8_t* rec = p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride;
+  uint8_t* rec = p.factors + ((size_t)c * p.Hv + h) * p.factor_stride;
 
   // For d < 32 the kappa groups past a 16-wide key row are contracted: keep them zero.
   if constexpr (D < 32) {
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
   const uint32_t vec_lane = 16 * grp;  // + 64 mt: rows 16 mt + 4 grp .. + 3 of a vector plane
 
   auto rec_rsrc = [&](int c) {
-    return make_rsrc(p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
+    return make_rsrc(p.factors + ((size_t)c * p.Hv + h) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
   };
 
   // ---- operands of one chunk
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
 #pragma unroll
         for (int i = 0; i < NTI; ++i)
           KTf[j][s][i] = ld16h(rr, frag_lane, Cfg::KT_OFF + (((jt0 + j) * 2 + s) * NTI + i) * 1024);
-    egn = uniform_load(reinterpret_cast<const float*>(p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride +
+    egn = uniform_load(reinterpret_cast<const float*>(p.factors + ((size_t)c * p.Hv + h) * p.factor_stride +
                                                       Cfg::EGN_OFF));
   };
 
@@ -943,7 +943,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   //      or past the chunk's last row write zeros.
   const IO* v_pair = p.v + (int64_t)h * D + 16 * SP * sg;
   auto stage_chunk = [&](const ChunkDesc& cd, int c, lds_u8* B) {
-    const rsrc_t rr = make_rsrc(p.factors + ((size_t)h * p.n_chunks + c) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
+    const rsrc_t rr = make_rsrc(p.factors + ((size_t)c * p.Hv + h) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
     const rsrc_t rv = make_rsrc(v_pair + cd.row * p.v_stride, (uint32_t)cd.len * vsb);
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
@@ -1215,7 +1215,7 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
 template <typename IO, int D>
 static hipError_t launch_factorize_t(const FactorizeArgs<IO>& a, int n_chunks, hipStream_t st) {
   if (n_chunks == 0) return hipSuccess;
-  dim3 grid(n_chunks, a.Hv);
+  dim3 grid(a.Hv, n_chunks);
   hipLaunchKernelGGL((factorize_kernel<IO, D>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
