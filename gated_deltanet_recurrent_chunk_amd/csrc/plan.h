@@ -117,10 +117,12 @@ void plan_conv(const std::vector<SeqSpan>& spans, size_t n_pages, ConvPlan* plan
 // bytes per lane of a 64-lane wave), ntf (or nti) bf16 terms each:
 //   T = (I + A)^-1: 6 fragments x ntf (the (row tile, k-step) pairs of its lower triangle)
 //   P = scale * exp(g_t - g_s) q_t.k_s (s <= t): 6 x ntf, same pairs
-//   K^T: (d / 16) row tiles x 2 k-steps x nti
+//   K^T: (d / 16) row tiles x 2 k-steps x nti, except for bf16 inputs with d >= 64,
+//        whose scan forms K^T from the key rows it stages
 // then four fp32 row vectors of kChunk and one fp32 chunk scalar (16 bytes).
 constexpr size_t factor_record_bytes_c(int ntf, int nti, int d) {
-  return ((size_t)12 * ntf * 1024 + (size_t)(d / 16) * 2 * nti * 1024 + 4 * kChunk * 4 + 16 + kAlign - 1) /
+  const bool kt = !(nti == 1 && d >= 64);
+  return ((size_t)12 * ntf * 1024 + (kt ? (size_t)(d / 16) * 2 * nti * 1024 : 0) + 4 * kChunk * 4 + 16 + kAlign - 1) /
          kAlign * kAlign;
 }
 inline size_t factor_record_bytes(int ntf, int nti, int d) { return factor_record_bytes_c(ntf, nti, d); }

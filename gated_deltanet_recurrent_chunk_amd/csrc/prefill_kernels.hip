@@ -51,12 +51,15 @@ template <typename IO, int D>
 struct PrefillCfg {
   static constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
   static constexpr int DT = D / 16;
-  // factor record: [T'' fragments][PT'' fragments][K^T fragments][row vectors][chunk
-  // scalar], with T'' = diag(exp(g_n - g)) T diag(b) and PT'' = (scale P) T diag(b)
+  // The staged scan (bf16 inputs, d >= 64) forms its K^T operands from the key rows it
+  // stages anyway (transposing LDS reads); the register scan reads them from the record.
+  static constexpr bool HAS_KT = !(sizeof(IO) == 2 && D >= 64);
+  // factor record: [T'' fragments][PT'' fragments][K^T fragments (HAS_KT)][row vectors]
+  // [chunk scalar], with T'' = diag(exp(g_n - g)) T diag(b) and PT'' = (scale P) T diag(b)
   static constexpr int T_OFF = 0;
   static constexpr int P_OFF = kFragCombos * NTF * 1024;
   static constexpr int KT_OFF = 2 * kFragCombos * NTF * 1024;
-  static constexpr int VEC_OFF = KT_OFF + DT * 2 * NTI * 1024;
+  static constexpr int VEC_OFF = KT_OFF + (HAS_KT ? DT * 2 * NTI * 1024 : 0);
   // row vector planes (kChunk floats each): exp(g), scale exp(g)
   static constexpr int V_EG = 0, V_EGS = 1, NVEC = 2;
   static constexpr int EGN_OFF = VEC_OFF + NVEC * CT * 4;  // exp(g_n)
@@ -290,11 +293,11 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
     }
   }
 
-  // K^T fragments of state tiles jt = W, W + 4, ...: row col of tile jt is the key column
-  // the scan keeps at register position (jt, col / 4, col % 4) (kcol order); contraction
-  // over the chunk rows t = kappa(s, grp, e)
+  // K^T fragments of state tiles jt = W, W + 4, ... (register scan only): row col of
+  // tile jt is the key column the scan keeps at register position (jt, col / 4, col % 4)
+  // (kcol order); contraction over the chunk rows t = kappa(s, grp, e)
 #pragma unroll
-  for (int jt = W; jt < DT; jt += 4) {
+  for (int jt = W; jt < (Cfg::HAS_KT ? DT : 0); jt += 4) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -852,7 +855,8 @@ __device__ __forceinline__ void dma16(rsrc_t r, lds_u8* lds, uint32_t voff) {
 // assignment is a constant.
 template <typename IO, int D, int Q>
 __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const int u, const int sg, lds_u8* stage0,
-                                                 lds_u8* stage1, lds_u8* kqs, f32x4* xch) {
+                                                 lds_u8* stage1, lds_u8* kbuf0, lds_u8* kbuf1, lds_u8* qbuf,
+                                                 f32x4* xch) {
   using Cfg = PrefillCfg<IO, D>;
   using Shp = ScanStaged<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
@@ -870,13 +874,15 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   constexpr int GPW = (G + NW - 1) / NW;  // copies per wave; granules past G are padding
   constexpr int BUF = GPW * NW * 1024;
   constexpr int XCH = NSP == 2 ? SP * NSP * 6 * 64 : 1;  // f32x4 exchange slots
-  // key and query rows of a chunk (one buffer, refilled once every wave has read
-  // them): rows of RB bytes whose 16-byte pieces are permuted by an XOR with the row
-  // index, so that the 16 rows of one operand read land in distinct banks
+  // key rows of a chunk (two buffers, alternating: a chunk's keys serve its state update
+  // at the end of the chunk, after the next chunk's keys are requested) and query rows
+  // (one buffer, refilled once every wave has read them): rows of RB bytes whose 16-byte
+  // pieces are permuted by an XOR with the row index, so that the 16 rows of one operand
+  // read land in distinct banks
   constexpr int RB = D * ESZ, PPR = RB / 16, RPG = 1024 / RB, KQG = 64 / RPG, KQPW = 2 * KQG / NW;
   static_assert(KSH * NSP == KSD && DTH * NSP == DT && (VNP == 4 || VNP == 8) && VG * 1024 == 64 * VRB, "shape");
   static_assert(RPG * RB == 1024 && KQPW * NW == 2 * KQG, "key/query staging");
-  static_assert(2 * BUF + 16 * XCH + 2 * 64 * RB <= 160 * 1024, "LDS budget");
+  static_assert(2 * BUF + 16 * XCH + 3 * 64 * RB <= 160 * 1024, "LDS budget");
   const int seq = u / p.Hv, h = u - seq * p.Hv;
   const int hk = h / p.group;
   constexpr int q = Q, jj = Q / NSP, w = Q % NSP;  // slab within the pair, key half
@@ -956,8 +962,9 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     }
   };
 
-  // copies of the chunk's key and query rows: KQPW granules per wave, same on every path
-  auto stage_kq = [&](const ChunkDesc& cd) {
+  // copies of the chunk's key rows (into Kd) and query rows: KQPW granules per wave,
+  // same on every path
+  auto stage_kq = [&](const ChunkDesc& cd, lds_u8* Kd) {
     const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
     const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
 #pragma unroll
@@ -965,19 +972,42 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       const int g = q + gi * NW;  // wave-uniform: granules 0 .. KQG-1 keys, then queries
       const uint32_t r = RPG * (uint32_t)(g % KQG) + (uint32_t)lane / PPR;
       const uint32_t lp = ((uint32_t)lane % PPR) ^ (r % PPR);
-      dma16(g >= KQG ? rq : rk, kqs + 1024 * g, r * qsb + 16u * lp);
+      if (g < KQG)
+        dma16(rk, Kd + 1024 * g, r * qsb + 16u * lp);
+      else
+        dma16(rq, qbuf + 1024 * (g - KQG), r * qsb + 16u * lp);
     }
   };
   // this wave's A operands of X and Y: row 16 mt + col, key columns 32 (s0 + s) + 8 grp ..
   RowOp<IO> Kop[4][KSH], Qop[4][KSH];
-  auto read_kq = [&](int s) {  // k-step s0 + s
+  auto read_kq = [&](const lds_u8* Kb, int s) {  // k-step s0 + s
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int r = 16 * mt + col;
       const int off = r * RB + 16 * ((grp + 4 * (s0 + s)) ^ (r % PPR));
-      Kop[mt][s].v = lds_load<bf16x8>(kqs + off);
-      Qop[mt][s].v = lds_load<bf16x8>(kqs + 64 * RB + off);
+      Kop[mt][s].v = lds_load<bf16x8>(Kb + off);
+      Qop[mt][s].v = lds_load<bf16x8>(qbuf + off);
     }
+  };
+  // A operands of K^T for the state update (state tile jt0 + j, k-step s over the chunk
+  // rows), read transposed from the staged key rows.  In each 16-lane group of a
+  // transposing 64-bit read, lane i receives, as its element e, the 16-bit value at the
+  // address of lane 4 e + i / 4 plus i % 4 elements.  Lane L = 16 g + 4 e + c thus names
+  // row t = 32 s + 16 h + 4 g + e (half h = 0, 1 of the eight kappa elements) at the four
+  // key columns kcol(jt, c) .. + 3, and lane (col, g) receives K[t][key of its row col].
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  auto read_kt = [&](const lds_u8* Kb, int j, int s) {
+    const int jt = jt0 + j;
+    const int pc = 4 * (jt >> 1) + (lane & 3), half8 = 8 * (jt & 1);  // 16-byte piece, 8-byte half
+    u32x2 w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 32 * s + 16 * h + 4 * grp + ((lane >> 2) & 3);
+      const lds_u8* a = Kb + t * RB + 16 * (pc ^ (t % PPR)) + half8;
+      w[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                           (__attribute__((address_space(3))) v4s*)a));
+    }
+    return __builtin_bit_cast(bf16x8, u32x4{w[0][0], w[0][1], w[1][0], w[1][1]});
   };
   auto frag = [&](const lds_u8* B, int off, int f) {
     return lds_load<bf16x8>(B + off + 1024 * f + 16 * lane);
@@ -990,12 +1020,12 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   ChunkDesc cur = to_desc(chunk_raw(cb));
   u32x4 nxt_raw = chunk_raw(cb + 1 < ce ? cb + 1 : cb);
   stage_chunk(cur, cb, stage0);
-  stage_kq(cur);
+  stage_kq(cur, kbuf0);
 
-  auto step = [&](const int c, const lds_u8* Bc, lds_u8* Bn) {
+  auto step = [&](const int c, const lds_u8* Bc, lds_u8* Bn, const lds_u8* Kc, lds_u8* Kn) {
     const bool more = c + 1 < ce;
     const ChunkDesc nxt = to_desc(nxt_raw);
-    // Every wave's copies of this chunk (into Bc and kqs) have landed once each wave has
+    // Every wave's copies of this chunk (into Bc, Kc and the query buffer) have landed once each wave has
     // waited for all of its own vector memory operations and passed the barrier.  The
     // wait is explicit: the compiler's own count of outstanding LDS DMA follows the
     // data a wave reads itself, not the copies its partners read.  The copies were
@@ -1006,7 +1036,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     stage_chunk(nxt, more ? c + 1 : c, Bn);
     nxt_raw = chunk_raw(c + 2 < ce ? c + 2 : c + 1 - (more ? 0 : 1));
 
-    read_kq(0);
+    read_kq(Kc, 0);
     issue_point();
 
     // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains;
@@ -1016,7 +1046,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     for (int mt = 0; mt < 4; ++mt) X[mt] = Y[mt] = zero4();
 #pragma unroll
     for (int s = 0; s < KSH; ++s) {
-      if (s + 1 < KSH) read_kq(s + 1);
+      if (s + 1 < KSH) read_kq(Kc, s + 1);
       issue_point();
       bf16x8 sop[NTF];
       reg_operand<NTF>(S[2 * s], (2 * s + 1 < DTH) ? S[2 * s + 1] : zero4(), sop);
@@ -1060,7 +1090,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       lds_barrier();
       // every wave has read this chunk's key and query rows: copy the next chunk's
       // (the last chunk copies its own again, so that every path issues the same copies)
-      stage_kq(more ? nxt : cur);
+      stage_kq(more ? nxt : cur, Kn);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 xo = other[mt * 64];
@@ -1080,7 +1110,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       lds_barrier();
       // every wave has read this chunk's key and query rows: copy the next chunk's (the
       // last chunk copies its own again, so that every path issues the same copies)
-      stage_kq(more ? nxt : cur);
+      stage_kq(more ? nxt : cur, Kn);
     }
 
     // ---- B: R' = V - exp(g) X, Dt = T'' R' over the nonzero k-steps
@@ -1137,9 +1167,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
 #pragma unroll
     for (int j = 0; j < DTH; ++j)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int i = 0; i < NTI; ++i) KTf[j][s][i] = frag(Bc, Cfg::KT_OFF, ((jt0 + j) * 2 + s) * NTI + i);
+      for (int s = 0; s < 2; ++s) KTf[j][s][0] = read_kt(Kc, j, s);
     const float egn = lds_load<float>(Bc + Cfg::EGN_OFF);
     issue_point();
 
@@ -1168,8 +1196,8 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   // two steps per trip, so that each step's buffers are fixed LDS objects
 #pragma unroll 1
   for (int c = cb; c < ce; c += 2) {
-    step(c, stage0, stage1);
-    if (c + 1 < ce) step(c + 1, stage1, stage0);
+    step(c, stage0, stage1, kbuf0, kbuf1);
+    if (c + 1 < ce) step(c + 1, stage1, stage0, kbuf1, kbuf0);
   }
   store_state(sq.dst + head_off + (size_t)my_row * D);
 }
@@ -1183,7 +1211,7 @@ struct StagedLds {
   static constexpr int G = RG + 64 * Shp::SP * 16 * (int)sizeof(IO) / 1024;
   static constexpr int BUF = (G + Shp::NW - 1) / Shp::NW * Shp::NW * 1024;
   static constexpr int XCH = Shp::NSP == 2 ? Shp::SP * Shp::NSP * 6 * 64 : 1;
-  static constexpr int KQ = 2 * 64 * D * (int)sizeof(IO);
+  static constexpr int KR = 64 * D * (int)sizeof(IO);  // one chunk's key (or query) rows
 };
 
 template <typename IO, int D>
@@ -1192,7 +1220,12 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   constexpr int NG = ScanStaged<IO, D>::NG;
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[L::BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[L::BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t kqs[L::KQ];
+  // two key buffers and the query buffer as separate objects: the compiler tracks
+  // outstanding LDS DMA per object, and a chunk's keys are read after the next chunk's
+  // keys and queries are requested
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::KR];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::KR];
+  __shared__ __attribute__((aligned(1024))) uint8_t qbuf[L::KR];
   // [slab][wave][X tiles 0..3, partner's Y tiles][lane]
   __shared__ __attribute__((aligned(16))) f32x4 xch[L::XCH];
 
@@ -1203,10 +1236,14 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   const int sg = (blk >> 3) % NG;
   if (u >= p.n_seqs * p.Hv) return;
   switch (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))) {
-    case 0: scan_staged_wave<IO, D, 0>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
-    case 1: scan_staged_wave<IO, D, 1>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
-    case 2: scan_staged_wave<IO, D, 2>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
-    default: scan_staged_wave<IO, D, 3>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kqs, xch); break;
+    case 0: scan_staged_wave<IO, D, 0>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
+    case 1: scan_staged_wave<IO, D, 1>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
+    case 2: scan_staged_wave<IO, D, 2>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
+    default: scan_staged_wave<IO, D, 3>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
   }
 }
 
