@@ -871,7 +871,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   constexpr int RG = (Cfg::REC_BYTES + 1023) / 1024;
   constexpr int VRB = SP * 16 * ESZ, VNP = VRB / 16, VG = 64 * VRB / 1024;
   constexpr int V_OFF = RG * 1024, G = RG + VG;
-  constexpr int GPW = (G + NW - 1) / NW;  // copies per wave; granules past G are padding
+  constexpr int GPW = (G + NW - 1) / NW;  // copies per wave at most
   constexpr int BUF = GPW * NW * 1024;
   constexpr int XCH = NSP == 2 ? SP * NSP * 6 * 64 : 1;  // f32x4 exchange slots
   // key rows of a chunk (two buffers, alternating: a chunk's keys serve its state update
@@ -942,19 +942,20 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     return d;
   };
 
-  // ---- copies of chunk c into buffer B: 1 KiB granules g = q, q + NW, ...  Every wave
-  //      issues the same GPW copies on every path (padding granules read past the
-  //      record's end), so the compiler's counts of outstanding loads stay exact.  The
-  //      bounds of both descriptors are in the per-lane offset: lanes past the record
-  //      or past the chunk's last row write zeros.
+  // ---- copies of chunk c into buffer B: 1 KiB granules g = q, q + NW, ... < G.  A wave
+  //      issues the same copies on every path (the last chunk stages itself again), so
+  //      the compiler's counts of outstanding loads stay exact.  The bounds of both
+  //      descriptors are in the per-lane offset: lanes past the record or past the
+  //      chunk's last row write zeros.
   const IO* v_pair = p.v + (int64_t)h * D + 16 * SP * sg;
   auto stage_chunk = [&](const ChunkDesc& cd, int c, lds_u8* B) {
     const rsrc_t rr = make_rsrc(p.factors + ((size_t)c * p.Hv + h) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
     const rsrc_t rv = make_rsrc(v_pair + cd.row * p.v_stride, (uint32_t)cd.len * vsb);
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
-      const int g = q + gi * NW;  // wave-uniform
-      const bool is_v = g >= RG && g < G;
+      const int g = q + gi * NW;  // a constant of this wave
+      if (g >= G) continue;
+      const bool is_v = g >= RG;
       const uint32_t t = (64u / VNP) * (uint32_t)(g - RG) + (uint32_t)lane / VNP;
       const uint32_t lp = ((uint32_t)lane % VNP) ^ ((t >> 2) & (VNP - 1));
       const uint32_t voff = g < RG ? 1024u * g + 16u * lane : is_v ? t * vsb + 16u * lp : (uint32_t)Cfg::REC_BYTES;
