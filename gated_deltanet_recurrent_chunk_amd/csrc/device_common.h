@@ -116,21 +116,29 @@ __device__ __forceinline__ bf16x8 lds_operand(const bf16_bits* p0, const bf16_bi
 
 // Operand terms from fp32 register values laid out as the C tiles 2s and 2s+1:
 // v0 = tile 2s rows 0..3, v1 = tile 2s+1 rows 0..3 (pass zeros for a missing tile).
+// Elements are split two at a time: one packed conversion gives a pair's term, whose
+// two halves widen back to fp32 by a shift and a mask (the same values split_terms
+// forms one element at a time).
 template <int NT>
 __device__ __forceinline__ void reg_operand(const f32x4& v0, const f32x4& v1, bf16x8 (&out)[NT]) {
-  bf16_bits t[8][NT];
+  typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+  const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  uint32_t w[NT][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    split_terms<NT>(v0[r], t[r]);
-    split_terms<NT>(v1[r], t[4 + r]);
+  for (int k = 0; k < 4; ++k) {
+    float a = x[2 * k], b = x[2 * k + 1];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const uint32_t pr = pack_bf16x2(a, b);  // element 2k in the low half
+      w[i][k] = pr;
+      if (i + 1 < NT) {
+        a = a - __uint_as_float(pr << 16);
+        b = b - __uint_as_float(pr & 0xFFFF0000u);
+      }
+    }
   }
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    bf16_bits p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = t[e][i];
-    out[i] = pack8(p);
-  }
+  for (int i = 0; i < NT; ++i) out[i] = __builtin_bit_cast(bf16x8, u32x4_t{w[i][0], w[i][1], w[i][2], w[i][3]});
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
