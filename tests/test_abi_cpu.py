@@ -153,6 +153,41 @@ def test_flush_and_decode_validation_errors():
                 pool, ids, torch.zeros(2, 2, 32), stream=0) == "GDN_ERR_BAD_SHAPE"
 
 
+def test_replay_gates_norm_and_mixed_validation_errors():
+    layer = g.Layer(2, 2, 32)
+    pool = torch.zeros(2, 2, 32, 32)
+    ids = torch.zeros(2, dtype=torch.int32)
+    buf = torch.zeros(2, 65, 2, 32, dtype=torch.bfloat16)
+    ab = torch.zeros(2, 65, 2)
+    qn = torch.zeros(2, 4, 2, 32, dtype=torch.bfloat16)
+    o = torch.zeros(2, 4, 2, 32)
+    # a log longer than 64 rows
+    assert _err(g.replay_forward, layer, pool, ids, buf, buf, ab, ab, ids, ids, qn, o, stream=0) == "GDN_ERR_CAPACITY"
+    # fp32 inputs with d = 128
+    l32 = g.Layer(2, 2, 128, torch.float32)
+    assert _err(g.replay_forward, l32, torch.zeros(2, 2, 128, 128), ids, torch.zeros(2, 32, 2, 128),
+                torch.zeros(2, 32, 2, 128), torch.zeros(2, 32, 2), torch.zeros(2, 32, 2), ids, ids,
+                torch.zeros(2, 4, 2, 128), torch.zeros(2, 4, 2, 128), stream=0) == "GDN_ERR_BAD_SHAPE"
+    # an unknown flag in the activation field
+    bad = g.Layer(2, 2, 32, conv_act=0x200)
+    ba = torch.zeros(5, 4, dtype=torch.bfloat16)
+    A_log = torch.zeros(2)
+    dt = torch.zeros(2, dtype=torch.bfloat16)
+    gates_out = torch.zeros(5, 2)
+    assert _err(g.gates, bad, ba, A_log, dt, gates_out, gates_out, stream=0) == "GDN_ERR_BAD_DTYPE"
+    # gate rows not a multiple of 8 elements apart, and a negative epsilon
+    zr = torch.zeros(5, 2 * 32 + 4, dtype=torch.bfloat16)
+    w = torch.zeros(32, dtype=torch.bfloat16)
+    out = torch.zeros(5, 2, 32, dtype=torch.bfloat16)
+    assert _err(g.gated_norm, layer, torch.zeros(5, 2, 32), zr, w, out, stream=0) == "GDN_ERR_BAD_SHAPE"
+    zz = torch.zeros(5, 2, 32, dtype=torch.bfloat16)
+    assert _err(g.gated_norm, layer, torch.zeros(5, 2, 32), zz, w, out, eps=-1.0, stream=0) == "GDN_ERR_BAD_SHAPE"
+    # token rows closer than one row of heads
+    q = torch.zeros(4, 2, 32, dtype=torch.bfloat16)
+    assert _err(g.decode_mixed, layer, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2), pool, ids, ids,
+                torch.zeros(4, 2, 32), stream=0, qk_stride=16) == "GDN_ERR_BAD_SHAPE"
+
+
 def test_conv_validation_errors():
     layer = g.Layer(1, 1, 16, torch.bfloat16)
     C = layer.conv_channels
