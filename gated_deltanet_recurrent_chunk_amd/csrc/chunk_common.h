@@ -118,6 +118,15 @@ __device__ __forceinline__ void transpose_keys(const bf16_bits* Ks, int KP, bf16
   }
 }
 
+// Barrier among the waves of a workgroup that orders LDS traffic only (outstanding
+// global loads, stores and LDS DMA are not waited for).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Barrier that also completes this wave's outstanding vector memory operations (LDS DMA
+// included) before any wave passes it.
+__device__ __forceinline__ void full_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ----------------------------------------------------------------------------------
 // Chunk factorization shared by the prefill pre-pass and the replay flush.  One wave.
 //   Ks: NTI swizzled planes (row stride KP) of the chunk's key rows (rows >= n zero).
@@ -148,7 +157,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
     vec_out[2 * CT + lane] = bb;
     vec_out[3 * CT + lane] = edec;
   }
-  __syncthreads();
+  lds_barrier();
 
   // A = strict lower part of diag(b) exp(g_t - g_s) K K^T
 #pragma unroll
@@ -176,7 +185,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Forward substitution, lane j owns column j:  T[t][j] = [t == j] - sum_{s<t} A[t][s] T[s][j].
   // The sum runs as four interleaved partial sums (s mod 4) added in a fixed order.  Row
@@ -323,14 +332,6 @@ __device__ __forceinline__ float uniform_load(const float* p) {
 // it, which bounds how many operands the scheduler keeps live in registers.
 __device__ __forceinline__ void phase_fence() { asm volatile("" ::: "memory"); }
 
-// Barrier among the waves of a workgroup that orders LDS traffic only (outstanding
-// global loads, stores and LDS DMA are not waited for).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Barrier that also completes this wave's outstanding vector memory operations (LDS DMA
-// included) before any wave passes it.
-__device__ __forceinline__ void full_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 }  // namespace chunk
 }  // namespace gdn

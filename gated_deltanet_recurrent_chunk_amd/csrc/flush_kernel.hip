@@ -20,7 +20,8 @@ using namespace chunk;
 // ==================================================================================
 // Replay flush: one workgroup per (request, value head), one wave per 16-row slab of
 // the state.  Reads the state once, factorizes the accepted rows (wave 0), applies
-// them, writes the state once.
+// them, writes the state once.  The barriers order LDS only, so the state loads stay
+// in flight through the staging of the rows and the factorization.
 template <typename IO, int D, int CT>
 __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
   constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
@@ -55,26 +56,37 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
   const int hk = h / p.group;
   const int my_row = wave * 16 + col;
   float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
+  if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), tid, NTH);
+
+  // logged rows 0..n-1 of this slot, then the state: loads complete in issue order, so
+  // waiting for the rows (to stage them) leaves the state loads in flight until the
+  // products need them, past the factorization
+  constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + NTH - 1) / NTH;
+  const size_t row0 = (size_t)slot * p.buf_rows;
+  const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
+  const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
+  uint4 kv[PER_THR], vv[PER_THR];
+#pragma unroll
+  for (int i = 0; i < PER_THR; ++i) {
+    const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    kv[i] = load16(kb + (size_t)t * p.Hqk * D + j0, idx < PIECES && t < n);
+    vv[i] = load16(vb + (size_t)t * p.Hv * D + j0, idx < PIECES && t < n);
+  }
   f32x4 S[DT];
 #pragma unroll
   for (int jt = 0; jt < DT; ++jt)
     S[jt] = *reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp);
-
-  if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), tid, NTH);
-  __syncthreads();
-  // logged rows 0..n-1 of this slot
-  const size_t row0 = (size_t)slot * p.buf_rows;
-  const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
-  const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
-  for (int idx = tid; idx < CT * PER_ROW; idx += NTH) {
-    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    uint4 kv = load16(kb + (size_t)t * p.Hqk * D + j0, t < n);
-    store_row_terms<IO, NTI>(kv, Ks, CT * KP, KP, t, j0);
-    uint4 vv = load16(vb + (size_t)t * p.Hv * D + j0, t < n);
+  lds_barrier();  // the zero fill (d < 32) precedes the row stores
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv, e);
+  for (int i = 0; i < PER_THR; ++i) {
+    const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    if (idx < PIECES) {
+      store_row_terms<IO, NTI>(kv[i], Ks, CT * KP, KP, t, j0);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv[i], e);
+    }
   }
-  __syncthreads();
+  lds_barrier();
   transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
   if (wave == 0) {
     float la = 0.f, bb = 0.f;
@@ -87,10 +99,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
     factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, n, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
   } else {
     // match the barriers inside factorize_chunk
-    __syncthreads();
-    __syncthreads();
+    lds_barrier();
+    lds_barrier();
   }
-  __syncthreads();
+  lds_barrier();
 
   bf16x8 Sop[KSD][NTF];
 #pragma unroll
@@ -200,32 +212,44 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   const int hk = h / p.group;
   const int my_row = wave * 16 + col;
   const float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
-  f32x4 S[DT];
-#pragma unroll
-  for (int jt = 0; jt < DT; ++jt)
-    S[jt] = *reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp);
-
   if constexpr (D < 32) {
     zero_lds(Ks, sizeof(Ks), tid, NTH);
     zero_lds(Qs, sizeof(Qs), tid, NTH);
   }
-  __syncthreads();
-  // log rows 0 .. L-1 of this slot (keys, values), and the queries of the new rows
+
+  // log rows 0 .. L-1 of this slot (keys, values) and the queries of the new rows, then
+  // the state, whose loads stay in flight while the rows are staged and factorized
+  // (loads complete in issue order)
+  constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + NTH - 1) / NTH;
   const size_t row0 = (size_t)slot * p.buf_rows;
   const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
   const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
   const IO* qb = p.q_new + (size_t)r_ * p.max_new * p.Hqk * D + (size_t)hk * D;
-  for (int idx = tid; idx < CT * PER_ROW; idx += NTH) {
-    const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    uint4 kv = load16(kb + (size_t)t * p.Hqk * D + j0, t < L);
-    store_row_terms<IO, NTI>(kv, Ks, CT * KP, KP, t, j0);
-    uint4 qv = load16(qb + (size_t)(t >= m ? t - m : 0) * p.Hqk * D + j0, t >= m && t < L);
-    store_row_terms<IO, NTI>(qv, Qs, CT * KP, KP, t, j0);
-    uint4 vv = load16(vb + (size_t)t * p.Hv * D + j0, t < L);
+  uint4 kv[PER_THR], qv[PER_THR], vv[PER_THR];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv, e);
+  for (int i = 0; i < PER_THR; ++i) {
+    const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    const bool in = idx < PIECES;
+    kv[i] = load16(kb + (size_t)t * p.Hqk * D + j0, in && t < L);
+    qv[i] = load16(qb + (size_t)(t >= m ? t - m : 0) * p.Hqk * D + j0, in && t >= m && t < L);
+    vv[i] = load16(vb + (size_t)t * p.Hv * D + j0, in && t < L);
   }
-  __syncthreads();
+  f32x4 S[DT];
+#pragma unroll
+  for (int jt = 0; jt < DT; ++jt)
+    S[jt] = *reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp);
+  lds_barrier();  // the zero fills (d < 32) precede the row stores
+#pragma unroll
+  for (int i = 0; i < PER_THR; ++i) {
+    const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+    if (idx < PIECES) {
+      store_row_terms<IO, NTI>(kv[i], Ks, CT * KP, KP, t, j0);
+      store_row_terms<IO, NTI>(qv[i], Qs, CT * KP, KP, t, j0);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv[i], e);
+    }
+  }
+  lds_barrier();
   if (wave == 0) {
     float la = 0.f, bb = 0.f;
     if (lane < L) {
@@ -237,10 +261,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
     factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
   } else {
     // match the barriers inside factorize_chunk
-    __syncthreads();
-    __syncthreads();
+    lds_barrier();
+    lds_barrier();
   }
-  __syncthreads();
+  lds_barrier();
 
   // P tiles, dealt round robin to the waves, as NTF bf16 term planes (row t, column s)
   for (int ti = wave; ti < NPT; ti += NW) {
@@ -269,7 +293,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
       for (int q = 0; q < NTF; ++q) Ps[q * CT * TP + t * TP + swz(sc)] = tt[q];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // X = K S_0^T and Y = Q S_0^T for this wave's slab
   bf16x8 Sop[KSD][NTF];
