@@ -143,6 +143,18 @@ __device__ __forceinline__ void reg_operand(const f32x4& v0, const f32x4& v1, bf
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// 16-byte store written through to device-coherent memory (sc1): the lines do not sit
+// dirty in the L2 of one XCD until the end-of-kernel write-back, so for a state written
+// once and read by a later launch the write traffic overlaps the rest of the kernel.
+// No builtin sets the scope bits of a 16-byte store (atomic stores stop at 8 bytes, and
+// two 8-byte halves of each 16-byte piece leave every write partial), hence the asm.
+// The compiler checks no hazards for the instructions inside an asm statement: the
+// leading 24 wait states cover a read of a matrix-core result (19 for the longest
+// 16-pass instructions); its write-after-read check on the data registers does hold.
+__device__ __forceinline__ void store16_through(float* p, const f32x4& v) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tglobal_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
 // f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{}).
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {

@@ -22,8 +22,14 @@ using namespace chunk;
 // the state.  Reads the state once, factorizes the accepted rows (wave 0), applies
 // them, writes the state once.  The barriers order LDS only, so the state loads stay
 // in flight through the staging of the rows and the factorization.
+//
+// flush_tile applies n <= CT rows; the kernel's LDS is sized for its largest tile and
+// a workgroup takes the smallest tile (16, 32 or 64 rows) that holds its request's
+// rows, so a short log pays neither the substitution nor the products of a long one.
 template <typename IO, int D, int CT>
-__global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
+__device__ __forceinline__ void flush_tile(const FlushArgs<IO>& p, int h, int slot, int n, bf16_bits* Ks,
+                                           bf16_bits* KTs, float* Vs, float* As_, bf16_bits* Ts, float* vec,
+                                           float* vec_tmp) {
   constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
   constexpr int NW = D / 16, NTH = 64 * NW;
   constexpr int KP = row_stride(D), TP = row_stride(CT), VP = D + 4;
@@ -31,38 +37,33 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
   constexpr int MT = CT / 16, KST = (MT + 1) / 2;
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int PER_ROW = D / VEC;
-
-  __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
-  __shared__ __attribute__((aligned(16))) bf16_bits KTs[NTI * D * TP];
-  __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
-  __shared__ float As[CT][CT + 4];
-  __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
-  __shared__ __attribute__((aligned(16))) float vec[4 * CT];
-  __shared__ float vec_tmp[2 * CT];
-
-  // head-major grid: consecutive workgroups take consecutive heads of one request, so
-  // they sweep that request's contiguous state block in address order
-  const int h = blockIdx.x, r_ = blockIdx.y;
+  float (*As)[CT + 4] = reinterpret_cast<float (*)[CT + 4]>(As_);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
-  const int slot = p.slot_ids[r_];
-  const int n = p.n_accepted[r_];
-  if (slot < -1 || slot >= p.n_slots || n < 0 || n > p.buf_rows) {
-    if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
-    return;
-  }
-  if (slot < 0 || n == 0) return;  // padding or nothing accepted: untouched
 
   const int hk = h / p.group;
   const int my_row = wave * 16 + col;
   float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
-  if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), tid, NTH);
+  if constexpr (D < 32) zero_lds(Ks, NTI * CT * KP * sizeof(bf16_bits), tid, NTH);
+  if constexpr (CT < 32) {
+    // the operands' contraction runs over 32 columns: the 16 columns past a 16-row tile
+    // must read as zeros (their partners in the products are zero)
+    zero_lds(KTs, NTI * D * TP * sizeof(bf16_bits), tid, NTH);
+    zero_lds(Ts, NTF * CT * TP * sizeof(bf16_bits), tid, NTH);
+  }
 
   // logged rows 0..n-1 of this slot, then the state: loads complete in issue order, so
   // waiting for the rows (to stage them) leaves the state loads in flight until the
   // products need them, past the factorization
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + NTH - 1) / NTH;
   const size_t row0 = (size_t)slot * p.buf_rows;
+  // the rows' gates (wave 0) go first: the factorization waits for them
+  float a_row = 0.f, bb = 0.f;
+  if (wave == 0 && lane < n) {
+    const size_t ai = (row0 + lane) * p.Hv + h;
+    a_row = p.buf_a[ai];
+    bb = p.buf_b[ai];
+  }
   const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
   const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
   uint4 kv[PER_THR], vv[PER_THR];
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
   f32x4 S[DT];
 #pragma unroll
   for (int jt = 0; jt < DT; ++jt)
-    S[jt] = *reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp);
+    S[jt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp));
   lds_barrier();  // the zero fill (d < 32) precedes the row stores
 #pragma unroll
   for (int i = 0; i < PER_THR; ++i) {
@@ -89,13 +90,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
   lds_barrier();
   transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
   if (wave == 0) {
-    float la = 0.f, bb = 0.f;
-    if (lane < n) {
-      const size_t ai = (row0 + lane) * p.Hv + h;
-      la = __logf(p.buf_a[ai]);
-      bb = p.buf_b[ai];
-    }
-    const float g = wave_inclusive_scan(la);
+    const float g = wave_inclusive_scan(lane < n ? __logf(a_row) : 0.f);
     factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, n, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
   } else {
     // match the barriers inside factorize_chunk
@@ -161,8 +156,43 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
       op_terms<NTI>(KTs, D * TP, TP, 16 * jt + col, s, grp, a);
       mma_terms<NTI, NTF, ORD>(acc, a, Dtop[s]);
     }
-    *reinterpret_cast<f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp) = acc;
+    store16_through(state + (size_t)my_row * D + 16 * jt + 4 * grp, acc);
   }
+}
+
+template <typename IO, int D, int CT>
+__global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
+  constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF;
+  constexpr int KP = row_stride(D), TP = row_stride(CT), VP = D + 4;
+
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
+  __shared__ __attribute__((aligned(16))) bf16_bits KTs[NTI * D * TP];
+  __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
+  __shared__ __attribute__((aligned(16))) float As[CT * (CT + 4)];
+  __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
+  __shared__ __attribute__((aligned(16))) float vec[4 * CT];
+  __shared__ float vec_tmp[2 * CT];
+
+  // head-major grid: consecutive workgroups take consecutive heads of one request, so
+  // they sweep that request's contiguous state block in address order
+  const int h = blockIdx.x, r_ = blockIdx.y;
+  // both words are fetched before either is tested (one round trip, not two)
+  int slot = p.slot_ids[r_];
+  int n = p.n_accepted[r_];
+  asm volatile("" : "+s"(slot), "+s"(n));
+  const bool bad = (slot < -1) | (slot >= p.n_slots) | (n < 0) | (n > p.buf_rows);
+  if (bad) {
+    if (threadIdx.x == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
+    return;
+  }
+  if (slot < 0 || n == 0) return;  // padding or nothing accepted: untouched
+  if constexpr (CT > 16) {
+    if (n <= 16) return flush_tile<IO, D, 16>(p, h, slot, n, Ks, KTs, Vs, As, Ts, vec, vec_tmp);
+  }
+  if constexpr (CT > 32) {
+    if (n <= 32) return flush_tile<IO, D, 32>(p, h, slot, n, Ks, KTs, Vs, As, Ts, vec, vec_tmp);
+  }
+  flush_tile<IO, D, CT>(p, h, slot, n, Ks, KTs, Vs, As, Ts, vec, vec_tmp);
 }
 
 // ==================================================================================
@@ -200,9 +230,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   const int h = blockIdx.x, r_ = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
-  const int slot = p.slot_ids[r_];
-  const int m = p.n_logged[r_], n = p.n_new[r_];
-  if (slot < -1 || slot >= p.n_slots || m < 0 || n < 0 || m + n > p.buf_rows || n > p.max_new) {
+  // the three words are fetched before any is tested (one round trip)
+  int slot = p.slot_ids[r_];
+  int m = p.n_logged[r_], n = p.n_new[r_];
+  asm volatile("" : "+s"(slot), "+s"(m), "+s"(n));
+  const bool bad = (slot < -1) | (slot >= p.n_slots) | (m < 0) | (n < 0) | (m + n > p.buf_rows) | (n > p.max_new);
+  if (bad) {
     if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
     return;
   }
@@ -222,6 +255,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   // (loads complete in issue order)
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + NTH - 1) / NTH;
   const size_t row0 = (size_t)slot * p.buf_rows;
+  // the rows' gates (wave 0) go first: the factorization waits for them
+  float a_row = 0.f, bb = 0.f;
+  if (wave == 0 && lane < L) {
+    const size_t ai = (row0 + lane) * p.Hv + h;
+    a_row = p.buf_a[ai];
+    bb = p.buf_b[ai];
+  }
   const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
   const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
   const IO* qb = p.q_new + (size_t)r_ * p.max_new * p.Hqk * D + (size_t)hk * D;
@@ -251,13 +291,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   }
   lds_barrier();
   if (wave == 0) {
-    float la = 0.f, bb = 0.f;
-    if (lane < L) {
-      const size_t ai = (row0 + lane) * p.Hv + h;
-      la = __logf(p.buf_a[ai]);
-      bb = p.buf_b[ai];
-    }
-    const float g = wave_inclusive_scan(la);
+    const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
     factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
   } else {
     // match the barriers inside factorize_chunk
