@@ -135,13 +135,21 @@ __device__ __forceinline__ void full_barrier() {
 // tps) and the four per-row vectors g, exp(g), b, exp(g_n - g) into vec_out.
 // FOLD: writes T'' = diag(exp(g_n - g)) T diag(b) to Tout instead, and T^T (unscaled,
 // row j = column j of T) to Ttr in the same plane format.
-template <int CT, int D, int NTI, int NTF, int ORD, bool FOLD = false>
+// SPLIT (32-row chunks, no FOLD): the substitution runs on both halves of the wave, see
+// below; it holds half the registers of the one-half form.
+template <int CT, int D, int NTI, int NTF, int ORD, bool FOLD = false, bool SPLIT = false>
 __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n,
                                                 float g, float bb, bf16_bits* Tout, int tps, int tld,
                                                 float* vec_out, float* vec_lds, bf16_bits* Ttr = nullptr) {
   constexpr int KP = row_stride(D);
   constexpr int KSD = (D + 31) / 32;
   constexpr int MT = CT / 16;
+  static_assert(!SPLIT || (CT == 32 && !FOLD), "the split substitution covers 32-row chunks");
+  // SPLIT layout of A: two planes by the parity of the column s, A[t][s] at
+  // (s & 1) * SPL + t * (CT / 2) + (s >> 1); plane 1 starts 4 words further so that the
+  // two halves' row reads fall in different banks
+  constexpr int HS = CT / 2, SPL = CT * HS + 4;
+  float* const A2 = &As[0][0];
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
 
@@ -181,11 +189,60 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
         // reads into a branch per element) and kept or dropped by the select
         float dec = __expf(vec_lds[t] - gs), bt = vec_lds[CT + t];
         asm volatile("" : "+v"(dec), "+v"(bt));
-        As[t][sc] = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
+        const float val = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
+        if constexpr (SPLIT)
+          A2[(sc & 1) * SPL + t * HS + (sc >> 1)] = val;
+        else
+          As[t][sc] = val;
       }
     }
   }
   lds_barrier();
+
+  if constexpr (SPLIT) {
+    // Lane (h, j) = (lane >> 5, lane & 31) owns column j of T at the rows s = 2k + h and
+    // sums A[t][s] T[s][j] over those rows; one swap of the wave's halves adds the other
+    // parity's sum (own + other in both halves: the same value).  The own-parity row t + 1
+    // of A is requested before the sums of row t run.  Row t's count is the even
+    // parity's, ceil(t / 2); for the odd parity its last term is A[t][t] = 0 times a
+    // not yet computed (zero) T entry.
+    const int hf = lane >> 5, j = lane & 31;
+    const float* Ah = A2 + hf * SPL;
+    float Tc[HS];
+#pragma unroll
+    for (int k = 0; k < HS; ++k) Tc[k] = 0.f;
+    f32x4 arow[2][HS / 4];
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      if (t + 1 < CT) {
+#pragma unroll
+        for (int i = 0; i < ((t + 2) / 2 + 3) / 4; ++i)
+          arow[(t + 1) & 1][i] = *reinterpret_cast<const f32x4*>(Ah + (t + 1) * HS + 4 * i);
+      }
+      asm volatile("" ::: "memory");
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < (t + 1) / 2; ++k) {
+        const float av = arow[t & 1][k >> 2][k & 3];
+        if ((k & 1) == 0) p0 = fmaf(av, Tc[k], p0);
+        else p1 = fmaf(av, Tc[k], p1);
+      }
+      const float own = p0 + p1;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own), false, false);
+      const float val = (t == j ? 1.f : 0.f) - (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+      if ((t & 1) == hf) Tc[t >> 1] = val;
+      asm volatile("" : "+v"(Tc[t >> 1]) : : "memory");
+    }
+    const int pc = swz(j);
+#pragma unroll
+    for (int k = 0; k < HS; ++k) {
+      bf16_bits tt[NTF];
+      split_terms<NTF>(Tc[k], tt);
+#pragma unroll
+      for (int i = 0; i < NTF; ++i) Tout[i * tps + (2 * k + hf) * tld + pc] = tt[i];
+    }
+    return;
+  }
 
   // Forward substitution, lane j owns column j:  T[t][j] = [t == j] - sum_{s<t} A[t][s] T[s][j].
   // The sum runs as four interleaved partial sums (s mod 4) added in a fixed order.  Row

@@ -91,7 +91,7 @@ __device__ __forceinline__ void flush_tile(const FlushArgs<IO>& p, int h, int sl
   transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
   if (wave == 0) {
     const float g = wave_inclusive_scan(lane < n ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, n, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
+    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32>(Ks, CT * KP, As, n, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
   } else {
     // match the barriers inside factorize_chunk
     lds_barrier();
