@@ -19,17 +19,20 @@ using namespace chunk;
 
 // ==================================================================================
 // Replay flush: one workgroup per (request, value head), one wave per 16-row slab of
-// the state.  Reads the state once, factorizes the accepted rows (wave 0), applies
-// them, writes the state once.  The barriers order LDS only, so the state loads stay
-// in flight through the staging of the rows and the factorization.
+// the state.  Reads the state once, applies the accepted rows 32 at a time as blocks of
+// the chunked rule (each block factorized by wave 0, the state carried in registers from
+// block to block), writes the state once.  The barriers order LDS only, so the state
+// loads stay in flight through the staging of the first block and its factorization,
+// and the next block's rows are requested while the current one is applied.
 //
-// flush_tile applies n <= CT rows; the kernel's LDS is sized for its largest tile and
-// a workgroup takes the smallest tile (16, 32 or 64 rows) that holds its request's
-// rows, so a short log pays neither the substitution nor the products of a long one.
-template <typename IO, int D, int CT>
-__device__ __forceinline__ void flush_tile(const FlushArgs<IO>& p, int h, int slot, int n, bf16_bits* Ks,
-                                           bf16_bits* KTs, float* Vs, float* As_, bf16_bits* Ts, float* vec,
-                                           float* vec_tmp) {
+// One 32-row block covers the common case (a few accepted rows); its substitution runs
+// on both halves of the wave, so the kernel fits in fewer than 128 VGPRs and two
+// workgroups share a CU: the whole grid is resident at once.  (A 16-row block measured
+// slower than this 32-row one, and a 64-row block, at 256 VGPRs and twice the LDS, ran
+// in two rounds of workgroups.)
+template <typename IO, int D>
+__global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
+  constexpr int CT = 32;
   constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
   constexpr int NW = D / 16, NTH = 64 * NW;
   constexpr int KP = row_stride(D), TP = row_stride(CT), VP = D + 4;
@@ -37,138 +40,12 @@ __device__ __forceinline__ void flush_tile(const FlushArgs<IO>& p, int h, int sl
   constexpr int MT = CT / 16, KST = (MT + 1) / 2;
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int PER_ROW = D / VEC;
-  float (*As)[CT + 4] = reinterpret_cast<float (*)[CT + 4]>(As_);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int grp = lane >> 4, col = lane & 15;
-
-  const int hk = h / p.group;
-  const int my_row = wave * 16 + col;
-  float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
-  if constexpr (D < 32) zero_lds(Ks, NTI * CT * KP * sizeof(bf16_bits), tid, NTH);
-  if constexpr (CT < 32) {
-    // the operands' contraction runs over 32 columns: the 16 columns past a 16-row tile
-    // must read as zeros (their partners in the products are zero)
-    zero_lds(KTs, NTI * D * TP * sizeof(bf16_bits), tid, NTH);
-    zero_lds(Ts, NTF * CT * TP * sizeof(bf16_bits), tid, NTH);
-  }
-
-  // logged rows 0..n-1 of this slot, then the state: loads complete in issue order, so
-  // waiting for the rows (to stage them) leaves the state loads in flight until the
-  // products need them, past the factorization
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + NTH - 1) / NTH;
-  const size_t row0 = (size_t)slot * p.buf_rows;
-  // the rows' gates (wave 0) go first: the factorization waits for them
-  float a_row = 0.f, bb = 0.f;
-  if (wave == 0 && lane < n) {
-    const size_t ai = (row0 + lane) * p.Hv + h;
-    a_row = p.buf_a[ai];
-    bb = p.buf_b[ai];
-  }
-  const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
-  const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
-  uint4 kv[PER_THR], vv[PER_THR];
-#pragma unroll
-  for (int i = 0; i < PER_THR; ++i) {
-    const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    kv[i] = load16(kb + (size_t)t * p.Hqk * D + j0, idx < PIECES && t < n);
-    vv[i] = load16(vb + (size_t)t * p.Hv * D + j0, idx < PIECES && t < n);
-  }
-  f32x4 S[DT];
-#pragma unroll
-  for (int jt = 0; jt < DT; ++jt)
-    S[jt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp));
-  lds_barrier();  // the zero fill (d < 32) precedes the row stores
-#pragma unroll
-  for (int i = 0; i < PER_THR; ++i) {
-    const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-    if (idx < PIECES) {
-      store_row_terms<IO, NTI>(kv[i], Ks, CT * KP, KP, t, j0);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv[i], e);
-    }
-  }
-  lds_barrier();
-  transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
-  if (wave == 0) {
-    const float g = wave_inclusive_scan(lane < n ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32>(Ks, CT * KP, As, n, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
-  } else {
-    // match the barriers inside factorize_chunk
-    lds_barrier();
-    lds_barrier();
-  }
-  lds_barrier();
-
-  bf16x8 Sop[KSD][NTF];
-#pragma unroll
-  for (int s = 0; s < KSD; ++s) reg_operand<NTF>(S[2 * s], (2 * s + 1 < DT) ? S[2 * s + 1] : zero4(), Sop[s]);
-
-  f32x4 R[2 * KST];
-#pragma unroll
-  for (int mt = 0; mt < 2 * KST; ++mt) {
-    R[mt] = zero4();
-    if (mt >= MT) continue;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int s = 0; s < KSD; ++s) {
-      bf16x8 a[NTI];
-      op_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
-      mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * mt + 4 * grp + r;
-      float val = 0.f;
-      if (t < n) val = vec[2 * CT + t] * (Vs[t * VP + my_row] - vec[CT + t] * acc[r]);
-      R[mt][r] = val;
-    }
-  }
-  bf16x8 Rop[KST][NTF];
-#pragma unroll
-  for (int s = 0; s < KST; ++s) reg_operand<NTF>(R[2 * s], R[2 * s + 1], Rop[s]);
-  f32x4 Dt[2 * KST];
-#pragma unroll
-  for (int mt = 0; mt < 2 * KST; ++mt) {
-    Dt[mt] = zero4();
-    if (mt >= MT) continue;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int s = 0; s <= (mt >> 1); ++s) {
-      bf16x8 a[NTF];
-      op_terms<NTF>(Ts, CT * TP, TP, 16 * mt + col, s, grp, a);
-      mma_terms<NTF, NTF, ORD>(acc, a, Rop[s]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Dt[mt][r] = vec[3 * CT + 16 * mt + 4 * grp + r] * acc[r];
-  }
-  bf16x8 Dtop[KST][NTF];
-#pragma unroll
-  for (int s = 0; s < KST; ++s) reg_operand<NTF>(Dt[2 * s], Dt[2 * s + 1], Dtop[s]);
-  const float egn = vec[CT + n - 1];
-#pragma unroll
-  for (int jt = 0; jt < DT; ++jt) {
-    f32x4 acc;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = egn * S[jt][r];
-#pragma unroll
-    for (int s = 0; s < KST; ++s) {
-      bf16x8 a[NTI];
-      op_terms<NTI>(KTs, D * TP, TP, 16 * jt + col, s, grp, a);
-      mma_terms<NTI, NTF, ORD>(acc, a, Dtop[s]);
-    }
-    store16_through(state + (size_t)my_row * D + 16 * jt + 4 * grp, acc);
-  }
-}
-
-template <typename IO, int D, int CT>
-__global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
-  constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF;
-  constexpr int KP = row_stride(D), TP = row_stride(CT), VP = D + 4;
 
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
   __shared__ __attribute__((aligned(16))) bf16_bits KTs[NTI * D * TP];
   __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
-  __shared__ __attribute__((aligned(16))) float As[CT * (CT + 4)];
+  __shared__ float As[CT][CT + 4];
   __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
   __shared__ __attribute__((aligned(16))) float vec[4 * CT];
   __shared__ float vec_tmp[2 * CT];
@@ -176,23 +53,150 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
   // head-major grid: consecutive workgroups take consecutive heads of one request, so
   // they sweep that request's contiguous state block in address order
   const int h = blockIdx.x, r_ = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 4, col = lane & 15;
   // both words are fetched before either is tested (one round trip, not two)
   int slot = p.slot_ids[r_];
   int n = p.n_accepted[r_];
   asm volatile("" : "+s"(slot), "+s"(n));
   const bool bad = (slot < -1) | (slot >= p.n_slots) | (n < 0) | (n > p.buf_rows);
   if (bad) {
-    if (threadIdx.x == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
+    if (tid == 0 && h == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
     return;
   }
   if (slot < 0 || n == 0) return;  // padding or nothing accepted: untouched
-  if constexpr (CT > 16) {
-    if (n <= 16) return flush_tile<IO, D, 16>(p, h, slot, n, Ks, KTs, Vs, As, Ts, vec, vec_tmp);
-  }
-  if constexpr (CT > 32) {
-    if (n <= 32) return flush_tile<IO, D, 32>(p, h, slot, n, Ks, KTs, Vs, As, Ts, vec, vec_tmp);
-  }
-  flush_tile<IO, D, CT>(p, h, slot, n, Ks, KTs, Vs, As, Ts, vec, vec_tmp);
+
+  const int hk = h / p.group;
+  const int my_row = wave * 16 + col;
+  float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
+  if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), tid, NTH);  // padding columns, never written
+
+  // rows c0 .. c0 + nc - 1 of the slot's log: the gates (wave 0) first, since the
+  // factorization waits for them, then keys and values
+  const size_t row0 = (size_t)slot * p.buf_rows;
+  const IO* kb = p.buf_k + row0 * p.Hqk * D + (size_t)hk * D;
+  const IO* vb = p.buf_v + row0 * p.Hv * D + (size_t)h * D;
+  float a_row = 0.f, bb = 0.f;
+  uint4 kv[PER_THR], vv[PER_THR];
+  auto load_rows = [&](int c0, int nc) {
+    a_row = 0.f;
+    bb = 0.f;
+    if (wave == 0 && lane < nc) {
+      const size_t ai = (row0 + c0 + lane) * p.Hv + h;
+      a_row = p.buf_a[ai];
+      bb = p.buf_b[ai];
+    }
+#pragma unroll
+    for (int i = 0; i < PER_THR; ++i) {
+      const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+      kv[i] = load16(kb + (size_t)(c0 + t) * p.Hqk * D + j0, idx < PIECES && t < nc);
+      vv[i] = load16(vb + (size_t)(c0 + t) * p.Hv * D + j0, idx < PIECES && t < nc);
+    }
+  };
+  load_rows(0, n < CT ? n : CT);
+  // then the state: loads complete in issue order, so waiting for the rows (to stage
+  // them) leaves the state loads in flight until the products need them
+  f32x4 S[DT];
+#pragma unroll
+  for (int jt = 0; jt < DT; ++jt)
+    S[jt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp));
+
+  // one block of rows c0 .. c0 + nc - 1; written out twice below rather than as a loop,
+  // which would hoist every LDS address of the products out of it and hold them all in
+  // registers
+  auto apply_block = [&](const int c0, const int nc) {
+    // the previous block's readers are done with the LDS (first block: the zero fill,
+    // d < 32, precedes the row stores)
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < PER_THR; ++i) {
+      const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+      if (idx < PIECES) {
+        store_row_terms<IO, NTI>(kv[i], Ks, CT * KP, KP, t, j0);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv[i], e);
+      }
+    }
+    const float a_cur = a_row, b_cur = bb;
+    if (c0 + CT < n) load_rows(c0 + CT, n - c0 - CT);  // next block (n <= 2 CT)
+    lds_barrier();
+    transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
+    if (wave == 0) {
+      const float g = wave_inclusive_scan(lane < nc ? __logf(a_cur) : 0.f);
+      factorize_chunk<CT, D, NTI, NTF, ORD, false, true>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP, vec,
+                                                          vec_tmp);
+    } else {
+      // match the barriers inside factorize_chunk
+      lds_barrier();
+      lds_barrier();
+    }
+    lds_barrier();
+
+    // X = K S^T, R = b (V - e^g X), Dt = e^(g_n - g) T R, S^T <- e^(g_n) S^T + K^T Dt
+    bf16x8 Sop[KSD][NTF];
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) reg_operand<NTF>(S[2 * s], (2 * s + 1 < DT) ? S[2 * s + 1] : zero4(), Sop[s]);
+    f32x4 R[2 * KST];
+#pragma unroll
+    for (int mt = 0; mt < 2 * KST; ++mt) {
+      R[mt] = zero4();
+      if (mt >= MT) continue;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) {
+        bf16x8 a[NTI];
+        op_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
+        mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * mt + 4 * grp + r;
+        float val = 0.f;
+        if (t < nc) val = vec[2 * CT + t] * (Vs[t * VP + my_row] - vec[CT + t] * acc[r]);
+        R[mt][r] = val;
+      }
+    }
+    bf16x8 Rop[KST][NTF];
+#pragma unroll
+    for (int s = 0; s < KST; ++s) reg_operand<NTF>(R[2 * s], R[2 * s + 1], Rop[s]);
+    f32x4 Dt[2 * KST];
+#pragma unroll
+    for (int mt = 0; mt < 2 * KST; ++mt) {
+      Dt[mt] = zero4();
+      if (mt >= MT) continue;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s <= (mt >> 1); ++s) {
+        bf16x8 a[NTF];
+        op_terms<NTF>(Ts, CT * TP, TP, 16 * mt + col, s, grp, a);
+        mma_terms<NTF, NTF, ORD>(acc, a, Rop[s]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Dt[mt][r] = vec[3 * CT + 16 * mt + 4 * grp + r] * acc[r];
+    }
+    bf16x8 Dtop[KST][NTF];
+#pragma unroll
+    for (int s = 0; s < KST; ++s) reg_operand<NTF>(Dt[2 * s], Dt[2 * s + 1], Dtop[s]);
+    const float egn = vec[CT + nc - 1];
+#pragma unroll
+    for (int jt = 0; jt < DT; ++jt) {
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = egn * S[jt][r];
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        bf16x8 a[NTI];
+        op_terms<NTI>(KTs, D * TP, TP, 16 * jt + col, s, grp, a);
+        mma_terms<NTI, NTF, ORD>(acc, a, Dtop[s]);
+      }
+      S[jt] = acc;
+    }
+  };
+  static_assert(kMaxBufRows <= 2 * CT, "a log holds at most two blocks");
+  apply_block(0, n < CT ? n : CT);
+  if (n > CT) apply_block(CT, n - CT);
+#pragma unroll
+  for (int jt = 0; jt < DT; ++jt) store16_through(state + (size_t)my_row * D + 16 * jt + 4 * grp, S[jt]);
 }
 
 // ==================================================================================
@@ -427,30 +431,27 @@ hipError_t launch_replay(const ReplayArgs<float>& a, int D, int n_req, int ct, h
 }
 
 template <typename IO, int D>
-static hipError_t launch_flush_t(const FlushArgs<IO>& a, int n_req, int ct, hipStream_t st) {
+static hipError_t launch_flush_t(const FlushArgs<IO>& a, int n_req, hipStream_t st) {
   if (n_req == 0) return hipSuccess;
   dim3 grid(a.Hv, n_req);
-  if (ct <= 32)
-    hipLaunchKernelGGL((flush_kernel<IO, D, 32>), grid, dim3(64 * (D / 16)), 0, st, a);
-  else
-    hipLaunchKernelGGL((flush_kernel<IO, D, 64>), grid, dim3(64 * (D / 16)), 0, st, a);
+  hipLaunchKernelGGL((flush_kernel<IO, D>), grid, dim3(64 * (D / 16)), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st) {
+hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, hipStream_t st) {
   switch (D) {
-    case 16: return launch_flush_t<bf16_bits, 16>(a, n_req, ct, st);
-    case 32: return launch_flush_t<bf16_bits, 32>(a, n_req, ct, st);
-    case 64: return launch_flush_t<bf16_bits, 64>(a, n_req, ct, st);
-    case 128: return launch_flush_t<bf16_bits, 128>(a, n_req, ct, st);
+    case 16: return launch_flush_t<bf16_bits, 16>(a, n_req, st);
+    case 32: return launch_flush_t<bf16_bits, 32>(a, n_req, st);
+    case 64: return launch_flush_t<bf16_bits, 64>(a, n_req, st);
+    case 128: return launch_flush_t<bf16_bits, 128>(a, n_req, st);
     default: return hipErrorInvalidValue;
   }
 }
-hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, int ct, hipStream_t st) {
+hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, hipStream_t st) {
   switch (D) {
-    case 16: return launch_flush_t<float, 16>(a, n_req, ct, st);
-    case 32: return launch_flush_t<float, 32>(a, n_req, ct, st);
-    case 64: return launch_flush_t<float, 64>(a, n_req, ct, st);
+    case 16: return launch_flush_t<float, 16>(a, n_req, st);
+    case 32: return launch_flush_t<float, 32>(a, n_req, st);
+    case 64: return launch_flush_t<float, 64>(a, n_req, st);
     default: return hipErrorInvalidValue;
   }
 }

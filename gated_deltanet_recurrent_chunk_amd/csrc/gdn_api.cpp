@@ -534,17 +534,16 @@ gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t 
   if (!state_pool || !slot_ids || !buf_k || !buf_v || !buf_a || !buf_b || !n_accepted) return GDN_ERR_NULL_ARG;
   if (!aligned(state_pool, 16) || !aligned(buf_k, 16) || !aligned(buf_v, 16)) return GDN_ERR_BAD_SHAPE;
   if (n_req > 65535) return GDN_ERR_CAPACITY;
-  const int ct = buf_rows <= 32 ? 32 : 64;
   if (L.io == GDN_BF16) {
     FlushArgs<bf16_bits> fa{state_pool, slot_ids, n_accepted, static_cast<const bf16_bits*>(buf_k),
                             static_cast<const bf16_bits*>(buf_v), buf_a, buf_b, status, n_slots, buf_rows, L.Hqk,
                             L.Hv, L.Hv / L.Hqk};
-    return hip_status(launch_flush(fa, L.D, n_req, ct, stream));
+    return hip_status(launch_flush(fa, L.D, n_req, stream));
   }
   FlushArgs<float> fa{state_pool, slot_ids, n_accepted, static_cast<const float*>(buf_k),
                       static_cast<const float*>(buf_v), buf_a, buf_b, status, n_slots, buf_rows, L.Hqk, L.Hv,
                       L.Hv / L.Hqk};
-  return hip_status(launch_flush(fa, L.D, n_req, ct, stream));
+  return hip_status(launch_flush(fa, L.D, n_req, stream));
 }
 
 gdn_status gdn_gates(const gdn_layer* layer, hipStream_t stream, int64_t n_tokens, const void* ba,

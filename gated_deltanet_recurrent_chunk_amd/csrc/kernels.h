@@ -157,8 +157,8 @@ hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, int n_chun
 hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, int n_chunks, hipStream_t st);
 hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, hipStream_t st);
 hipError_t launch_scan(const ScanArgs<float>& a, int D, hipStream_t st);
-hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st);
-hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, int ct, hipStream_t st);
+hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, hipStream_t st);
+hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, hipStream_t st);
 hipError_t launch_replay(const ReplayArgs<bf16_bits>& a, int D, int n_req, int ct, hipStream_t st);
 hipError_t launch_replay(const ReplayArgs<float>& a, int D, int n_req, int ct, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs<bf16_bits>& a, int D, int n_req, hipStream_t st);

@@ -216,7 +216,7 @@ def test_flush_matches_sequential_oracle(g, D, dtype, rows):
     Hqk, Hv, n_slots = 2, 4, 6
     layer = g.Layer(Hqk, Hv, D, dtype)
     slots = [4, 0, 2, 5, -1, 1]
-    # counts on both sides of the 16-, 32- and 64-row tiles
+    # counts on both sides of the 32- and 64-row tiles
     acc = [min(rows, x) for x in ([16, 1, 17, 0, 5, rows] if rows <= 32 else [16, 1, 32, 0, 33, rows])]
     say(f"flush D={D} {dtype} rows={rows} acc={acc}")
     pool = gi.states(n_slots, Hv, D, seed=71).cuda()
