@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   f32x4 S[DT];
 #pragma unroll
   for (int jt = 0; jt < DT; ++jt)
-    S[jt] = *reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp);
+    S[jt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp));
   lds_barrier();  // the zero fills (d < 32) precede the row stores
 #pragma unroll
   for (int i = 0; i < PER_THR; ++i) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   lds_barrier();
   if (wave == 0) {
     const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
+    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
   } else {
     // match the barriers inside factorize_chunk
     lds_barrier();
