@@ -170,6 +170,8 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   // A = strict lower part of diag(b) exp(g_t - g_s) K K^T
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
+    // SPLIT: the substitution never reads rows t >= n, so their tiles are not formed
+    if (SPLIT && 16 * mt >= n) break;
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
       f32x4 acc = zero4();
@@ -205,34 +207,47 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
     // parity's sum (own + other in both halves: the same value).  The own-parity row t + 1
     // of A is requested before the sums of row t run.  Row t's count is the even
     // parity's, ceil(t / 2); for the odd parity its last term is A[t][t] = 0 times a
-    // not yet computed (zero) T entry.
+    // not yet computed (zero) T entry.  Rows t >= n of A are zero, so T's rows there are
+    // those of the identity: with n <= 16 only the first 16 rows are substituted (one
+    // uniform branch between two unrolled forms; a branch per row would hold more
+    // registers).
     const int hf = lane >> 5, j = lane & 31;
     const float* Ah = A2 + hf * SPL;
     float Tc[HS];
 #pragma unroll
     for (int k = 0; k < HS; ++k) Tc[k] = 0.f;
-    f32x4 arow[2][HS / 4];
+    auto substitute = [&](auto nr_) {
+      constexpr int NR = decltype(nr_)::value;
+      f32x4 arow[2][HS / 4];
 #pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      if (t + 1 < CT) {
+      for (int t = 0; t < NR; ++t) {
+        if (t + 1 < NR) {
 #pragma unroll
-        for (int i = 0; i < ((t + 2) / 2 + 3) / 4; ++i)
-          arow[(t + 1) & 1][i] = *reinterpret_cast<const f32x4*>(Ah + (t + 1) * HS + 4 * i);
+          for (int i = 0; i < ((t + 2) / 2 + 3) / 4; ++i)
+            arow[(t + 1) & 1][i] = *reinterpret_cast<const f32x4*>(Ah + (t + 1) * HS + 4 * i);
+        }
+        asm volatile("" ::: "memory");
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < (t + 1) / 2; ++k) {
+          const float av = arow[t & 1][k >> 2][k & 3];
+          if ((k & 1) == 0) p0 = fmaf(av, Tc[k], p0);
+          else p1 = fmaf(av, Tc[k], p1);
+        }
+        const float own = p0 + p1;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own), false, false);
+        const float val = (t == j ? 1.f : 0.f) - (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+        if ((t & 1) == hf) Tc[t >> 1] = val;
+        asm volatile("" : "+v"(Tc[t >> 1]) : : "memory");
       }
-      asm volatile("" ::: "memory");
-      float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-      for (int k = 0; k < (t + 1) / 2; ++k) {
-        const float av = arow[t & 1][k >> 2][k & 3];
-        if ((k & 1) == 0) p0 = fmaf(av, Tc[k], p0);
-        else p1 = fmaf(av, Tc[k], p1);
-      }
-      const float own = p0 + p1;
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own), false, false);
-      const float val = (t == j ? 1.f : 0.f) - (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
-      if ((t & 1) == hf) Tc[t >> 1] = val;
-      asm volatile("" : "+v"(Tc[t >> 1]) : : "memory");
-    }
+      for (int t = NR; t < CT; ++t)
+        if ((t & 1) == hf) Tc[t >> 1] = t == j ? 1.f : 0.f;
+    };
+    if (n <= CT / 2)
+      substitute(std::integral_constant<int, CT / 2>{});
+    else
+      substitute(std::integral_constant<int, CT>{});
     const int pc = swz(j);
 #pragma unroll
     for (int k = 0; k < HS; ++k) {

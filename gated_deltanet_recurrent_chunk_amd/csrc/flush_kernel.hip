@@ -31,7 +31,7 @@ using namespace chunk;
 // slower than this 32-row one, and a 64-row block, at 256 VGPRs and twice the LDS, ran
 // in two rounds of workgroups.)
 template <typename IO, int D>
-__global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
+__global__ __launch_bounds__(64 * (D / 16), 4) void flush_kernel(FlushArgs<IO> p) {
   constexpr int CT = 32;
   constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
   constexpr int NW = D / 16, NTH = 64 * NW;
@@ -118,7 +118,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
       }
     }
     const float a_cur = a_row, b_cur = bb;
-    if (c0 + CT < n) load_rows(c0 + CT, n - c0 - CT);  // next block (n <= 2 CT)
     lds_barrier();
     transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
     if (wave == 0) {
@@ -131,6 +130,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
       lds_barrier();
     }
     lds_barrier();
+    // the next block's rows (n <= 2 CT), requested after the factorization, whose
+    // registers they would otherwise add to, and in flight during the products
+    if (c0 + CT < n) load_rows(c0 + CT, n - c0 - CT);
 
     // X = K S^T, R = b (V - e^g X), Dt = e^(g_n - g) T R, S^T <- e^(g_n) S^T + K^T Dt
     bf16x8 Sop[KSD][NTF];
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
 #pragma unroll
     for (int mt = 0; mt < 2 * KST; ++mt) {
       R[mt] = zero4();
-      if (mt >= MT) continue;
+      if (mt >= MT || 16 * mt >= nc) continue;  // rows t >= nc: R = 0
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < KSD; ++s) {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void flush_kernel(FlushArgs<IO> p) {
 #pragma unroll
     for (int mt = 0; mt < 2 * KST; ++mt) {
       Dt[mt] = zero4();
-      if (mt >= MT) continue;
+      if (mt >= MT || 16 * mt >= nc) continue;  // rows t >= nc: identity rows of T, R = 0
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s <= (mt >> 1); ++s) {
