@@ -29,6 +29,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-I", os.path.j
           # matrix-core results in ordinary VGPRs: the kernels read every product back
           # with vector instructions, and accumulators in AGPRs cost a copy per register
           "-mllvm", "-amdgpu-mfma-vgpr-form"]
+# per-source flags: the flush kernel takes its two per-request index arrays as leading
+# scalar arguments, preloaded into SGPRs at wave launch (one memory round trip fewer
+# before its first loads)
+EXTRA = {"flush_kernel.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -38,7 +42,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.rsplit(".", 1)[0] + ".o")
         objs.append(obj)
-        cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".hip"):
             cmd = cmd[:1] + ["-x", "hip"] + cmd[1:]
         if verbose:

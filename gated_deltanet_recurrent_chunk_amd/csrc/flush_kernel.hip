@@ -31,7 +31,8 @@ using namespace chunk;
 // slower than this 32-row one, and a 64-row block, at 256 VGPRs and twice the LDS, ran
 // in two rounds of workgroups.)
 template <typename IO, int D>
-__global__ __launch_bounds__(64 * (D / 16), 4) void flush_kernel(FlushArgs<IO> p) {
+__global__ __launch_bounds__(64 * (D / 16), (sizeof(IO) == 2 && D >= 64) ? 4 : 1) void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted,
+                                                                  FlushArgs<IO> p) {
   constexpr int CT = 32;
   constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
   constexpr int NW = D / 16, NTH = 64 * NW;
@@ -55,9 +56,11 @@ __global__ __launch_bounds__(64 * (D / 16), 4) void flush_kernel(FlushArgs<IO> p
   const int h = blockIdx.x, r_ = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
-  // both words are fetched before either is tested (one round trip, not two)
-  int slot = p.slot_ids[r_];
-  int n = p.n_accepted[r_];
+  // slot_ids and n_accepted (also in p) come first in the argument list: preloaded into
+  // SGPRs at launch where the build asks for it; both words are fetched before either is
+  // tested (one round trip, not two)
+  int slot = slot_ids[r_];
+  int n = n_accepted[r_];
   asm volatile("" : "+s"(slot), "+s"(n));
   const bool bad = (slot < -1) | (slot >= p.n_slots) | (n < 0) | (n > p.buf_rows);
   if (bad) {
@@ -436,7 +439,7 @@ template <typename IO, int D>
 static hipError_t launch_flush_t(const FlushArgs<IO>& a, int n_req, hipStream_t st) {
   if (n_req == 0) return hipSuccess;
   dim3 grid(a.Hv, n_req);
-  hipLaunchKernelGGL((flush_kernel<IO, D>), grid, dim3(64 * (D / 16)), 0, st, a);
+  hipLaunchKernelGGL((flush_kernel<IO, D>), grid, dim3(64 * (D / 16)), 0, st, a.slot_ids, a.n_accepted, a);
   return hipGetLastError();
 }
 

@@ -861,7 +861,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   using Shp = ScanStaged<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
   constexpr int DT = D / 16, KSD = D / 32;
-  constexpr int NSP = Shp::NSP, SP = Shp::SP, NW = Shp::NW, NG = Shp::NG;
+  constexpr int NSP = Shp::NSP, SP = Shp::SP, NW = Shp::NW;
   constexpr int KSH = KSD / NSP, DTH = DT / NSP, MR = 4 / NSP;
   constexpr int ESZ = sizeof(IO);
   // staged chunk: the factor record (its last 1 KiB granule partial), then 64 value
