@@ -279,8 +279,8 @@ gdn_status gdn_decode_mixed(const gdn_layer* layer, hipStream_t stream, int32_t 
 
 /* ReplaySSM flush ("Caching less to serve more requests", section "What we changed"):
  * each request keeps one state plus a log of per-token inputs since it; the flush
- * folds the first n_accepted[r] logged rows of request r into its state as one
- * blocked update, in one launch for all requests.  The state in slot slot_ids[r] of
+ * folds the first n_accepted[r] logged rows of request r into its state as blocked
+ * updates of up to 32 rows each, in one launch for all requests.  The state in slot slot_ids[r] of
  * state_pool [n_slots][n_v_heads][d][d] is read once and written once; rows at or
  * past n_accepted[r] are never read (a rollback is just a smaller n_accepted).
  *   buf_k [n_slots][buf_rows][n_qk_heads][d], buf_v [n_slots][buf_rows][n_v_heads][d]
