@@ -181,7 +181,11 @@ __device__ __forceinline__ void row_terms(const RowOp<float>& o, bf16x8 (&t)[NT]
 template <typename IO, int D>
 struct FactorLds {
   using Cfg = PrefillCfg<IO, D>;
-  static constexpr int KP = row_stride(D), TP = row_stride(CT);
+  // T planes unpadded (rows of 64 elements, 128 bytes): with padded rows the two plane
+  // arrays took 18,432 bytes each and the workgroup 54,272 bytes, which LDS allocation
+  // granules round past a third of the CU's 160 KiB, so only two workgroups were
+  // resident (measured: 512 at once over 256 CUs).  Unpadded: 52,224 bytes, three.
+  static constexpr int KP = row_stride(D), TP = CT;
   static constexpr int KS = Cfg::NTI * CT * KP;  // bf16 elements of the key (or query) planes
   static constexpr int TT = Cfg::NTF * CT * TP;  // bf16 elements of T^T (or T'') planes
   static constexpr int QT = KS > TT ? KS : TT;   // query planes, later T''; key planes, later T^T
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int PER_ROW = D / VEC;
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + 255) / 256;
-  // 54,272 bytes at d = 128 with bf16 inputs: three workgroups per CU
+  // 52,224 bytes at d = 128 with bf16 inputs: three workgroups per CU
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[L::QT];  // key rows, later T^T
   __shared__ __attribute__((aligned(16))) bf16_bits QT[L::QT];  // query rows, later T''
   // A; its diagonal blocks later hold the T_ii planes, its padding columns the row vectors
