@@ -181,10 +181,12 @@ __device__ __forceinline__ void row_terms(const RowOp<float>& o, bf16x8 (&t)[NT]
 template <typename IO, int D>
 struct FactorLds {
   using Cfg = PrefillCfg<IO, D>;
-  // T planes unpadded (rows of 64 elements, 128 bytes): with padded rows the two plane
-  // arrays took 18,432 bytes each and the workgroup 54,272 bytes, which LDS allocation
-  // granules round past a third of the CU's 160 KiB, so only two workgroups were
-  // resident (measured: 512 at once over 256 CUs).  Unpadded: 52,224 bytes, three.
+  // T planes unpadded (rows of 64 elements, 128 bytes), in the xor layout (16-byte pieces
+  // permuted by row) so that 16-row operand reads stay free of bank conflicts: with
+  // padded rows the two plane arrays took 18,432 bytes each and the workgroup 54,272
+  // bytes, which LDS allocation granules round past a third of the CU's 160 KiB, so only
+  // two workgroups were resident (measured: 512 at once over 256 CUs).  Now 52,224
+  // bytes, three.
   static constexpr int KP = row_stride(D), TP = CT;
   static constexpr int KS = Cfg::NTI * CT * KP;  // bf16 elements of the key (or query) planes
   static constexpr int TT = Cfg::NTF * CT * TP;  // bf16 elements of T^T (or T'') planes
@@ -394,7 +396,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       for (int r = 0; r < 4; ++r) split_terms<NTF>(Tb[i][r], tt[r]);
 #pragma unroll
       for (int q = 0; q < NTF; ++q)
-        *reinterpret_cast<uint2*>(Tt + q * CT * TP + (16 * W + col) * TP + swz(16 * i + 4 * grp)) =
+        *reinterpret_cast<uint2*>(Tt + q * CT * TP + xrun<2 * TP>(16 * W + col, swz(16 * i + 4 * grp))) =
             uint2{(uint32_t)tt[0][q] | ((uint32_t)tt[1][q] << 16), (uint32_t)tt[2][q] | ((uint32_t)tt[3][q] << 16)};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -402,7 +404,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
         bf16_bits t2[NTF];
         split_terms<NTF>((Tb[i][r] * rowvec(As, 3, t)) * bj, t2);
 #pragma unroll
-        for (int q = 0; q < NTF; ++q) Tl[q * CT * TP + t * TP + pc] = t2[q];
+        for (int q = 0; q < NTF; ++q) Tl[q * CT * TP + xoff<2 * TP>(t, pc >> 3) + (pc & 7)] = t2[q];
       }
     }
   }
@@ -414,7 +416,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
   for (int it = W; it < kFragCombos * NTF; it += 4) {
     const int f = it / NTF, q = it % NTF;
     const int mt = f < 2 ? f : 2 + (f - 2) / 2, s = f < 2 ? 0 : (f - 2) % 2;
-    const bf16x8 v = op_read(Tl + q * CT * TP, TP, 16 * mt + col, s, grp);
+    const bf16x8 v = xop_read<2 * TP>(Tl + q * CT * TP, 16 * mt + col, s, grp);
     *reinterpret_cast<bf16x8*>(rec + Cfg::T_OFF + it * 1024 + lane * 16) = v;
   }
   // PT'' = (scale P) T diag(b) for row tile ut = W, through its transpose: tile (jt, W)
@@ -433,7 +435,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
 #pragma unroll
       for (int sp = jt >> 1; sp < NPS; ++sp) {
         bf16x8 a[NTF];
-        op_terms<NTF>(Tt, CT * TP, TP, 16 * jt + col, sp, grp, a);
+        xop_terms<2 * TP, NTF>(Tt, CT * TP, 16 * jt + col, sp, grp, a);
         mma_terms<NTF, NTF, ORD>(acc[h2], a, Pfr[sp]);
       }
     }
