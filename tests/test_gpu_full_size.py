@@ -194,10 +194,13 @@ def test_varlen_27b_stepped_resume_is_bit_identical_to_cold(g):
     assert rel_l2(f64(cold_S[i][heads]), S_ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("counts", ["uniform", 16, 17])
-def test_flush_4b_full_size_all_heads(g, counts):
+@pytest.mark.parametrize("counts,rows", [("uniform", None), (16, None), (17, None), (32, 64), (33, 64)])
+def test_flush_4b_full_size_all_heads(g, counts, rows):
+    """The flush at the 4B shape: 32-slot log (the pages' size) and a 64-slot log whose
+    33 accepted rows take two 32-row blocks."""
     w = gi.FLUSH_4B
-    n_req, H, D, rows = w["n_req"], w["n_heads"], w["head_dim"], w["buf_rows"]
+    n_req, H, D = w["n_req"], w["n_heads"], w["head_dim"]
+    rows = rows or w["buf_rows"]
     layer = g.Layer(16, H, D, torch.bfloat16)
     acc = gi.accepted_counts(n_req, w["seed"]) if counts == "uniform" else torch.full((n_req,), counts, dtype=torch.int32)
     say(f"full-size flush counts={acc.tolist()}")
