@@ -299,18 +299,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
     }
   }
   lds_barrier();
-  if (wave == 0) {
-    const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
-  } else {
-    // match the barriers inside factorize_chunk
-    lds_barrier();
-    lds_barrier();
-  }
-  lds_barrier();
-
-  // P tiles, dealt round robin to the waves, as NTF bf16 term planes (row t, column s)
-  for (int ti = wave; ti < NPT; ti += NW) {
+  // P tiles, as NTF bf16 term planes (row t, column s): they need the gates only, so the
+  // waves other than wave 0 form them while wave 0 factorizes (between the barrier that
+  // publishes the gate vectors and the next one); with one wave, after the factorization
+  auto p_tiles = [&](int first, int step) {
+  for (int ti = first; ti < NPT; ti += step) {
     const int mt = MT == 4 ? (ti < 2 ? 0 : ti < 4 ? 1 : ti < 8 ? 2 : 3) : MT == 2 ? ti >> 1 : 0;
     const int nt = MT == 4 ? (ti < 4 ? ti & 1 : (ti - 4) & 3) : MT == 2 ? ti & 1 : 0;
     f32x4 acc = zero4();
@@ -335,6 +328,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
 #pragma unroll
       for (int q = 0; q < NTF; ++q) Ps[q * CT * TP + t * TP + swz(sc)] = tt[q];
     }
+  }
+  };
+  if (wave == 0) {
+    const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
+    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
+    if constexpr (NW == 1) {
+      lds_barrier();
+      p_tiles(0, 1);
+    }
+  } else {
+    // match the barriers inside factorize_chunk; the first publishes the gate vectors
+    lds_barrier();
+    p_tiles(wave - 1, NW - 1);
+    lds_barrier();
   }
   lds_barrier();
 
