@@ -1,9 +1,10 @@
 // flush_kernel.hip -- the ReplaySSM kernels ("Caching less to serve more requests",
 // section "What we changed"): each request keeps one state plus a log of its per-token
 // inputs since it.
-//   flush:   folds the first n accepted rows of the log into the state as one block of
-//            the chunked gated delta rule (chunk_common.h), one launch for all requests.
-//            The state is read once and written once; rows at or past n are never read.
+//   flush:   folds the first n accepted rows of the log into the state as blocks of up
+//            to 32 rows of the chunked gated delta rule (chunk_common.h), one launch for
+//            all requests.  The state is read once and written once; rows at or past n
+//            are never read.
 //   replay:  the outputs of new rows appended behind the logged ones, computed from the
 //            state and the log as one block of the same rule; nothing is written back.
 #include <hip/hip_runtime.h>
@@ -26,13 +27,14 @@ using namespace chunk;
 // and the next block's rows are requested while the current one is applied.
 //
 // One 32-row block covers the common case (a few accepted rows); its substitution runs
-// on both halves of the wave, so the kernel fits in fewer than 128 VGPRs and two
-// workgroups share a CU: the whole grid is resident at once.  (A 16-row block measured
-// slower than this 32-row one, and a 64-row block, at 256 VGPRs and twice the LDS, ran
-// in two rounds of workgroups.)
+// on both halves of the wave and, with at most 16 rows, skips the empty half.  The
+// kernel fits in 128 VGPRs, so two workgroups share a CU and the whole grid is resident
+// at once.  (A 16-row block measured slower than this 32-row one, and a 64-row block,
+// at 256 VGPRs and twice the LDS, ran in two rounds of workgroups.)  The state is read
+// non-temporal and written through to device scope (store16_through).
 template <typename IO, int D>
-__global__ __launch_bounds__(64 * (D / 16), (sizeof(IO) == 2 && D >= 64) ? 4 : 1) void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted,
-                                                                  FlushArgs<IO> p) {
+__global__ __launch_bounds__(64 * (D / 16), (sizeof(IO) == 2 && D >= 64) ? 4 : 1)
+void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<IO> p) {
   constexpr int CT = 32;
   constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
   constexpr int NW = D / 16, NTH = 64 * NW;
