@@ -186,3 +186,50 @@ def accepted_counts(n_req: int, seed: int, max_rows: int = 16):
 def permutation(n: int, seed: int):
     g = _gen(seed, 60_000)
     return torch.randperm(n, generator=g)
+
+
+# ---------------------------------------------------------------- harder input domains
+# Inputs at the edges of the contract (a in (0, 1], b in [0, 1]), for parity cases the
+# workloads' distributions never reach: gates at the smallest normal decay (the value
+# the packed core's gate step clamps to) and at exactly 1, write strengths of exactly 0
+# and 1, keys far from unit norm and keys nearly parallel to each other.  The update
+# stays bounded while b_t |k_t|^2 <= 2; the draws keep to that range.
+A_CLAMP = 2.0 ** -126  # the smallest normal fp32 value
+
+
+def edge_gates(T: int, n_v: int, seed: int = 0):
+    """a, b [T, n_v] fp32: a is 2^-126 (a full reset) with probability 0.2, exactly 1
+    with probability 0.2, else exp(-softplus(N(0,1)) * 0.1); b is exactly 0 or 1 with
+    probability 0.25 each, else sigmoid(N(0,1))."""
+    g = _gen(seed, 70_000)
+    u = torch.rand(T, n_v, generator=g)
+    a = torch.exp(-torch.nn.functional.softplus(torch.randn(T, n_v, generator=g)) * 0.1)
+    a = torch.where(u < 0.2, torch.full_like(a, A_CLAMP), torch.where(u < 0.4, torch.ones_like(a), a))
+    w = torch.rand(T, n_v, generator=g)
+    b = torch.sigmoid(torch.randn(T, n_v, generator=g))
+    b = torch.where(w < 0.25, torch.zeros_like(b), torch.where(w < 0.5, torch.ones_like(b), b))
+    return a.float().contiguous(), b.float().contiguous()
+
+
+def scaled_keys(T: int, n_qk: int, d: int, io_dtype=torch.bfloat16, seed: int = 0, lo: float = 0.25,
+                hi: float = 4.0):
+    """k [T, n_qk, d]: unit rows times a norm log-uniform in [lo, hi] (cast to io dtype),
+    and the squared norm of each row as cast, [T, n_qk] fp32 (for bounding b)."""
+    g = _gen(seed, 71_000)
+    k = _unit_rows(torch.randn(T, n_qk, d, generator=g))
+    r = torch.exp(torch.log(torch.tensor(lo)) + torch.rand(T, n_qk, 1, generator=g) *
+                  (torch.log(torch.tensor(hi)) - torch.log(torch.tensor(lo))))
+    k = (k * r).to(io_dtype)
+    return k, (k.float() ** 2).sum(-1)
+
+
+def collinear_keys(T: int, n_qk: int, d: int, io_dtype=torch.bfloat16, seed: int = 0, spread: float = 0.05,
+                   run: int = 48):
+    """k [T, n_qk, d] unit rows that stay nearly parallel over runs of `run` tokens: each
+    run shares a base direction, and every row adds a random offset of norm about
+    `spread` before normalising (cosines between rows of a run near 1 - spread^2)."""
+    g = _gen(seed, 72_000)
+    n_runs = (T + run - 1) // run
+    base = _unit_rows(torch.randn(n_runs, n_qk, d, generator=g)).repeat_interleave(run, 0)[:T]
+    k = _unit_rows(base + spread * torch.randn(T, n_qk, d, generator=g) / d ** 0.5)
+    return k.to(io_dtype)

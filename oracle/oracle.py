@@ -239,10 +239,13 @@ def bf16_round(x) -> np.ndarray:
     Used to compare bf16-typed GPU results with oracle values rounded the same way.
     Goes through float32 first, then rounds the float32 bit pattern to 8 significant
     bits with ties to even (the float64 -> float32 step is the nearest float32; the
-    double rounding this implies is documented where the comparison is made).
+    double rounding this implies is documented where the comparison is made).  Values
+    past the largest bf16 round to infinity; infinities and zeros keep their sign; a
+    NaN stays a NaN (the rounding increment is not applied to it).
     """
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     u = f.view(np.uint32).astype(np.uint64)
     lsb = (u >> 16) & 1
-    u = (u + 0x7FFF + lsb) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    r = (u + 0x7FFF + lsb) & 0xFFFF0000
+    r = np.where(np.isnan(f), u | 0x00400000, r) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)

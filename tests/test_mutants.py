@@ -6,6 +6,7 @@ the CPU into a temporary library.  Every pin test of the oracle is then run agai
 it; at least one must fail.  The real oracle passes all of them (test_oracle_pins.py).
 """
 import inspect
+import numpy as np
 import os
 import subprocess
 
@@ -71,3 +72,36 @@ def test_pins_reject_mutant(name, tmp_path):
     finally:
         oracle._swap_library(prev)
     assert failed, f"no pin caught mutant {name}"
+
+
+# bf16 rounding is Python (oracle.bf16_round); its mutants replace the function.
+def _bf16_truncate(x):
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    return (f.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+
+def _bf16_ties_away(x):
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    return ((u + 0x8000) & 0xFFFF0000).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _bf16_ties_up_in_magnitude_only_for_odd(x):  # ties to odd
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + (1 - lsb)) & 0xFFFF0000).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("mutant", [_bf16_truncate, _bf16_ties_away, _bf16_ties_up_in_magnitude_only_for_odd])
+def test_pins_reject_bf16_rounding_mutant(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "bf16_round", mutant)
+    failed = []
+    for fn in _pins():
+        if "bf16" not in getattr(fn, "__name__", ""):
+            continue
+        try:
+            fn()
+        except AssertionError:
+            failed.append(fn.__name__)
+    assert failed, f"no pin caught {mutant.__name__}"

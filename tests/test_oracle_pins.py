@@ -414,3 +414,83 @@ def test_boundary_counts_of_the_workloads():
     assert oracle.count_boundaries(0, 8192, 896) == 9
     assert oracle.count_boundaries(0, 229376, 896) == 256
     assert oracle.count_boundaries(1792, 12000 - 1792, 896) == 11
+
+
+# ---------------------------------------------------------------- bf16 rounding
+# Every bf16-typed expected value (conv outputs, conv + norm, gated norm) is the oracle's
+# fp64 result passed through oracle.bf16_round.  These pins fix that rounding to
+# round-to-nearest with ties to even on 8 significant bits (bf16 keeps fp32's exponent
+# range, subnormals included), independently of how the oracle implements it.
+
+def _bf16_exact(x: float) -> float:
+    """Nearest bf16 to x by exact rational arithmetic, ties to even; inf past the
+    largest finite bf16 (round-to-nearest overflow rule)."""
+    from fractions import Fraction
+    import math
+    if x == 0 or math.isinf(x) or math.isnan(x):
+        return x
+    s = -1.0 if x < 0 else 1.0
+    fx = Fraction(abs(x))
+    e = max(math.frexp(abs(x))[1] - 1, -126)       # exponent of the leading bit, clamped to normal range
+    quantum = Fraction(2) ** (e - 7)               # spacing of bf16 values at this exponent
+    m = fx / quantum
+    n = math.floor(m)
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * quantum
+    if val >= Fraction(2) ** 128 - Fraction(2) ** 119:  # >= (max bf16 + half ulp) rounds to inf
+        return s * math.inf
+    return s * float(val)
+
+
+def test_bf16_round_hand_ties():
+    cases = [
+        (1.0 + 2.0 ** -8, 1.0),                     # halfway between 1 and 1 + 2^-7: even is 1
+        (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),     # halfway, the odd neighbour loses
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0 + 2.0 ** -7),   # just past halfway rounds up
+        (1.0 + 2.0 ** -8 - 2.0 ** -20, 1.0),               # just below halfway rounds down
+        (-(1.0 + 2.0 ** -8), -1.0),
+        (-(1.0 + 3 * 2.0 ** -8), -(1.0 + 2.0 ** -6)),
+        (2.0 ** -134, 0.0),                         # half the smallest bf16 subnormal: ties to 0
+        (3 * 2.0 ** -134, 2.0 ** -132),             # 1.5 subnormal quanta: ties to the even 2
+        (2.0 ** -133, 2.0 ** -133),                 # the smallest subnormal itself
+        (255 * 2.0 ** -133 + 2.0 ** -134, 2.0 ** -125),  # largest subnormal + half: carries into normal
+        (3.3895313892515355e38, 3.3895313892515355e38),  # the largest finite bf16
+        (3.4028234663852886e38, np.inf),            # the largest fp32 rounds past it
+        (0.0, 0.0), (np.inf, np.inf), (-np.inf, -np.inf),
+    ]
+    got = oracle.bf16_round(np.array([c[0] for c in cases]))
+    for (x, want), y in zip(cases, got):
+        assert y == want, (x, want, y)
+    assert np.signbit(oracle.bf16_round(np.array([-0.0]))[0])
+    assert np.isnan(oracle.bf16_round(np.array([np.nan]))[0])
+    # a NaN whose payload sits only in the low 16 bits stays a NaN (no carry into inf)
+    low_nan = np.array([0x7F800001], dtype=np.uint32).view(np.float32).astype(np.float64)
+    assert np.isnan(oracle.bf16_round(low_nan)[0])
+
+
+def test_bf16_round_matches_exact_rational_rounding():
+    """On fp32-representable inputs (no double rounding), across normal, subnormal and
+    near-overflow magnitudes, including constructed ties."""
+    r = rng(77)
+    bits = r.integers(0, 2 ** 32, size=4000, dtype=np.uint64).astype(np.uint32)
+    # force a quarter of them onto exact ties (low 16 bits = 0x8000)
+    bits[:1000] = (bits[:1000] & 0xFFFF0000) | 0x8000
+    f = bits.view(np.float32)
+    x = f[np.isfinite(f)].astype(np.float64)
+    got = oracle.bf16_round(x)
+    want = np.array([_bf16_exact(float(v)) for v in x])
+    assert np.array_equal(got, want)
+
+
+def test_bf16_round_matches_torch_cpu_conversion():
+    import torch
+    r = rng(78)
+    bits = r.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    bits[:5000] = (bits[:5000] & 0xFFFF0000) | 0x8000
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).float().numpy().astype(np.float64)
+    got = oracle.bf16_round(f.astype(np.float64))
+    assert np.array_equal(got, want)
