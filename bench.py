@@ -313,7 +313,8 @@ def main():
 
     # ------------------------------------------------------------ mixed batch (27B layer)
     # one packed batch: 256 decode tokens (rows 0..255) and the 8,192-token prefill behind
-    # them; the conv runs over all 257 sequences, the prefill over its rows, the decode
+    # them; the conv runs over the prefill sequence and, in its decode regime, over the
+    # decode tokens (their tails in a slot pool), the prefill over its rows, the decode
     # tokens through decode_mixed
     mT = n_dec + T
     mx = torch.cat([gi.conv_inputs(n_dec, C, 4, torch.bfloat16, seed=1008)[0].to(dev), x])
@@ -322,16 +323,13 @@ def main():
     ma, mb = torch.cat([da, a]), torch.cat([db, b])
     mo = torch.empty(mT, H, D, dtype=torch.float32, device=dev)
     mtails = torch.zeros(n_dec, 3, C, dtype=torch.bfloat16, device=dev)
-    m_cu = list(range(n_dec + 1)) + [n_dec + T]
-    m_sp = [100] * n_dec + [0]
-    m_refs = [("slot", mtails[i], mtails[i]) for i in range(n_dec)] + [("zero", None, tail)]
-    m_pages = list(range(n_ck))
-    mcws = torch.empty(g.conv_workspace_bytes(layer, m_cu, m_sp, BLOCK), dtype=torch.uint8, device=dev)
     mrows = torch.arange(n_dec, dtype=torch.int32, device=dev)
     pre = slice(n_dec, mT)
 
     def mixed_step():
-        g.conv_update(layer, mx, w, m_refs, m_cu, m_sp, my, ckpt=pool, page_ids=m_pages, workspace=mcws)
+        g.conv_update(layer, mx[pre], w, [("zero", None, tail)], cu, sp, my[pre], ckpt=pool, page_ids=page_ids,
+                      workspace=cws)
+        g.conv_decode(layer, mx, w, mtails, dslots, my, rows=mrows)
         g.chunk_prefill(layer, mq[pre], mk[pre], mv[pre], ma[pre], mb[pre], cu, sp, [("zero", None, S)], mo[pre],
                         ckpt=pool, page_ids=page_ids, workspace=ws)
         g.decode_mixed(layer, mq, mk, mv, ma, mb, dpool, dslots, mrows, mo)

@@ -37,7 +37,8 @@ SRC_ZERO, SRC_SLOT, SRC_CHECKPOINT = 0, 1, 2
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_BAD_DTYPE",
                 4: "GDN_ERR_BAD_VARLEN", 5: "GDN_ERR_OFF_BOUNDARY", 6: "GDN_ERR_PAGE_TOO_SMALL",
                 7: "GDN_ERR_BAD_PAGE", 8: "GDN_ERR_CAPACITY", 9: "GDN_ERR_WORKSPACE", 10: "GDN_ERR_HIP",
-                11: "GDN_ERR_BAD_SOURCE"}
+                11: "GDN_ERR_BAD_SOURCE", 12: "GDN_ERR_STAGING"}
+INLINE_SEQS, INLINE_PAGES = 8, 256  # tables up to this size travel in the kernel arguments
 
 
 class _Layer(ctypes.Structure):
@@ -53,6 +54,10 @@ class _Varlen(ctypes.Structure):
 
 class _StateRef(ctypes.Structure):
     _fields_ = [("src_kind", ctypes.c_int32), ("src", ctypes.c_void_p), ("dst", ctypes.c_void_p)]
+
+
+class _Staging(ctypes.Structure):
+    _fields_ = [("host", ctypes.c_void_p), ("bytes", ctypes.c_size_t)]
 
 
 class _Ckpt(ctypes.Structure):
@@ -80,13 +85,18 @@ _decl("gdn_floor_chunk", _i64, [_i64, _i64])
 _decl("gdn_count_boundaries", _i64, [_i64, _i64, _i64])
 _decl("gdn_block_size_for_state", _i64, [_i64, _i64, _i64])
 _decl("gdn_prefill_workspace_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
+_decl("gdn_prefill_staging_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
 _decl("gdn_conv_workspace_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
-_decl("gdn_conv_update", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz])
+_decl("gdn_conv_staging_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
+_decl("gdn_conv_update", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz,
+                                _P(_Staging)])
+_decl("gdn_conv_decode", _i32, [_P(_Layer), _vp, _i32, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp])
 _decl("gdn_chunk_prefill", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
-                                  _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz])
-_decl("gdn_prefill_factorize", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _i64, _vp, _vp, _i32, _vp, _sz])
+                                  _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz, _P(_Staging)])
+_decl("gdn_prefill_factorize", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _i64, _vp, _vp, _i32, _vp, _sz,
+                                      _P(_Staging)])
 _decl("gdn_prefill_scan", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _P(_StateRef),
-                                 _P(_Ckpt), _vp, _vp, _sz])
+                                 _P(_Ckpt), _vp, _vp, _sz, _P(_Staging)])
 _decl("gdn_decode_step", _i32, [_P(_Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp])
 _decl("gdn_replay_flush", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp])
 _decl("gdn_decode_mixed", _i32, [_P(_Layer), _vp, _i32, _i64, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp,
@@ -99,7 +109,7 @@ _decl("gdn_replay_forward", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_state_bytes", "gdn_conv_tail_bytes",
             "gdn_checkpoint_bytes", "gdn_conv_channels", "gdn_cached_prefix_tokens", "gdn_floor_chunk",
             "gdn_count_boundaries", "gdn_block_size_for_state", "gdn_prefill_workspace_bytes",
-            "gdn_conv_workspace_bytes", "gdn_conv_update", "gdn_chunk_prefill", "gdn_prefill_factorize",
+            "gdn_prefill_staging_bytes", "gdn_conv_workspace_bytes", "gdn_conv_staging_bytes", "gdn_conv_update", "gdn_conv_decode", "gdn_chunk_prefill", "gdn_prefill_factorize",
             "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush", "gdn_replay_forward",
             "gdn_gates", "gdn_gated_norm", "gdn_decode_mixed")
 
@@ -247,6 +257,15 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _sync(stream):
+    if stream is None:
+        torch.cuda.current_stream().synchronize()
+    elif hasattr(stream, "synchronize"):
+        stream.synchronize()
+    else:
+        torch.cuda.ExternalStream(int(stream)).synchronize()
+
+
 # ------------------------------------------------------------------ helpers
 
 def cached_prefix_tokens(shared: int, block: int) -> int:
@@ -275,6 +294,38 @@ def conv_workspace_bytes(layer: Layer, cu_seqlens, start_pos, block: int) -> int
     return int(_lib.gdn_conv_workspace_bytes(ctypes.byref(layer.c()), ctypes.byref(v.c), int(block)))
 
 
+def prefill_staging_bytes(layer: Layer, cu_seqlens, start_pos, block: int) -> int:
+    v = _Varlens(cu_seqlens, start_pos)
+    return int(_lib.gdn_prefill_staging_bytes(ctypes.byref(layer.c()), ctypes.byref(v.c), int(block)))
+
+
+def conv_staging_bytes(layer: Layer, cu_seqlens, start_pos, block: int) -> int:
+    v = _Varlens(cu_seqlens, start_pos)
+    return int(_lib.gdn_conv_staging_bytes(ctypes.byref(layer.c()), ctypes.byref(v.c), int(block)))
+
+
+def pinned_staging(nbytes: int) -> torch.Tensor:
+    """A pinned host buffer for gdn_staging (keep it untouched until the stream has passed
+    the call that used it)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, pin_memory=True)
+
+
+def _staging(need: int, staging):
+    """(struct pointer or None, wait): a call whose tables exceed the kernel arguments
+    needs a staging buffer.  Without one from the caller, a pinned buffer is made here and
+    the binding waits for the stream after the call, so that the buffer outlives the
+    copy that reads it (the synchronous convenience path)."""
+    if need <= 0:
+        return None, None, False
+    own = staging is None
+    if own:
+        staging = pinned_staging(need)
+    _need(staging.device.type == "cpu" and staging.dtype == torch.uint8 and staging.is_contiguous(),
+          "staging must be a contiguous uint8 host tensor (pin_memory=True)")
+    st = _Staging(staging.data_ptr(), staging.numel())
+    return st, staging, own
+
+
 def _workspace(nbytes: int, device, workspace):
     if workspace is not None:
         return workspace
@@ -286,7 +337,7 @@ def _workspace(nbytes: int, device, workspace):
 # ------------------------------------------------------------------ the hot path
 
 def conv_update(layer: Layer, x, w, tails, cu_seqlens, start_pos, y, ckpt=None, page_ids=None,
-                workspace=None, stream=None):
+                workspace=None, stream=None, staging=None):
     """Causal conv update (gdn_conv_update). tails: per sequence (kind, src, dst)."""
     v = _Varlens(cu_seqlens, start_pos)
     rows = int(cu_seqlens[-1]) if len(cu_seqlens) else 0
@@ -303,10 +354,35 @@ def conv_update(layer: Layer, x, w, tails, cu_seqlens, start_pos, y, ckpt=None, 
     ws = _workspace(conv_workspace_bytes(layer, cu_seqlens, start_pos, block), x.device, workspace)
     ck, keep = _ckpt_c(ckpt, page_ids)
     refs = _refs(tails)
+    sg, sg_keep, wait = _staging(conv_staging_bytes(layer, cu_seqlens, start_pos, block), staging)
     st = _lib.gdn_conv_update(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(v.c), _ptr(x), _ptr(w),
-                              refs, ctypes.byref(ck), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0)
+                              refs, ctypes.byref(ck), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0,
+                              ctypes.byref(sg) if sg is not None else None)
     _check(st, "gdn_conv_update")
+    if wait:
+        _sync(stream)
     return ws
+
+
+def conv_decode(layer: Layer, x, w, tail_pool, slot_ids, y, rows=None, status=None, stream=None):
+    """The conv's decode regime (gdn_conv_decode): request r's new row is row rows[r] (or
+    r) of x [n_rows, C]; its previous rows are slot slot_ids[r] of tail_pool [n_slots,
+    conv_width - 1, C], updated in place; y row rows[r] gets the conv output."""
+    n_req = int(slot_ids.numel())
+    C = layer.conv_channels
+    n_rows = int(x.shape[0])
+    _need(slot_ids.dtype == torch.int32 and (rows is None or (rows.dtype == torch.int32 and rows.numel() >= n_req)),
+          "int32 slot_ids / rows")
+    _rows_ok(x, n_rows, C, layer.io_dtype, "x")
+    _rows_ok(y, n_rows, C, layer.io_dtype, "y")
+    _rows_ok(w, C, layer.conv_width, layer.io_dtype, "w")
+    _need(rows is not None or n_rows >= n_req, "x: one row per request")
+    _need(tail_pool.dtype == layer.io_dtype and tail_pool.is_contiguous()
+          and tuple(tail_pool.shape[1:]) == (layer.conv_width - 1, C), "tail_pool: [slots, conv_width - 1, C]")
+    st = _lib.gdn_conv_decode(ctypes.byref(layer.c()), _stream(stream), n_req, n_rows, _ptr(x), _ptr(w),
+                              _ptr(tail_pool), int(tail_pool.shape[0]), _ptr(slot_ids), _ptr(rows), _ptr(y),
+                              _ptr(status))
+    _check(st, "gdn_conv_decode")
 
 
 def _check_prefill_operands(layer, cu_seqlens, start_pos, q, k, v, a, b, o, states, qs, vs):
@@ -334,7 +410,7 @@ def _check_prefill_operands(layer, cu_seqlens, start_pos, q, k, v, a, b, o, stat
 
 
 def chunk_prefill(layer: Layer, q, k, v, a, b, cu_seqlens, start_pos, states, o, ckpt=None, page_ids=None,
-                  workspace=None, stream=None, qk_stride=None, v_stride=None):
+                  workspace=None, stream=None, qk_stride=None, v_stride=None, staging=None):
     """Chunked varlen prefill with block checkpoints (gdn_chunk_prefill).
     states: per sequence (kind, src, dst)."""
     vl = _Varlens(cu_seqlens, start_pos)
@@ -345,37 +421,47 @@ def chunk_prefill(layer: Layer, q, k, v, a, b, cu_seqlens, start_pos, states, o,
     ws = _workspace(prefill_workspace_bytes(layer, cu_seqlens, start_pos, block), q.device, workspace)
     ck, keep = _ckpt_c(ckpt, page_ids)
     refs = _refs(states)
+    sg, sg_keep, wait = _staging(prefill_staging_bytes(layer, cu_seqlens, start_pos, block), staging)
     st = _lib.gdn_chunk_prefill(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(vl.c), _ptr(q), _ptr(k),
                                 _ptr(v), qs, vs, _ptr(a), _ptr(b), refs, ctypes.byref(ck), _ptr(o), _ptr(ws),
-                                ws.numel() if ws is not None else 0)
+                                ws.numel() if ws is not None else 0, ctypes.byref(sg) if sg is not None else None)
     _check(st, "gdn_chunk_prefill")
+    if wait:
+        _sync(stream)
     return ws
 
 
 def prefill_factorize(layer: Layer, q, k, a, b, cu_seqlens, start_pos, block, workspace, stream=None,
-                      qk_stride=None):
+                      qk_stride=None, staging=None):
     vl = _Varlens(cu_seqlens, start_pos)
     qs = qk_stride if qk_stride is not None else layer.n_qk_heads * layer.head_dim
     _check_prefill_operands(layer, cu_seqlens, start_pos, q, k, None, a, b, None,
                             [("zero", None, None)] * len(start_pos), qs, 0)
+    sg, sg_keep, wait = _staging(prefill_staging_bytes(layer, cu_seqlens, start_pos, block), staging)
     st = _lib.gdn_prefill_factorize(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(vl.c), _ptr(q),
                                     _ptr(k), qs, _ptr(a), _ptr(b), int(block), _ptr(workspace),
-                                    workspace.numel())
+                                    workspace.numel(), ctypes.byref(sg) if sg is not None else None)
     _check(st, "gdn_prefill_factorize")
+    if wait:
+        _sync(stream)
 
 
 def prefill_scan(layer: Layer, q, k, v, cu_seqlens, start_pos, states, o, workspace, ckpt=None, page_ids=None,
-                 stream=None, qk_stride=None, v_stride=None):
+                 stream=None, qk_stride=None, v_stride=None, staging=None):
     vl = _Varlens(cu_seqlens, start_pos)
     ck, keep = _ckpt_c(ckpt, page_ids)
     refs = _refs(states)
     qs = qk_stride if qk_stride is not None else layer.n_qk_heads * layer.head_dim
     vs = v_stride if v_stride is not None else layer.n_v_heads * layer.head_dim
     _check_prefill_operands(layer, cu_seqlens, start_pos, q, k, v, None, None, o, states, qs, vs)
+    block = ckpt.block if ckpt is not None else 0
+    sg, sg_keep, wait = _staging(prefill_staging_bytes(layer, cu_seqlens, start_pos, block), staging)
     st = _lib.gdn_prefill_scan(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(vl.c), _ptr(q), _ptr(k),
                                _ptr(v), qs, vs, refs, ctypes.byref(ck), _ptr(o), _ptr(workspace),
-                               workspace.numel())
+                               workspace.numel(), ctypes.byref(sg) if sg is not None else None)
     _check(st, "gdn_prefill_scan")
+    if wait:
+        _sync(stream)
 
 
 def decode_step(layer: Layer, q, k, v, a, b, state_pool, slot_ids, o, status=None, stream=None):

@@ -384,18 +384,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
 #endif
 }
 
-// A chunk descriptor read through the constant address space: a wave-uniform address
-// there becomes a scalar load (SMEM, counted by lgkmcnt), so waiting for it never waits
-// for the vector loads in flight, and the fields land in SGPRs.  The table is not
-// written while a kernel runs.
-__device__ __forceinline__ ChunkDesc uniform_chunk(const ChunkDesc* cdp) {
-  const auto* cp = (const __attribute__((address_space(4))) ChunkDesc*)cdp;
-  ChunkDesc d;
-  d.row = cp->row;
-  d.len = cp->len;
-  d.page = cp->page;
-  return d;
-}
+// A wave-uniform fp32 through the constant address space: a scalar load into an SGPR.
 __device__ __forceinline__ float uniform_load(const float* p) {
   return *(const __attribute__((address_space(4))) float*)p;
 }

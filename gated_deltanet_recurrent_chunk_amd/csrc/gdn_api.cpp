@@ -1,22 +1,15 @@
 // gdn_api.cpp -- the extern "C" entry points of libgdn (see include/gdn.h).
 //
 // Each call validates everything it can on the host (plan.cpp) before anything is
-// enqueued, uploads the small per-call tables (chunk grid, per-sequence pointers,
-// checkpoint page ids) into the caller's workspace, and launches the kernels.
-//
-// Table uploads go through one pinned host staging ring per process (allocated on
-// first use and kept): a table is copied into the ring and an asynchronous copy is
-// enqueued on the caller's stream, followed by an event; a ring region is reused only
-// after the event that last covered it has completed.  This keeps every call
-// asynchronous with respect to the host.  The events skip the system-scope fence: they
-// only tell the host that a copy has finished reading the ring, and the fence's cache
-// writeback and invalidation would delay the kernel that follows and start it with cold
-// caches.  Completed events are kept and reused.
+// enqueued, then launches its kernels.  The prefill and conv kernels take the call's
+// table -- one entry per sequence plus the checkpoint page ids -- inside their kernel
+// arguments; a table too large for that is written into the caller's pinned staging
+// buffer and copied from there into the caller's workspace on the call's stream.  The
+// library holds no memory and no state between calls, so calls on different streams
+// never wait for each other.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
-#include <deque>
-#include <mutex>
 #include <vector>
 
 #include "../../include/gdn.h"
@@ -26,72 +19,6 @@
 using namespace gdn;
 
 namespace {
-
-constexpr size_t kRingBytes = (size_t)32 << 20;
-
-struct StagingRing {
-  std::mutex mu;
-  uint8_t* base = nullptr;
-  size_t head = 0;
-  struct Seg {
-    size_t off, len;
-    hipEvent_t ev;
-  };
-  std::deque<Seg> live;
-  std::vector<hipEvent_t> spare;
-};
-StagingRing g_ring;
-
-hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
-  if (bytes == 0) return hipSuccess;
-  std::lock_guard<std::mutex> lock(g_ring.mu);
-  if (bytes > kRingBytes) {
-    // larger than the whole ring: a plain copy that completes before the call returns
-    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return e;
-    return hipStreamSynchronize(stream);
-  }
-  if (!g_ring.base) {
-    void* p = nullptr;
-    hipError_t e = hipHostMalloc(&p, kRingBytes, hipHostMallocPortable);
-    if (e != hipSuccess) return e;
-    g_ring.base = static_cast<uint8_t*>(p);
-    g_ring.head = 0;
-  }
-  size_t off = align_up(g_ring.head);
-  if (off + bytes > kRingBytes) off = 0;
-  for (auto it = g_ring.live.begin(); it != g_ring.live.end();) {
-    const bool overlap = !(it->off + it->len <= off || off + bytes <= it->off);
-    if (overlap) {
-      hipError_t e = hipEventSynchronize(it->ev);
-      if (e != hipSuccess) return e;
-    } else if (hipEventQuery(it->ev) != hipSuccess) {
-      ++it;
-      continue;
-    }
-    g_ring.spare.push_back(it->ev);
-    it = g_ring.live.erase(it);
-  }
-  std::memcpy(g_ring.base + off, src, bytes);
-  hipError_t e = hipMemcpyAsync(dst, g_ring.base + off, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return e;
-  hipEvent_t ev;
-  if (!g_ring.spare.empty()) {
-    ev = g_ring.spare.back();
-    g_ring.spare.pop_back();
-  } else {
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
-    if (e != hipSuccess) return e;
-  }
-  e = hipEventRecord(ev, stream);
-  if (e != hipSuccess) {
-    g_ring.spare.push_back(ev);
-    return e;
-  }
-  g_ring.live.push_back({off, bytes, ev});
-  g_ring.head = off + bytes;
-  return hipSuccess;
-}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p) % a == 0; }
 
@@ -120,7 +47,7 @@ struct PrefillPrep {
   LayerInfo L;
   std::vector<SeqSpan> spans;
   std::vector<int32_t> pages, page_begin;
-  PrefillPlan plan;
+  CallPlan plan;
 };
 
 gdn_status prep_prefill(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block, const gdn_ckpt* ckpt,
@@ -134,9 +61,8 @@ gdn_status prep_prefill(const gdn_layer* layer, const gdn_varlen* varlen, int32_
     s = check_ckpt(ckpt, P->L, P->spans, &P->pages, &P->page_begin);
     if (s != GDN_OK) return s;
   }
-  plan_prefill(P->L, P->spans, block, ckpt ? &P->pages : nullptr, ckpt ? &P->page_begin : nullptr, &P->plan);
-  if (P->plan.chunks.size() > (size_t)INT32_MAX) return GDN_ERR_CAPACITY;
-  return GDN_OK;
+  return plan_call(P->L, P->spans, block, ckpt ? &P->pages : nullptr, ckpt ? &P->page_begin : nullptr, true,
+                   &P->plan);
 }
 
 gdn_status check_workspace(void* ws, size_t ws_bytes, size_t need) {
@@ -145,11 +71,26 @@ gdn_status check_workspace(void* ws, size_t ws_bytes, size_t need) {
   return GDN_OK;
 }
 
+gdn_status check_staging(const CallPlan& plan, const gdn_staging* staging) {
+  if (!plan.staged) return GDN_OK;
+  if (!staging || !staging->host || staging->bytes < plan.table_bytes) return GDN_ERR_STAGING;
+  return GDN_OK;
+}
+
+// A staged table: written into the caller's staging buffer, then copied on the stream
+// into the table region at the start of the workspace.  The caller keeps the staging
+// buffer untouched until the stream has passed this copy.
+gdn_status stage_table(const CallPlan& plan, const gdn_staging* staging, void* ws, hipStream_t stream) {
+  if (!plan.staged) return GDN_OK;
+  staged_table(plan, static_cast<uint8_t*>(staging->host));
+  return hip_status(hipMemcpyAsync(ws, staging->host, plan.table_bytes, hipMemcpyHostToDevice, stream));
+}
+
 template <typename IO>
 gdn_status do_factorize(const PrefillPrep& P, hipStream_t stream, const void* q, const void* k, int64_t qk_stride,
                         const float* a, const float* b, void* ws) {
   FactorizeArgs<IO> fa;
-  fa.chunks = reinterpret_cast<const ChunkDesc*>(static_cast<uint8_t*>(ws) + P.plan.off_chunks);
+  fill_call_table(P.plan, ws, &fa.tab);
   fa.q = static_cast<const IO*>(q);
   fa.k = static_cast<const IO*>(k);
   fa.qk_stride = qk_stride;
@@ -157,29 +98,24 @@ gdn_status do_factorize(const PrefillPrep& P, hipStream_t stream, const void* q,
   fa.b = b;
   fa.factors = static_cast<uint8_t*>(ws) + P.plan.off_factors;
   fa.factor_stride = P.plan.factor_stride;
-  fa.n_chunks = (int32_t)P.plan.chunks.size();
   fa.Hv = P.L.Hv;
   fa.group = P.L.Hv / P.L.Hqk;
   fa.scale = P.L.scale;
-  return hip_status(launch_factorize(fa, P.L.D, fa.n_chunks, stream));
+  return hip_status(launch_factorize(fa, P.L.D, stream));
 }
 
 template <typename IO>
 gdn_status do_scan(const PrefillPrep& P, hipStream_t stream, const void* q, const void* k, const void* v,
                    int64_t qk_stride, int64_t v_stride, const gdn_ckpt* ckpt, float* o, void* ws) {
   ScanArgs<IO> sa;
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  sa.chunks = reinterpret_cast<const ChunkDesc*>(w + P.plan.off_chunks);
-  sa.seqs = reinterpret_cast<const ScanSeq*>(w + P.plan.off_seqs);
+  fill_call_table(P.plan, ws, &sa.tab);
   sa.q = static_cast<const IO*>(q);
   sa.k = static_cast<const IO*>(k);
   sa.v = static_cast<const IO*>(v);
   sa.qk_stride = qk_stride;
   sa.v_stride = v_stride;
-  sa.factors = w + P.plan.off_factors;
+  sa.factors = static_cast<uint8_t*>(ws) + P.plan.off_factors;
   sa.factor_stride = P.plan.factor_stride;
-  sa.n_chunks = (int32_t)P.plan.chunks.size();
-  sa.n_seqs = (int32_t)P.spans.size();
   sa.Hv = P.L.Hv;
   sa.group = P.L.Hv / P.L.Hqk;
   sa.o = o;
@@ -188,24 +124,13 @@ gdn_status do_scan(const PrefillPrep& P, hipStream_t stream, const void* q, cons
   return hip_status(launch_scan(sa, P.L.D, stream));
 }
 
-// Host image of the chunk table and, when states != null, of the sequence table.
-std::vector<uint8_t> prefill_tables(const PrefillPrep& P, const gdn_state_ref* states, bool with_seqs) {
-  const size_t bytes = with_seqs ? P.plan.off_factors : P.plan.off_seqs;
-  std::vector<uint8_t> buf(bytes, 0);
-  if (!P.plan.chunks.empty())
-    std::memcpy(buf.data() + P.plan.off_chunks, P.plan.chunks.data(), P.plan.chunks.size() * sizeof(ChunkDesc));
-  if (with_seqs) {
-    ScanSeq* sq = reinterpret_cast<ScanSeq*>(buf.data() + P.plan.off_seqs);
-    for (size_t s = 0; s < P.spans.size(); ++s) {
-      const gdn_state_ref& r = states[s];
-      sq[s].src = r.src_kind == GDN_SRC_ZERO ? nullptr : static_cast<const float*>(r.src);
-      sq[s].dst = static_cast<float*>(r.dst);
-      sq[s].chunk_begin = P.plan.seq_chunk_begin[s];
-      sq[s].chunk_end = P.plan.seq_chunk_begin[s + 1];
-      sq[s].pad0 = sq[s].pad1 = 0;
-    }
+// The state references of the scan go into the table entries.
+void set_state_refs(PrefillPrep* P, const gdn_state_ref* states) {
+  for (size_t s = 0; s < P->spans.size(); ++s) {
+    const gdn_state_ref& r = states[s];
+    P->plan.seqs[s].src = r.src_kind == GDN_SRC_ZERO ? nullptr : r.src;
+    P->plan.seqs[s].dst = r.dst;
   }
-  return buf;
 }
 
 gdn_status check_states(const PrefillPrep& P, const gdn_state_ref* states, int32_t block) {
@@ -274,6 +199,7 @@ const char* gdn_status_string(gdn_status s) {
     case GDN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case GDN_ERR_HIP: return "HIP runtime error";
     case GDN_ERR_BAD_SOURCE: return "unknown state source kind";
+    case GDN_ERR_STAGING: return "the call's tables need a pinned host staging buffer (missing or too small)";
   }
   return "unknown status";
 }
@@ -321,30 +247,56 @@ int64_t gdn_prefill_workspace_bytes(const gdn_layer* layer, const gdn_varlen* va
   return (int64_t)P.plan.total_bytes;
 }
 
+int64_t gdn_prefill_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block) {
+  PrefillPrep P;
+  if (prep_prefill(layer, varlen, block, nullptr, &P) != GDN_OK) return -1;
+  return (int64_t)P.plan.table_bytes;
+}
+
+namespace {
+gdn_status prep_conv(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block, const gdn_ckpt* ckpt,
+                     LayerInfo* L, std::vector<SeqSpan>* spans, CallPlan* plan) {
+  gdn_status s = check_layer(layer, L);
+  if (s != GDN_OK) return s;
+  s = check_varlen(varlen, spans);
+  if (s != GDN_OK) return s;
+  if (block < 0) return GDN_ERR_BAD_SHAPE;
+  std::vector<int32_t> pages, page_begin;
+  if (ckpt) {
+    s = check_ckpt(ckpt, *L, *spans, &pages, &page_begin);
+    if (s != GDN_OK) return s;
+  }
+  return plan_call(*L, *spans, block, ckpt ? &pages : nullptr, ckpt ? &page_begin : nullptr, false, plan);
+}
+}  // namespace
+
 int64_t gdn_conv_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block) {
   LayerInfo L;
   std::vector<SeqSpan> spans;
-  if (check_layer(layer, &L) != GDN_OK || check_varlen(varlen, &spans) != GDN_OK || block < 0) return -1;
-  size_t n_pages = 0;
-  for (auto& sp : spans) n_pages += (size_t)count_boundaries(sp.p0, sp.len, block);
-  ConvPlan plan;
-  plan_conv(spans, n_pages, &plan);
-  return (int64_t)plan.total_bytes;
+  CallPlan plan;
+  if (prep_conv(layer, varlen, block, nullptr, &L, &spans, &plan) != GDN_OK) return -1;
+  return (int64_t)plan.table_bytes;
+}
+
+int64_t gdn_conv_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block) {
+  return gdn_conv_workspace_bytes(layer, varlen, block);
 }
 
 gdn_status gdn_prefill_factorize(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
                                  const void* q, const void* k, int64_t qk_stride, const float* a, const float* b,
-                                 int32_t block, void* workspace, size_t workspace_bytes) {
+                                 int32_t block, void* workspace, size_t workspace_bytes,
+                                 const gdn_staging* staging) {
   PrefillPrep P;
   gdn_status s = prep_prefill(layer, varlen, block, nullptr, &P);
   if (s != GDN_OK) return s;
   s = check_qkv(P.L, q, k, nullptr, qk_stride, 0, true, false);
   if (s != GDN_OK) return s;
-  if (!P.plan.chunks.empty() && (!a || !b)) return GDN_ERR_NULL_ARG;
+  if (P.plan.n_units > 0 && (!a || !b)) return GDN_ERR_NULL_ARG;
   s = check_workspace(workspace, workspace_bytes, P.plan.total_bytes);
   if (s != GDN_OK) return s;
-  std::vector<uint8_t> tab = prefill_tables(P, nullptr, false);
-  s = hip_status(upload(workspace, tab.data(), tab.size(), stream));
+  s = check_staging(P.plan, staging);
+  if (s != GDN_OK) return s;
+  s = stage_table(P.plan, staging, workspace, stream);
   if (s != GDN_OK) return s;
   return P.L.io == GDN_BF16 ? do_factorize<bf16_bits>(P, stream, q, k, qk_stride, a, b, workspace)
                             : do_factorize<float>(P, stream, q, k, qk_stride, a, b, workspace);
@@ -353,20 +305,22 @@ gdn_status gdn_prefill_factorize(const gdn_layer* layer, hipStream_t stream, con
 gdn_status gdn_prefill_scan(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen, const void* q,
                             const void* k, const void* v, int64_t qk_stride, int64_t v_stride,
                             const gdn_state_ref* states, const gdn_ckpt* ckpt, float* o, void* workspace,
-                            size_t workspace_bytes) {
+                            size_t workspace_bytes, const gdn_staging* staging) {
   if (!ckpt) return GDN_ERR_NULL_ARG;
   PrefillPrep P;
   gdn_status s = prep_prefill(layer, varlen, ckpt->block, ckpt, &P);
   if (s != GDN_OK) return s;
   s = check_qkv(P.L, q, k, v, qk_stride, v_stride, true, true);
   if (s != GDN_OK) return s;
-  if (!o && !P.plan.chunks.empty()) return GDN_ERR_NULL_ARG;
+  if (!o && P.plan.n_units > 0) return GDN_ERR_NULL_ARG;
   s = check_states(P, states, ckpt->block);
   if (s != GDN_OK) return s;
   s = check_workspace(workspace, workspace_bytes, P.plan.total_bytes);
   if (s != GDN_OK) return s;
-  std::vector<uint8_t> tab = prefill_tables(P, states, true);
-  s = hip_status(upload(workspace, tab.data(), tab.size(), stream));
+  s = check_staging(P.plan, staging);
+  if (s != GDN_OK) return s;
+  set_state_refs(&P, states);
+  s = stage_table(P.plan, staging, workspace, stream);
   if (s != GDN_OK) return s;
   return P.L.io == GDN_BF16 ? do_scan<bf16_bits>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace)
                             : do_scan<float>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
@@ -375,20 +329,22 @@ gdn_status gdn_prefill_scan(const gdn_layer* layer, hipStream_t stream, const gd
 gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen, const void* q,
                              const void* k, const void* v, int64_t qk_stride, int64_t v_stride, const float* a,
                              const float* b, const gdn_state_ref* states, const gdn_ckpt* ckpt, float* o,
-                             void* workspace, size_t workspace_bytes) {
+                             void* workspace, size_t workspace_bytes, const gdn_staging* staging) {
   if (!ckpt) return GDN_ERR_NULL_ARG;
   PrefillPrep P;
   gdn_status s = prep_prefill(layer, varlen, ckpt->block, ckpt, &P);
   if (s != GDN_OK) return s;
   s = check_qkv(P.L, q, k, v, qk_stride, v_stride, true, true);
   if (s != GDN_OK) return s;
-  if (!P.plan.chunks.empty() && (!a || !b || !o)) return GDN_ERR_NULL_ARG;
+  if (P.plan.n_units > 0 && (!a || !b || !o)) return GDN_ERR_NULL_ARG;
   s = check_states(P, states, ckpt->block);
   if (s != GDN_OK) return s;
   s = check_workspace(workspace, workspace_bytes, P.plan.total_bytes);
   if (s != GDN_OK) return s;
-  std::vector<uint8_t> tab = prefill_tables(P, states, true);
-  s = hip_status(upload(workspace, tab.data(), tab.size(), stream));
+  s = check_staging(P.plan, staging);
+  if (s != GDN_OK) return s;
+  set_state_refs(&P, states);
+  s = stage_table(P.plan, staging, workspace, stream);
   if (s != GDN_OK) return s;
   if (P.L.io == GDN_BF16) {
     s = do_factorize<bf16_bits>(P, stream, q, k, qk_stride, a, b, workspace);
@@ -402,20 +358,16 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream, const g
 
 gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen, const void* x,
                            const void* w, const gdn_state_ref* tails, const gdn_ckpt* ckpt, void* y,
-                           void* workspace, size_t workspace_bytes) {
-  LayerInfo L;
-  gdn_status s = check_layer(layer, &L);
-  if (s != GDN_OK) return s;
-  std::vector<SeqSpan> spans;
-  s = check_varlen(varlen, &spans);
-  if (s != GDN_OK) return s;
+                           void* workspace, size_t workspace_bytes, const gdn_staging* staging) {
   if (!ckpt) return GDN_ERR_NULL_ARG;
-  std::vector<int32_t> pages, page_begin;
-  s = check_ckpt(ckpt, L, spans, &pages, &page_begin);
+  LayerInfo L;
+  std::vector<SeqSpan> spans;
+  CallPlan plan;
+  gdn_status s = prep_conv(layer, varlen, ckpt->block, ckpt, &L, &spans, &plan);
   if (s != GDN_OK) return s;
   s = check_sources(tails, spans, ckpt->block);
   if (s != GDN_OK) return s;
-  int64_t total_rows = spans.empty() ? 0 : spans.back().row0 + spans.back().len;
+  const int64_t total_rows = spans.empty() ? 0 : spans.back().row0 + spans.back().len;
   if (total_rows > 0 && (!x || !y)) return GDN_ERR_NULL_ARG;
   if (!w && !spans.empty()) return GDN_ERR_NULL_ARG;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16)) return GDN_ERR_BAD_SHAPE;
@@ -423,68 +375,82 @@ gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn
     if (tails[i].src_kind != GDN_SRC_ZERO && !aligned(tails[i].src, 16)) return GDN_ERR_BAD_SHAPE;
     if (!aligned(tails[i].dst, 16)) return GDN_ERR_BAD_SHAPE;
   }
-  ConvPlan plan;
-  plan_conv(spans, pages.size(), &plan);
-  const std::vector<ConvTile>& tiles = plan.tiles;
-  const size_t off_tiles = plan.off_tiles, off_pages = plan.off_pages, need = plan.total_bytes;
-  if (tiles.size() > (size_t)INT32_MAX) return GDN_ERR_CAPACITY;
-  s = check_workspace(workspace, workspace_bytes, need);
+  if (plan.staged) {
+    s = check_workspace(workspace, workspace_bytes, plan.table_bytes);
+    if (s != GDN_OK) return s;
+  }
+  s = check_staging(plan, staging);
   if (s != GDN_OK) return s;
-  if (tiles.empty()) return GDN_OK;
-  std::vector<uint8_t> buf(need, 0);
-  ConvSeq* cs = reinterpret_cast<ConvSeq*>(buf.data());
+  if (plan.n_units == 0) return GDN_OK;
   for (size_t i = 0; i < spans.size(); ++i) {
     const gdn_state_ref& r = tails[i];
     const uint8_t* src = static_cast<const uint8_t*>(r.src);
     if (r.src_kind == GDN_SRC_ZERO) src = nullptr;
     if (r.src_kind == GDN_SRC_CHECKPOINT) src += L.state_bytes;  // tail region of the page
-    cs[i].src_tail = src;
-    cs[i].dst_tail = r.dst;
-    cs[i].row0 = spans[i].row0;
-    cs[i].p0 = spans[i].p0;
-    cs[i].len = spans[i].len;
-    cs[i].page_begin = page_begin[i];
-    cs[i].pad = 0;
+    plan.seqs[i].src = src;
+    plan.seqs[i].dst = r.dst;
   }
-  std::memcpy(buf.data() + off_tiles, tiles.data(), tiles.size() * sizeof(ConvTile));
-  if (!pages.empty()) std::memcpy(buf.data() + off_pages, pages.data(), pages.size() * sizeof(int32_t));
-  s = hip_status(upload(workspace, buf.data(), buf.size(), stream));
+  s = stage_table(plan, staging, workspace, stream);
   if (s != GDN_OK) return s;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (L.io == GDN_BF16) {
-    ConvArgs<bf16_bits> ca;
-    ca.seqs = reinterpret_cast<const ConvSeq*>(ws);
-    ca.tiles = reinterpret_cast<const ConvTile*>(ws + off_tiles);
-    ca.pages = reinterpret_cast<const int32_t*>(ws + off_pages);
-    ca.x = static_cast<const bf16_bits*>(x);
-    ca.w = static_cast<const bf16_bits*>(w);
-    ca.y = static_cast<bf16_bits*>(y);
+  auto fill = [&](auto& ca, auto tag) {
+    using IO = decltype(tag);
+    fill_call_table(plan, workspace, &ca.tab);
+    ca.x = static_cast<const IO*>(x);
+    ca.w = static_cast<const IO*>(w);
+    ca.y = static_cast<IO*>(y);
     ca.ckpt_pool = static_cast<uint8_t*>(ckpt->pool);
     ca.page_bytes = (size_t)ckpt->page_bytes;
     ca.tail_offset = (size_t)L.state_bytes;
     ca.channels = L.channels;
     ca.qk_channels = 2 * (int64_t)L.Hqk * L.D;
     ca.head_dim = L.D;
-    ca.block = ckpt->block;
     ca.act = L.act;
-    return hip_status(launch_conv(ca, (int)tiles.size(), stream));
+  };
+  if (L.io == GDN_BF16) {
+    ConvArgs<bf16_bits> ca;
+    fill(ca, bf16_bits{});
+    return hip_status(launch_conv(ca, stream));
   }
   ConvArgs<float> ca;
-  ca.seqs = reinterpret_cast<const ConvSeq*>(ws);
-  ca.tiles = reinterpret_cast<const ConvTile*>(ws + off_tiles);
-  ca.pages = reinterpret_cast<const int32_t*>(ws + off_pages);
-  ca.x = static_cast<const float*>(x);
-  ca.w = static_cast<const float*>(w);
-  ca.y = static_cast<float*>(y);
-  ca.ckpt_pool = static_cast<uint8_t*>(ckpt->pool);
-  ca.page_bytes = (size_t)ckpt->page_bytes;
-  ca.tail_offset = (size_t)L.state_bytes;
-  ca.channels = L.channels;
-  ca.qk_channels = 2 * (int64_t)L.Hqk * L.D;
-  ca.head_dim = L.D;
-  ca.block = ckpt->block;
-  ca.act = L.act;
-  return hip_status(launch_conv(ca, (int)tiles.size(), stream));
+  fill(ca, float{});
+  return hip_status(launch_conv(ca, stream));
+}
+
+gdn_status gdn_conv_decode(const gdn_layer* layer, hipStream_t stream, int32_t n_req, int64_t n_rows,
+                           const void* x, const void* w, void* tail_pool, int64_t n_slots, const int32_t* slot_ids,
+                           const int32_t* rows, void* y, int32_t* status) {
+  LayerInfo L;
+  gdn_status s = check_layer(layer, &L);
+  if (s != GDN_OK) return s;
+  if (n_req < 0 || n_slots < 0 || n_rows < 0) return GDN_ERR_BAD_SHAPE;
+  if (n_req == 0) return GDN_OK;
+  if (!x || !w || !tail_pool || !slot_ids || !y) return GDN_ERR_NULL_ARG;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(tail_pool, 16) || !aligned(y, 16)) return GDN_ERR_BAD_SHAPE;
+  if (n_req > 65535) return GDN_ERR_CAPACITY;
+  auto fill = [&](auto& ca, auto tag) {
+    using IO = decltype(tag);
+    ca.x = static_cast<const IO*>(x);
+    ca.w = static_cast<const IO*>(w);
+    ca.y = static_cast<IO*>(y);
+    ca.tail_pool = static_cast<IO*>(tail_pool);
+    ca.slot_ids = slot_ids;
+    ca.rows = rows;
+    ca.status = status;
+    ca.n_slots = n_slots;
+    ca.n_rows = rows ? n_rows : (int64_t)n_req;
+    ca.channels = L.channels;
+    ca.qk_channels = 2 * (int64_t)L.Hqk * L.D;
+    ca.head_dim = L.D;
+    ca.act = L.act;
+  };
+  if (L.io == GDN_BF16) {
+    ConvDecodeArgs<bf16_bits> ca;
+    fill(ca, bf16_bits{});
+    return hip_status(launch_conv_decode(ca, n_req, stream));
+  }
+  ConvDecodeArgs<float> ca;
+  fill(ca, float{});
+  return hip_status(launch_conv_decode(ca, n_req, stream));
 }
 
 gdn_status gdn_decode_step(const gdn_layer* layer, hipStream_t stream, int32_t n_req, const void* q, const void* k,

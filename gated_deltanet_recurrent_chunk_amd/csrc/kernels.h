@@ -2,17 +2,21 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "plan.h"
+
 
 namespace gdn {
 
 typedef uint16_t bf16_bits;
 
+// Argument blocks of the prefill and conv kernels carry the call's table (plan.h) by
+// value: up to kInlineSeqs sequences and kInlinePages checkpoint pages travel inline.
 template <typename IO>
 struct FactorizeArgs {
-  const ChunkDesc* chunks;
+  CallTable tab;  // units = chunks
   const IO* q;
   const IO* k;
   int64_t qk_stride;  // elements per token row of q and k
@@ -20,7 +24,6 @@ struct FactorizeArgs {
   const float* b;
   uint8_t* factors;
   size_t factor_stride;
-  int32_t n_chunks;
   int32_t Hv;
   int32_t group;  // value heads per query/key head
   float scale;
@@ -28,8 +31,7 @@ struct FactorizeArgs {
 
 template <typename IO>
 struct ScanArgs {
-  const ChunkDesc* chunks;
-  const ScanSeq* seqs;
+  CallTable tab;  // units = chunks; src / dst are the states
   const IO* q;
   const IO* k;
   const IO* v;
@@ -37,8 +39,6 @@ struct ScanArgs {
   int64_t v_stride;
   const uint8_t* factors;
   size_t factor_stride;
-  int32_t n_chunks;
-  int32_t n_seqs;
   int32_t Hv;
   int32_t group;
   float* o;
@@ -109,9 +109,7 @@ struct DecodeArgs {
 
 template <typename IO>
 struct ConvArgs {
-  const ConvSeq* seqs;
-  const ConvTile* tiles;
-  const int32_t* pages;
+  CallTable tab;  // units = tiles of kConvTile rows; src / dst are the tails
   const IO* x;
   const IO* w;
   IO* y;
@@ -121,8 +119,24 @@ struct ConvArgs {
   int64_t channels;
   int64_t qk_channels;  // 2 * Hqk * head_dim: the channels normalized per head (flag)
   int32_t head_dim;
-  int32_t block;
   int32_t act;          // gdn_act, optionally | GDN_CONV_QK_L2NORM
+};
+
+template <typename IO>
+struct ConvDecodeArgs {
+  const IO* x;           // row t at x + t * channels
+  const IO* w;           // [channels][4]
+  IO* y;                 // row t at y + t * channels
+  IO* tail_pool;         // [n_slots][3][channels], updated in place
+  const int32_t* slot_ids;
+  const int32_t* rows;   // token row of each request (nullptr: row r)
+  int32_t* status;
+  int64_t n_slots;
+  int64_t n_rows;
+  int64_t channels;
+  int64_t qk_channels;
+  int32_t head_dim;
+  int32_t act;
 };
 
 template <typename IO>
@@ -149,12 +163,21 @@ struct NormArgs {
   float eps;
 };
 
+// Argument blocks stay within 4 KiB, a size every HIP launch path accepts, and carry
+// their table first: kernels read it at offset 0 of the kernel-argument segment.
+static_assert(sizeof(FactorizeArgs<float>) <= 4096 && sizeof(ScanArgs<float>) <= 4096 &&
+                  sizeof(ConvArgs<float>) <= 4096, "kernel argument size");
+static_assert(offsetof(FactorizeArgs<float>, tab) == 0 && offsetof(FactorizeArgs<bf16_bits>, tab) == 0 &&
+                  offsetof(ScanArgs<float>, tab) == 0 && offsetof(ScanArgs<bf16_bits>, tab) == 0 &&
+                  offsetof(ConvArgs<float>, tab) == 0 && offsetof(ConvArgs<bf16_bits>, tab) == 0,
+              "the call table leads every argument block");
+
 hipError_t launch_gates(const GateArgs<bf16_bits>& a, hipStream_t st);
 hipError_t launch_gates(const GateArgs<float>& a, hipStream_t st);
 hipError_t launch_gated_norm(const NormArgs<bf16_bits>& a, int D, hipStream_t st);
 hipError_t launch_gated_norm(const NormArgs<float>& a, int D, hipStream_t st);
-hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, int n_chunks, hipStream_t st);
-hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, int n_chunks, hipStream_t st);
+hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, hipStream_t st);
+hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, hipStream_t st);
 hipError_t launch_scan(const ScanArgs<bf16_bits>& a, int D, hipStream_t st);
 hipError_t launch_scan(const ScanArgs<float>& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs<bf16_bits>& a, int D, int n_req, hipStream_t st);
@@ -163,7 +186,9 @@ hipError_t launch_replay(const ReplayArgs<bf16_bits>& a, int D, int n_req, int c
 hipError_t launch_replay(const ReplayArgs<float>& a, int D, int n_req, int ct, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs<bf16_bits>& a, int D, int n_req, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs<float>& a, int D, int n_req, hipStream_t st);
-hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st);
-hipError_t launch_conv(const ConvArgs<float>& a, int n_tiles, hipStream_t st);
+hipError_t launch_conv(const ConvArgs<bf16_bits>& a, hipStream_t st);
+hipError_t launch_conv_decode(const ConvDecodeArgs<bf16_bits>& a, int n_req, hipStream_t st);
+hipError_t launch_conv_decode(const ConvDecodeArgs<float>& a, int n_req, hipStream_t st);
+hipError_t launch_conv(const ConvArgs<float>& a, hipStream_t st);
 
 }  // namespace gdn

@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <cstring>
 #include <unordered_set>
 
 namespace gdn {
@@ -146,57 +147,76 @@ void chunk_grid(int64_t p0, int64_t len, int32_t block, std::vector<int64_t>* cu
   cuts->push_back(end);
 }
 
-void plan_prefill(const LayerInfo& L, const std::vector<SeqSpan>& spans, int32_t block,
-                  const std::vector<int32_t>* pages, const std::vector<int32_t>* page_begin,
-                  PrefillPlan* plan) {
-  plan->chunks.clear();
-  plan->seq_chunk_begin.assign(spans.size() + 1, 0);
-  std::vector<int64_t> cuts;
+gdn_status plan_call(const LayerInfo& L, const std::vector<SeqSpan>& spans, int32_t block,
+                     const std::vector<int32_t>* pages, const std::vector<int32_t>* page_begin,
+                     bool prefill, CallPlan* plan) {
+  if (block < 0 || block > (1 << 24)) return GDN_ERR_CAPACITY;
+  plan->block = block;
+  plan->lcm = grid_lcm((uint32_t)block);
+  plan->seqs.assign(spans.size(), SeqEntry{});
+  // one page per crossed boundary; without page ids (the factorize stage) the list holds
+  // -1s, so that both prefill stages lay out the workspace the same way
+  int64_t n_bound = 0;
+  for (const SeqSpan& sp : spans) n_bound += count_boundaries(sp.p0, sp.len, block);
+  if (n_bound > (1 << 30)) return GDN_ERR_CAPACITY;
+  if (pages && (int64_t)pages->size() != n_bound) return GDN_ERR_BAD_PAGE;
+  plan->pages = pages ? *pages : std::vector<int32_t>((size_t)n_bound, -1);
+  int64_t units = 0, bound = 0;
   for (size_t s = 0; s < spans.size(); ++s) {
-    plan->seq_chunk_begin[s] = (int32_t)plan->chunks.size();
     const SeqSpan& sp = spans[s];
-    chunk_grid(sp.p0, sp.len, block, &cuts);
-    int64_t b_index = 0;  // crossed boundaries so far in this sequence
-    for (size_t c = 0; c + 1 < cuts.size(); ++c) {
-      ChunkDesc d;
-      d.row = sp.row0 + (cuts[c] - sp.p0);
-      d.len = (int32_t)(cuts[c + 1] - cuts[c]);
-      d.page = -1;
-      if (block > 0 && cuts[c + 1] % block == 0) {
-        if (pages && !pages->empty()) d.page = (*pages)[(size_t)((*page_begin)[s] + b_index)];
-        ++b_index;
-      }
-      plan->chunks.push_back(d);
-    }
+    if (sp.p0 + sp.len >= kMaxPosition || sp.row0 + sp.len > ((int64_t)1 << 40)) return GDN_ERR_CAPACITY;
+    SeqEntry& e = plan->seqs[s];
+    e.row0 = sp.row0;
+    e.p0 = (int32_t)sp.p0;
+    e.len = (int32_t)sp.len;
+    e.unit0 = (int32_t)units;
+    e.n_units = (int32_t)(prefill ? chunk_count((uint32_t)sp.p0, (uint32_t)sp.len, (uint32_t)block, plan->lcm)
+                                  : tile_count((uint32_t)sp.len));
+    e.page0 = page_begin ? (*page_begin)[s] : (int32_t)bound;
+    bound += count_boundaries(sp.p0, sp.len, block);
+    units += e.n_units;
+    if (units > INT32_MAX / 2) return GDN_ERR_CAPACITY;
   }
-  plan->seq_chunk_begin[spans.size()] = (int32_t)plan->chunks.size();
-  const size_t n_chunks = plan->chunks.size();
-  plan->off_chunks = 0;
-  plan->off_seqs = align_up(n_chunks * sizeof(ChunkDesc));
-  plan->off_factors = plan->off_seqs + align_up(spans.size() * sizeof(ScanSeq));
-  plan->factor_stride = factor_record_bytes(L.ntf, L.nti, L.D);
-  plan->total_bytes = plan->off_factors + plan->factor_stride * n_chunks * (size_t)L.Hv;
+  plan->n_units = (int32_t)units;
+  plan->staged = spans.size() > (size_t)kInlineSeqs || plan->pages.size() > (size_t)kInlinePages;
+  plan->off_pages = align_up(spans.size() * sizeof(SeqEntry));
+  plan->off_unit_seq = plan->off_pages + align_up(plan->pages.size() * sizeof(int32_t));
+  plan->table_bytes = plan->staged ? plan->off_unit_seq + align_up((size_t)units * sizeof(int32_t)) : 0;
+  // the workspace always reserves the staged table's room, so that its size does not
+  // depend on how the table travels
+  const size_t table_room = plan->off_unit_seq + align_up((size_t)units * sizeof(int32_t));
+  plan->off_factors = table_room;
+  plan->factor_stride = prefill ? factor_record_bytes(L.ntf, L.nti, L.D) : 0;
+  plan->total_bytes = plan->off_factors + plan->factor_stride * (size_t)units * (size_t)L.Hv;
   if (plan->total_bytes == 0) plan->total_bytes = kAlign;
+  return GDN_OK;
 }
 
-void plan_conv(const std::vector<SeqSpan>& spans, size_t n_pages, ConvPlan* plan) {
-  plan->tiles.clear();
-  for (size_t s = 0; s < spans.size(); ++s) {
-    // a zero-length sequence still gets one empty tile, which passes its tail through
-    if (spans[s].len == 0) plan->tiles.push_back(ConvTile{spans[s].row0, 0, (int32_t)s});
-    for (int64_t r = 0; r < spans[s].len; r += kConvTile) {
-      ConvTile t;
-      t.row = spans[s].row0 + r;
-      t.len = (int32_t)std::min<int64_t>(kConvTile, spans[s].len - r);
-      t.seq = (int32_t)s;
-      plan->tiles.push_back(t);
-    }
+void staged_table(const CallPlan& plan, uint8_t* out) {
+  std::memset(out, 0, plan.table_bytes);
+  std::memcpy(out, plan.seqs.data(), plan.seqs.size() * sizeof(SeqEntry));
+  if (!plan.pages.empty()) std::memcpy(out + plan.off_pages, plan.pages.data(), plan.pages.size() * sizeof(int32_t));
+  int32_t* us = reinterpret_cast<int32_t*>(out + plan.off_unit_seq);
+  for (size_t s = 0; s < plan.seqs.size(); ++s)
+    for (int32_t u = 0; u < plan.seqs[s].n_units; ++u) us[plan.seqs[s].unit0 + u] = (int32_t)s;
+}
+
+void fill_call_table(const CallPlan& plan, const void* ws, CallTable* t) {
+  std::memset(t, 0, sizeof(CallTable));
+  t->n_seqs = (int32_t)plan.seqs.size();
+  t->n_pages = (int32_t)plan.pages.size();
+  t->n_units = plan.n_units;
+  t->block = plan.block;
+  t->lcm = plan.lcm;
+  if (plan.staged) {
+    const uint8_t* w = static_cast<const uint8_t*>(ws);
+    t->seqs = reinterpret_cast<const SeqEntry*>(w);
+    t->pages = reinterpret_cast<const int32_t*>(w + plan.off_pages);
+    t->unit_seq = reinterpret_cast<const int32_t*>(w + plan.off_unit_seq);
+  } else {
+    if (!plan.seqs.empty()) std::memcpy(t->inl_seqs, plan.seqs.data(), plan.seqs.size() * sizeof(SeqEntry));
+    if (!plan.pages.empty()) std::memcpy(t->inl_pages, plan.pages.data(), plan.pages.size() * sizeof(int32_t));
   }
-  plan->off_seqs = 0;
-  plan->off_tiles = align_up(spans.size() * sizeof(ConvSeq));
-  plan->off_pages = plan->off_tiles + align_up(plan->tiles.size() * sizeof(ConvTile));
-  plan->total_bytes = plan->off_pages + align_up(n_pages * sizeof(int32_t));
-  if (plan->total_bytes == 0) plan->total_bytes = kAlign;
 }
 
 }  // namespace gdn

@@ -29,6 +29,7 @@
 // of a chunk requests the operands of the next phase before it computes.
 #include <hip/hip_runtime.h>
 
+#include "call_table.h"
 #include "chunk_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -79,9 +80,9 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // around every access).
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(join_address(lo, hi));
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ u32x2 ld8(rsrc_t r, uint32_t off) {
@@ -473,7 +474,11 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
 
   const int h = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const ChunkDesc cd = uniform_chunk(p.chunks + c);
+  // this chunk's rows, from its sequence's table entry
+  const_table* tab = kernarg_table();
+  const SeqEntry se = seq_entry(tab, unit_sequence(tab, c));
+  const uint32_t start = chunk_start((uint32_t)se.p0, (uint32_t)(c - se.unit0), (uint32_t)tab->block, tab->lcm);
+  const ChunkPos cd = chunk_at(se, start, (uint32_t)tab->block);
   const int n = cd.len;
   const int hk = h / p.group;
   uint8_t* rec = p.factors + ((size_t)c * p.Hv + h) * p.factor_stride;
@@ -584,18 +589,21 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
 
   // All slabs of one (sequence, head) go to the same XCD (workgroups are dealt to the
   // eight XCDs round robin), so their shared chunk operands meet in one L2.
-  const int blk = blockIdx.x;
-  const int u = (blk / (8 * NS)) * 8 + (blk & 7);
-  const int sl = (blk >> 3) % NS;
-  if (u >= p.n_seqs * p.Hv) return;
+  const int bid = blockIdx.x;
+  const int u = (bid / (8 * NS)) * 8 + (bid & 7);
+  const int sl = (bid >> 3) % NS;
+  const_table* tab = kernarg_table();
+  if (u >= tab->n_seqs * p.Hv) return;
   const int seq = u / p.Hv, h = u - seq * p.Hv;
   const int hk = h / p.group;
   const int w = NSP == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
   const int my_row = 16 * sl + col;
-  const auto* sqp = (const __attribute__((address_space(4))) ScanSeq*)(p.seqs + seq);  // scalar loads
-  const ScanSeq sq{sqp->src, sqp->dst, sqp->chunk_begin, sqp->chunk_end, 0, 0};
-  const int cb = sq.chunk_begin, ce = sq.chunk_end;
+  const SeqEntry se = seq_entry(tab, seq);
+  const float* sq_src = static_cast<const float*>(se.src);
+  float* sq_dst = static_cast<float*>(se.dst);
+  const int cb = se.unit0, ce = se.unit0 + se.n_units;
+  const uint32_t blk = (uint32_t)tab->block;
   const size_t head_off = (size_t)h * D * D;
   const int jt0 = DTH * w, s0 = KSH * w;  // first state tile and k-step of this wave
   const int mt0 = MR * w;                 // first output row tile of this wave
@@ -603,8 +611,8 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
   f32x4 S[DTH];
 #pragma unroll
   for (int j = 0; j < DTH; ++j) {
-    if (sq.src)
-      S[j] = *reinterpret_cast<const f32x4*>(sq.src + head_off + (size_t)my_row * D + kcol<D>(jt0 + j, grp));
+    if (sq_src)
+      S[j] = *reinterpret_cast<const f32x4*>(sq_src + head_off + (size_t)my_row * D + kcol<D>(jt0 + j, grp));
     else
       S[j] = zero4();
   }
@@ -613,7 +621,7 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
     for (int j = 0; j < DTH; ++j) *reinterpret_cast<f32x4*>(dst + kcol<D>(jt0 + j, grp)) = S[j];
   };
   if (cb >= ce) {
-    store_state(sq.dst + head_off + (size_t)my_row * D);
+    store_state(sq_dst + head_off + (size_t)my_row * D);
     return;
   }
 
@@ -641,7 +649,7 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
   bf16x8 Tf[kFragCombos][NTF], Pf[MR][2][NTF], KTf[DTH][2][NTI];
   float egn;
 
-  auto load_A = [&](const ChunkDesc& cd) {
+  auto load_A = [&](const ChunkPos& cd) {
     const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
     const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
 #pragma unroll
@@ -652,7 +660,7 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
         Qop[mt][s] = load_row_op<IO, D>(rq, kq_off[mt], s0 + s);
       }
   };
-  auto load_B = [&](const ChunkDesc& cd, int c) {
+  auto load_B = [&](const ChunkPos& cd, int c) {
     // one descriptor for the chunk's rows: the tile row goes into the offset, so the
     // descriptor's length bounds every row
     const rsrc_t rv = make_rsrc(p.v + cd.row * p.v_stride + (int64_t)h * D + 16 * sl, (uint32_t)cd.len * vsb);
@@ -702,14 +710,15 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
   // One phase of lookahead: each phase first requests the operands of the next one
   // (the last phase those of the next chunk's first), then computes.  About 20-40
   // vector loads are in flight at a time, within the 63 the wave's counter tracks.
-  ChunkDesc cur = uniform_chunk(p.chunks + cb);
+  uint32_t pos = (uint32_t)se.p0;
+  ChunkPos cur = chunk_at(se, pos, blk);
   load_A(cur);
 
 #pragma unroll 1
   for (int c = cb; c < ce; ++c) {
     // the next chunk (the last one loads itself again: in bounds, and unused)
-    const int cn = __builtin_amdgcn_readfirstlane(c + 1 < ce ? c + 1 : c);
-    const ChunkDesc nxt = uniform_chunk(p.chunks + cn);
+    const uint32_t npos = c + 1 < ce ? pos + (uint32_t)cur.len : pos;
+    const ChunkPos nxt = chunk_at(se, npos, blk);
 
     // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains
     load_B(cur, c);
@@ -815,12 +824,16 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
     }
 
     // ---- checkpoint: the state after this chunk, bit for bit
-    if (cur.page >= 0)
-      store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)cur.page * p.page_bytes) + head_off +
-                  (size_t)my_row * D);
+    if (cur.page_index >= 0) {
+      const int32_t pid = *((const const_i32*)page_list(tab) + cur.page_index);
+      if (pid >= 0)
+        store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)pid * p.page_bytes) + head_off +
+                    (size_t)my_row * D);
+    }
     cur = nxt;
+    pos = npos;
   }
-  store_state(sq.dst + head_off + (size_t)my_row * D);
+  store_state(sq_dst + head_off + (size_t)my_row * D);
 }
 
 // ==================================================================================
@@ -895,9 +908,12 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   const int sl = SP * sg + jj;
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
   const int my_row = 16 * sl + col;
-  const auto* sqp = (const __attribute__((address_space(4))) ScanSeq*)(p.seqs + seq);  // scalar loads
-  const ScanSeq sq{sqp->src, sqp->dst, sqp->chunk_begin, sqp->chunk_end, 0, 0};
-  const int cb = sq.chunk_begin, ce = sq.chunk_end;
+  const_table* tab = kernarg_table();
+  const SeqEntry se = seq_entry(tab, seq);
+  const float* sq_src = static_cast<const float*>(se.src);
+  float* sq_dst = static_cast<float*>(se.dst);
+  const int cb = se.unit0, ce = se.unit0 + se.n_units;
+  const uint32_t blk = (uint32_t)tab->block;
   const size_t head_off = (size_t)h * D * D;
   constexpr int jt0 = DTH * w, s0 = KSH * w;  // first state tile and k-step of this wave
   constexpr int mt0 = MR * w;                 // first output row tile of this wave
@@ -905,8 +921,8 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   f32x4 S[DTH];
 #pragma unroll
   for (int j = 0; j < DTH; ++j) {
-    if (sq.src)
-      S[j] = *reinterpret_cast<const f32x4*>(sq.src + head_off + (size_t)my_row * D + kcol<D>(jt0 + j, grp));
+    if (sq_src)
+      S[j] = *reinterpret_cast<const f32x4*>(sq_src + head_off + (size_t)my_row * D + kcol<D>(jt0 + j, grp));
     else
       S[j] = zero4();
   }
@@ -915,7 +931,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     for (int j = 0; j < DTH; ++j) *reinterpret_cast<f32x4*>(dst + kcol<D>(jt0 + j, grp)) = S[j];
   };
   if (cb >= ce) {
-    store_state(sq.dst + head_off + (size_t)my_row * D);
+    store_state(sq_dst + head_off + (size_t)my_row * D);
     return;
   }
 
@@ -935,17 +951,14 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   const int v_byte = (16 * jj + col) * ESZ;
   auto v_rd = [&](int mt) { return V_OFF + 16 * ((v_byte >> 4) ^ ((4 * mt + grp) & (VNP - 1))) + (v_byte & 15); };
 
-  // chunk descriptors: one vector load (every lane the same 16 bytes) a chunk ahead;
-  // a scalar load would make every wait on LDS reads a wait for all of them
-  const rsrc_t rcd = make_rsrc(p.chunks, (uint32_t)p.n_chunks * (uint32_t)sizeof(ChunkDesc));
-  auto chunk_raw = [&](int c) { return ld16(rcd, (uint32_t)c * (uint32_t)sizeof(ChunkDesc), 0); };
-  auto to_desc = [](const u32x4& v) {
-    ChunkDesc d;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(v[0]), hi = __builtin_amdgcn_readfirstlane(v[1]);
-    d.row = (int64_t)(((uint64_t)hi << 32) | lo);
-    d.len = __builtin_amdgcn_readfirstlane(v[2]);
-    d.page = __builtin_amdgcn_readfirstlane(v[3]);
-    return d;
+  // Chunks are derived from the sequence's entry (scalar arithmetic); the checkpoint
+  // page id of a chunk that ends on a block boundary is fetched with a vector load a
+  // chunk ahead (a scalar load would make every wait on LDS reads a wait for it too).
+  // The descriptor bounds the page list, so the unused fetches of chunks that end off a
+  // boundary (index clamped to 0) never leave it.
+  const rsrc_t rpg = make_rsrc(page_list(tab), (uint32_t)tab->n_pages * 4u);
+  auto page_raw = [&](const ChunkPos& cd) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rpg, (uint32_t)(cd.page_index > 0 ? cd.page_index : 0) * 4u, 0, 0);
   };
 
   // ---- copies of chunk c into buffer B: 1 KiB granules g = q, q + NW, ... < G.  A wave
@@ -954,7 +967,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   //      descriptors are in the per-lane offset: lanes past the record or past the
   //      chunk's last row write zeros.
   const IO* v_pair = p.v + (int64_t)h * D + 16 * SP * sg;
-  auto stage_chunk = [&](const ChunkDesc& cd, int c, lds_u8* B) {
+  auto stage_chunk = [&](const ChunkPos& cd, int c, lds_u8* B) {
     const rsrc_t rr = make_rsrc(p.factors + ((size_t)c * p.Hv + h) * p.factor_stride, (uint32_t)Cfg::REC_BYTES);
     const rsrc_t rv = make_rsrc(v_pair + cd.row * p.v_stride, (uint32_t)cd.len * vsb);
 #pragma unroll
@@ -971,7 +984,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
 
   // copies of the chunk's key rows (into Kd) and query rows: KQPW granules per wave,
   // same on every path
-  auto stage_kq = [&](const ChunkDesc& cd, lds_u8* Kd) {
+  auto stage_kq = [&](const ChunkPos& cd, lds_u8* Kd) {
     const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
     const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
 #pragma unroll
@@ -1024,14 +1037,16 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   };
   auto issue_point = [] { __builtin_amdgcn_sched_barrier(0); };
 
-  ChunkDesc cur = to_desc(chunk_raw(cb));
-  u32x4 nxt_raw = chunk_raw(cb + 1 < ce ? cb + 1 : cb);
+  // cur: the chunk in work; nxt: the one after it (the last chunk is its own next)
+  uint32_t npos = ce - cb > 1 ? (uint32_t)se.p0 + (uint32_t)chunk_at(se, (uint32_t)se.p0, blk).len : (uint32_t)se.p0;
+  ChunkPos cur = chunk_at(se, (uint32_t)se.p0, blk);
+  ChunkPos nxt = chunk_at(se, npos, blk);
+  uint32_t cur_pid = page_raw(cur);
   stage_chunk(cur, cb, stage0);
   stage_kq(cur, kbuf0);
 
   auto step = [&](const int c, const lds_u8* Bc, lds_u8* Bn, const lds_u8* Kc, lds_u8* Kn) {
     const bool more = c + 1 < ce;
-    const ChunkDesc nxt = to_desc(nxt_raw);
     // Every wave's copies of this chunk (into Bc, Kc and the query buffer) have landed once each wave has
     // waited for all of its own vector memory operations and passed the barrier.  The
     // wait is explicit: the compiler's own count of outstanding LDS DMA follows the
@@ -1041,7 +1056,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     // (the last chunk stages itself again: every path issues the same copies, so the
     // compiler's counts of outstanding loads stay exact)
     stage_chunk(nxt, more ? c + 1 : c, Bn);
-    nxt_raw = chunk_raw(c + 2 < ce ? c + 2 : c + 1 - (more ? 0 : 1));
+    const uint32_t nxt_pid = page_raw(nxt);
 
     read_kq(Kc, 0);
     issue_point();
@@ -1194,10 +1209,18 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     }
 
     // ---- checkpoint: the state after this chunk, bit for bit
-    if (cur.page >= 0)
-      store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)cur.page * p.page_bytes) + head_off +
-                  (size_t)my_row * D);
+    if (cur.page_index >= 0) {
+      const int32_t pid = (int32_t)__builtin_amdgcn_readfirstlane(cur_pid);
+      if (pid >= 0)
+        store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)pid * p.page_bytes) + head_off +
+                    (size_t)my_row * D);
+    }
+    // advance: the chunk after next (the last chunk stays its own next)
+    const uint32_t nnpos = c + 2 < ce ? npos + (uint32_t)nxt.len : npos;
     cur = nxt;
+    cur_pid = nxt_pid;
+    nxt = chunk_at(se, nnpos, blk);
+    npos = nnpos;
   };
 
   // two steps per trip, so that each step's buffers are fixed LDS objects
@@ -1206,7 +1229,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     step(c, stage0, stage1, kbuf0, kbuf1);
     if (c + 1 < ce) step(c + 1, stage1, stage0, kbuf1, kbuf0);
   }
-  store_state(sq.dst + head_off + (size_t)my_row * D);
+  store_state(sq_dst + head_off + (size_t)my_row * D);
 }
 
 // LDS of a staged-scan workgroup (the layout is stated in scan_staged_wave).
@@ -1241,7 +1264,7 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   const int blk = blockIdx.x;
   const int u = (blk / (8 * NG)) * 8 + (blk & 7);
   const int sg = (blk >> 3) % NG;
-  if (u >= p.n_seqs * p.Hv) return;
+  if (u >= kernarg_table()->n_seqs * p.Hv) return;
   switch (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))) {
     case 0: scan_staged_wave<IO, D, 0>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
                                                 (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
@@ -1257,16 +1280,16 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
 // ==================================================================================
 // Launchers
 template <typename IO, int D>
-static hipError_t launch_factorize_t(const FactorizeArgs<IO>& a, int n_chunks, hipStream_t st) {
-  if (n_chunks == 0) return hipSuccess;
-  dim3 grid(a.Hv, n_chunks);
+static hipError_t launch_factorize_t(const FactorizeArgs<IO>& a, hipStream_t st) {
+  if (a.tab.n_units == 0) return hipSuccess;
+  dim3 grid(a.Hv, a.tab.n_units);
   hipLaunchKernelGGL((factorize_kernel<IO, D>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <typename IO, int D>
 static hipError_t launch_scan_t(const ScanArgs<IO>& a, hipStream_t st) {
-  const int64_t units = (int64_t)a.n_seqs * a.Hv;
+  const int64_t units = (int64_t)a.tab.n_seqs * a.Hv;
   if (units == 0) return hipSuccess;
   if constexpr (ScanStaged<IO, D>::OK) {
     using Shp = ScanStaged<IO, D>;
@@ -1281,20 +1304,20 @@ static hipError_t launch_scan_t(const ScanArgs<IO>& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, int n_chunks, hipStream_t st) {
+hipError_t launch_factorize(const FactorizeArgs<bf16_bits>& a, int D, hipStream_t st) {
   switch (D) {
-    case 16: return launch_factorize_t<bf16_bits, 16>(a, n_chunks, st);
-    case 32: return launch_factorize_t<bf16_bits, 32>(a, n_chunks, st);
-    case 64: return launch_factorize_t<bf16_bits, 64>(a, n_chunks, st);
-    case 128: return launch_factorize_t<bf16_bits, 128>(a, n_chunks, st);
+    case 16: return launch_factorize_t<bf16_bits, 16>(a, st);
+    case 32: return launch_factorize_t<bf16_bits, 32>(a, st);
+    case 64: return launch_factorize_t<bf16_bits, 64>(a, st);
+    case 128: return launch_factorize_t<bf16_bits, 128>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
-hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, int n_chunks, hipStream_t st) {
+hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, hipStream_t st) {
   switch (D) {
-    case 16: return launch_factorize_t<float, 16>(a, n_chunks, st);
-    case 32: return launch_factorize_t<float, 32>(a, n_chunks, st);
-    case 64: return launch_factorize_t<float, 64>(a, n_chunks, st);
+    case 16: return launch_factorize_t<float, 16>(a, st);
+    case 32: return launch_factorize_t<float, 32>(a, st);
+    case 64: return launch_factorize_t<float, 64>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -4,6 +4,7 @@
 // consecutive lanes touch consecutive 16-byte pieces of a row.
 #include <hip/hip_runtime.h>
 
+#include "call_table.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "plan.h"
@@ -202,12 +203,14 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
   const int tix = (int)(blockIdx.x / ng), cg = (int)(blockIdx.x % ng);
   const int64_t c0 = ((int64_t)cg * 256 + threadIdx.x) * VEC;
   if (c0 >= p.channels) return;
-  const ConvTile tile = p.tiles[tix];
-  const ConvSeq sq = p.seqs[tile.seq];
+  // the tile's sequence, and its rows [rel0, rel0 + n) within it
+  const_table* tab = kernarg_table();
+  const SeqEntry sq = seq_entry(tab, unit_sequence(tab, tix));
   const int64_t C = p.channels;
-  const int64_t rel0 = tile.row - sq.row0;
-  const int n = tile.len;
-  const IO* src = reinterpret_cast<const IO*>(sq.src_tail);
+  const int64_t rel0 = (int64_t)(tix - sq.unit0) * TR;
+  const int n = (int)min((int64_t)TR, (int64_t)sq.len - rel0);
+  const int64_t tile_row = sq.row0 + rel0;
+  const IO* src = reinterpret_cast<const IO*>(sq.src);
   auto row_ptr = [&](int64_t rel) -> const uint4* {
     if (rel >= 0) return reinterpret_cast<const uint4*>(p.x + (sq.row0 + rel) * C + c0);
     if (src) return reinterpret_cast<const uint4*>(src + (3 + rel) * C + c0);
@@ -245,11 +248,12 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
   // p0 + rel0 + t + 1), and the ordinal of the first such boundary in the sequence
   uint32_t bmask = 0;
   int64_t bord0 = 0;
-  if (p.block > 0) {
+  const int64_t block = tab->block;
+  if (block > 0) {
     const int64_t first = sq.p0 + rel0 + 1, last = sq.p0 + rel0 + n;
-    const int64_t nb = (first + p.block - 1) / p.block;  // first boundary index >= first
-    bord0 = nb - sq.p0 / p.block - 1;
-    for (int64_t P = nb * p.block; P <= last; P += p.block) bmask |= 1u << (uint32_t)(P - first);
+    const int64_t nb = (first + block - 1) / block;  // first boundary index >= first
+    bord0 = nb - sq.p0 / block - 1;
+    for (int64_t P = nb * block; P <= last; P += block) bmask |= 1u << (uint32_t)(P - first);
   }
   int64_t bord = bord0;
   // sliding window over the unpacked rows: each input row is converted once
@@ -287,10 +291,10 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
         for (int e = 0; e < VEC; ++e) yv[e] *= inv;
       }
     }
-    store_vec<IO, VEC>(p.y + (tile.row + t) * C + c0, yv);
+    store_vec<IO, VEC>(p.y + (tile_row + t) * C + c0, yv);
     if (bmask & (1u << t)) {
       {
-        const int32_t pid = p.pages[sq.page_begin + bord++];
+        const int32_t pid = page_list(tab)[sq.page0 + bord++];
         if (pid >= 0) {
           uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<IO*>(p.ckpt_pool + (size_t)pid * p.page_bytes +
                                                                       p.tail_offset) + c0);
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
     }
   }
   if (rel0 == 0) {
-    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<IO*>(sq.dst_tail) + c0);
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<IO*>(sq.dst) + c0);
     const size_t rs = C * sizeof(IO) / 16;
     uint4 tl[3];
 #pragma unroll
@@ -320,6 +324,87 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) dst[i * rs] = tl[i];
   }
+}
+
+// ==================================================================================
+// Conv, decode regime: one new row per request, its three previous rows in a slot of a
+// tail pool.  Thread = VEC consecutive channels of one request (grid: channel groups x
+// requests).  The tail slot is read whole before it is rewritten with the last three
+// raw rows, so the in-place update is safe; slot -1 reads and writes nothing.
+template <typename IO, bool SILU, bool NORM>
+__global__ __launch_bounds__(256) void conv_decode_kernel(ConvDecodeArgs<IO> p) {
+  constexpr int VEC = 16 / sizeof(IO);
+  const int r = blockIdx.y;
+  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * VEC;
+  const int slot = p.slot_ids[r];
+  const int64_t row = p.rows ? (int64_t)p.rows[r] : (int64_t)r;
+  if (slot < -1 || slot >= p.n_slots || (slot >= 0 && (row < 0 || row >= p.n_rows))) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && p.status) atomicOr(p.status, 1 << GDN_ERR_CAPACITY);
+    return;
+  }
+  if (slot < 0 || c0 >= p.channels) return;
+  const int64_t C = p.channels;
+  IO* tail = p.tail_pool + (int64_t)slot * 3 * C + c0;
+  const uint4 t0 = *reinterpret_cast<const uint4*>(tail);
+  const uint4 t1 = *reinterpret_cast<const uint4*>(tail + C);
+  const uint4 t2 = *reinterpret_cast<const uint4*>(tail + 2 * C);
+  const uint4 xr = *reinterpret_cast<const uint4*>(p.x + row * C + c0);
+  float wr[4 * VEC];
+  load_vec<IO, 4 * VEC>(p.w + c0 * 4, wr);
+  float x0[VEC], x1[VEC], x2[VEC], x3[VEC], yv[VEC];
+  unpack_row<IO>(t0, x0);
+  unpack_row<IO>(t1, x1);
+  unpack_row<IO>(t2, x2);
+  unpack_row<IO>(xr, x3);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    float acc = wr[4 * e] * x0[e];
+    acc = fmaf(wr[4 * e + 1], x1[e], acc);
+    acc = fmaf(wr[4 * e + 2], x2[e], acc);
+    acc = fmaf(wr[4 * e + 3], x3[e], acc);
+    if constexpr (SILU) acc = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));
+    yv[e] = acc;
+  }
+  if constexpr (NORM) {
+    if (c0 < p.qk_channels) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ss = fmaf(yv[e], yv[e], ss);
+      for (int off = 1; off < p.head_dim / VEC; off <<= 1) ss += __shfl_xor(ss, off);
+      const float inv = rsqrtf(ss + 1e-6f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) yv[e] *= inv;
+    }
+  }
+  store_vec<IO, VEC>(p.y + row * C + c0, yv);
+  *reinterpret_cast<uint4*>(tail) = t1;
+  *reinterpret_cast<uint4*>(tail + C) = t2;
+  *reinterpret_cast<uint4*>(tail + 2 * C) = xr;
+}
+
+template <typename IO>
+static hipError_t launch_conv_decode_t(const ConvDecodeArgs<IO>& a, int n_req, hipStream_t st) {
+  if (n_req == 0) return hipSuccess;
+  constexpr int VEC = 16 / sizeof(IO);
+  const int64_t groups = (a.channels / VEC + 255) / 256;
+  if (groups > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)groups, (unsigned)n_req);
+  const bool silu = (a.act & ~GDN_CONV_QK_L2NORM) == GDN_ACT_SILU, norm = (a.act & GDN_CONV_QK_L2NORM) != 0;
+  if (silu && norm)
+    hipLaunchKernelGGL((conv_decode_kernel<IO, true, true>), grid, dim3(256), 0, st, a);
+  else if (silu)
+    hipLaunchKernelGGL((conv_decode_kernel<IO, true, false>), grid, dim3(256), 0, st, a);
+  else if (norm)
+    hipLaunchKernelGGL((conv_decode_kernel<IO, false, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((conv_decode_kernel<IO, false, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_conv_decode(const ConvDecodeArgs<bf16_bits>& a, int n_req, hipStream_t st) {
+  return launch_conv_decode_t(a, n_req, st);
+}
+hipError_t launch_conv_decode(const ConvDecodeArgs<float>& a, int n_req, hipStream_t st) {
+  return launch_conv_decode_t(a, n_req, st);
 }
 
 // ==================================================================================
@@ -352,7 +437,8 @@ hipError_t launch_decode(const DecodeArgs<float>& a, int D, int n_req, hipStream
 }
 
 template <typename IO>
-static hipError_t launch_conv_t(const ConvArgs<IO>& a, int n_tiles, hipStream_t st) {
+static hipError_t launch_conv_t(const ConvArgs<IO>& a, hipStream_t st) {
+  const int n_tiles = a.tab.n_units;
   if (n_tiles == 0) return hipSuccess;
   constexpr int VEC = 16 / sizeof(IO);
   const int64_t groups = a.channels / VEC;
@@ -370,12 +456,8 @@ static hipError_t launch_conv_t(const ConvArgs<IO>& a, int n_tiles, hipStream_t 
     hipLaunchKernelGGL((conv_kernel<IO, false, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
-hipError_t launch_conv(const ConvArgs<bf16_bits>& a, int n_tiles, hipStream_t st) {
-  return launch_conv_t<bf16_bits>(a, n_tiles, st);
-}
-hipError_t launch_conv(const ConvArgs<float>& a, int n_tiles, hipStream_t st) {
-  return launch_conv_t<float>(a, n_tiles, st);
-}
+hipError_t launch_conv(const ConvArgs<bf16_bits>& a, hipStream_t st) { return launch_conv_t<bf16_bits>(a, st); }
+hipError_t launch_conv(const ConvArgs<float>& a, hipStream_t st) { return launch_conv_t<float>(a, st); }
 
 // ==================================================================================
 // Gates of the packed core ("Hybrid linear attention (gated DeltaNet)", "Packed-core

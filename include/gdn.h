@@ -17,8 +17,17 @@
  *
  * Conventions for every call:
  *   - Pointers marked [host] are host memory read before the call returns; all other
- *     pointers are device memory of the current HIP device.  The caller owns all
- *     memory; libgdn allocates and frees nothing and keeps no state between calls.
+ *     pointers are device memory of the current HIP device, except a gdn_staging
+ *     buffer (pinned host memory, below).  The caller owns all memory; libgdn allocates
+ *     and frees nothing and keeps no state between calls, so calls on different streams
+ *     never wait for one another.
+ *   - A call's small tables (one entry per sequence, one page id per crossed block
+ *     boundary) travel in the kernel arguments when the batch has at most
+ *     GDN_INLINE_SEQS sequences and GDN_INLINE_PAGES boundaries.  Past that, the call
+ *     writes them into the caller's gdn_staging buffer and copies them from there into
+ *     its workspace on `stream`; the caller must leave that buffer untouched until the
+ *     stream has passed the call (as for any asynchronous copy from host memory), and
+ *     gdn_*_staging_bytes gives the size (0 when none is needed).
  *   - Work is enqueued on `stream` and runs asynchronously.  Argument validation is
  *     synchronous and happens before anything is enqueued: on any error the call
  *     returns a non-zero gdn_status, enqueues nothing and modifies no memory (fail
@@ -31,6 +40,13 @@
  *   - Masked or unused rows are excluded by selection, never by multiplying with a
  *     mask, so NaN bit patterns in rows a call must not read cannot reach a result
  *     ("Prefix caching on Gated DeltaNet hybrids", "The in-page layout", defect 1).
+ *   - Domain.  The results hold the stated accuracy (relative L2 1e-3 with bf16 inputs,
+ *     1e-5 with fp32 inputs) for a_t in (0, 1] and b_t in [0, 1] with b_t |k_t|^2 <= 2:
+ *     the range in which the update S (I - b k k^T) does not grow the state (unit keys,
+ *     as the packed core's post-conv step makes them, are always in it).  Outside it
+ *     the state grows geometrically and so do fp32 rounding errors.  A state decayed
+ *     below 2^-126 (the smallest normal fp32, e.g. by a = 2^-126) is held as an fp32
+ *     subnormal or zero, without relative precision.
  *
  * Determinism.  For one sequence, given its inputs, its start position, the bits of
  * its state source and the layer descriptor, every output, checkpoint and final state
@@ -53,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -67,7 +83,8 @@ typedef enum gdn_status {
   GDN_ERR_CAPACITY = 8,        /* a count exceeds what the call supports (rows, slots) */
   GDN_ERR_WORKSPACE = 9,       /* workspace NULL, too small or misaligned */
   GDN_ERR_HIP = 10,            /* a HIP runtime call failed while enqueueing */
-  GDN_ERR_BAD_SOURCE = 11      /* unknown state source kind */
+  GDN_ERR_BAD_SOURCE = 11,     /* unknown state source kind */
+  GDN_ERR_STAGING = 12         /* the tables need a staging buffer: missing or too small */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -133,8 +150,9 @@ typedef struct gdn_state_ref {
  * pages of block * bytes-per-token; any page_bytes >= gdn_checkpoint_bytes works.
  * A checkpoint is written when a sequence's absolute position reaches a positive
  * multiple of `block` (the call's last row included): it holds the state after
- * exactly that many tokens ("a full block must keep the recurrent state after its
- * last token", same section).  page_ids lists one page per crossed boundary,
+ * exactly that many tokens, i.e. the state that closes the block (same page and
+ * section: a complete block carries the recurrent state reached at its end).
+ * Positions stay below 2^30 (GDN_ERR_CAPACITY).  page_ids lists one page per crossed boundary,
  * sequences in order and boundaries in order (gdn_count_boundaries gives the count
  * per sequence); -1 means "do not store this one".  block == 0 disables
  * checkpoints; the pool and page_ids are then not read. */
@@ -142,22 +160,43 @@ typedef struct gdn_ckpt {
   void* pool;                /* device, 256-byte aligned */
   int64_t page_bytes;        /* multiple of 256 */
   int64_t n_pages;
-  int32_t block;             /* tokens per cache block, >= 0 */
+  int32_t block;             /* tokens per cache block, 0 .. 2^24 */
   const int32_t* page_ids;   /* [host] */
 } gdn_ckpt;
+
+/* Host staging for the per-call tables of a batch larger than the kernel arguments
+ * carry (more than GDN_INLINE_SEQS sequences or GDN_INLINE_PAGES crossed boundaries).
+ * `host` is caller-owned host memory of at least gdn_*_staging_bytes bytes, pinned
+ * (hipHostMalloc, or a torch tensor with pin_memory=True) so that the copy from it is
+ * asynchronous; the call writes the tables into it and enqueues one copy into the
+ * table region of the workspace.  Keep it untouched until the stream has passed the
+ * call.  May be NULL when the staging size is 0. */
+#define GDN_INLINE_SEQS 8
+#define GDN_INLINE_PAGES 256
+typedef struct gdn_staging {
+  void* host;
+  size_t bytes;
+} gdn_staging;
 
 /* ---------------------------------------------------------------- sizes and helpers */
 
 int32_t gdn_abi_version(void);
 const char* gdn_status_string(gdn_status status);
 
-/* Bytes of one fp32 state: n_v_heads * d * d * 4.  -1 if the layer is invalid. */
+/* Bytes of one fp32 state: n_v_heads * d * d * 4 (3 MiB at 48 heads of 128 x 128, the
+ * figure of "Prefix caching on Gated DeltaNet hybrids", "Why hits were wrong").  -1 if
+ * the layer is invalid. */
 int64_t gdn_state_bytes(const gdn_layer* layer);
-/* Bytes of one conv tail: (conv_width - 1) * (2 n_qk_heads + n_v_heads) d * sizeof(io). */
+/* Bytes of one conv tail: (conv_width - 1) * (2 n_qk_heads + n_v_heads) d * sizeof(io),
+ * the conv part of the state (same page and section; "Hybrid linear attention (gated
+ * DeltaNet)", "Why this family is different"). */
 int64_t gdn_conv_tail_bytes(const gdn_layer* layer);
-/* State plus conv tail, rounded up to 256 bytes: the minimum page_bytes. */
+/* State plus conv tail, rounded up to 256 bytes: the minimum page_bytes (the
+ * per-layer checkpoint that "Prefix caching on Gated DeltaNet hybrids", "Why hits
+ * were wrong", stores in an attention page). */
 int64_t gdn_checkpoint_bytes(const gdn_layer* layer);
-/* Number of conv channels (2 n_qk_heads + n_v_heads) * d. */
+/* Number of conv channels (2 n_qk_heads + n_v_heads) * d: the packed q | k | v rows the
+ * conv runs over ("Hybrid linear attention (gated DeltaNet)", "Packed-core traces"). */
 int64_t gdn_conv_channels(const gdn_layer* layer);
 
 /* Tokens served from cache for a shared prefix: whole blocks only, the last full
@@ -176,12 +215,23 @@ int64_t gdn_count_boundaries(int64_t start_pos, int64_t n_tokens, int64_t block)
 int64_t gdn_block_size_for_state(int64_t state_bytes, int64_t attn_bytes_per_token,
                                  int64_t alignment);
 
-/* Workspace bytes gdn_chunk_prefill needs for this batch and block. -1 if invalid. */
+/* Workspace bytes gdn_chunk_prefill needs for this batch and block: room for the
+ * staged tables, then one record of chunk factors per (chunk, value head) -- the
+ * state-free half of the chunked form of the rule (the WY / UT transform of
+ * "Gated Delta Networks", Yang, Kautz & Hatamizadeh, ICLR 2025).  -1 if invalid. */
 int64_t gdn_prefill_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
                                     int32_t block);
-/* Workspace bytes gdn_conv_update needs for this batch and block. -1 if invalid. */
+/* Bytes of pinned host staging a prefill of this batch and block needs; 0 when its
+ * tables fit the kernel arguments.  -1 if invalid. */
+int64_t gdn_prefill_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
+                                  int32_t block);
+/* Workspace bytes gdn_conv_update needs (the staged tables only; 0 when they fit the
+ * kernel arguments, and the workspace may then be NULL).  -1 if invalid. */
 int64_t gdn_conv_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
                                  int32_t block);
+/* Bytes of pinned host staging a conv of this batch needs; 0 when none.  -1 if invalid. */
+int64_t gdn_conv_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
+                               int32_t block);
 
 /* ---------------------------------------------------------------- the hot path */
 
@@ -201,7 +251,25 @@ int64_t gdn_conv_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varle
 gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
                            const void* x, const void* w, const gdn_state_ref* tails,
                            const gdn_ckpt* ckpt, void* y, void* workspace,
-                           size_t workspace_bytes);
+                           size_t workspace_bytes, const gdn_staging* staging);
+
+/* The conv's decode regime ("Hybrid linear attention (gated DeltaNet)", "The part that
+ * is easy to get wrong": gdn_conv_decode beside gdn_conv_prefill): one new row per
+ * request, whose previous conv_width - 1 rows sit in slot slot_ids[r] of a tail pool.
+ * For each request r with its row t = rows[r] (rows NULL: t = r):
+ *   y[t][c] = act(w[c][0] tail[0][c] + w[c][1] tail[1][c] + w[c][2] tail[2][c] + w[c][3] x[t][c])
+ * (the GDN_CONV_QK_L2NORM flag normalises the q and k heads as in gdn_conv_update), and
+ * the slot becomes (tail[1], tail[2], x[t]).
+ *   x, y [n_rows][C] io_dtype (the packed rows of a batch; C = gdn_conv_channels);
+ *   w [C][conv_width]; tail_pool [n_slots][conv_width - 1][C] io_dtype, updated in place;
+ *   slot_ids, rows [n_req] int32 (device).  Slot -1 reads and writes nothing; a slot
+ *   outside [-1, n_slots) or a row outside [0, n_rows) leaves the request untouched and
+ *   sets GDN_ERR_CAPACITY in *status (device int32, may be NULL).  Two requests must not
+ *   share a slot.  No checkpoint tail is written: after a token that ends a block, the
+ *   slot holds exactly that block's tail. */
+gdn_status gdn_conv_decode(const gdn_layer* layer, hipStream_t stream, int32_t n_req, int64_t n_rows,
+                           const void* x, const void* w, void* tail_pool, int64_t n_slots,
+                           const int32_t* slot_ids, const int32_t* rows, void* y, int32_t* status);
 
 /* Chunked varlen prefill of the gated delta rule with block checkpoints ("Hybrid
  * linear attention (gated DeltaNet)", "The part that is easy to get wrong":
@@ -224,7 +292,8 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream,
                              const gdn_varlen* varlen, const void* q, const void* k,
                              const void* v, int64_t qk_stride, int64_t v_stride, const float* a,
                              const float* b, const gdn_state_ref* states, const gdn_ckpt* ckpt,
-                             float* o, void* workspace, size_t workspace_bytes);
+                             float* o, void* workspace, size_t workspace_bytes,
+                             const gdn_staging* staging);
 
 /* The two stages of gdn_chunk_prefill, for callers that schedule or time them apart.
  * gdn_prefill_factorize computes, for every chunk and value head, the state-free
@@ -234,17 +303,20 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream,
  * transposed.  gdn_prefill_scan then walks each sequence chunk by chunk and applies
  * them to the state.  The scan must run on the same stream after a factorize with the
  * same layer, varlen, q, k, a, b, ckpt->block and workspace.  Together they do exactly
- * what gdn_chunk_prefill does.  Strides: qk_stride * io bytes, v_stride * io bytes and
+ * what gdn_chunk_prefill does.  Each stages its own tables when the batch needs it
+ * (two calls in a row need two staging buffers, or a wait between them).  Strides: qk_stride * io bytes, v_stride * io bytes and
  * n_v_heads * d * 4 must each stay below 2^31 / 64 (GDN_ERR_BAD_SHAPE otherwise; the
  * same holds for gdn_chunk_prefill). */
 gdn_status gdn_prefill_factorize(const gdn_layer* layer, hipStream_t stream,
                                  const gdn_varlen* varlen, const void* q, const void* k,
                                  int64_t qk_stride, const float* a, const float* b, int32_t block,
-                                 void* workspace, size_t workspace_bytes);
+                                 void* workspace, size_t workspace_bytes,
+                                 const gdn_staging* staging);
 gdn_status gdn_prefill_scan(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
                             const void* q, const void* k, const void* v, int64_t qk_stride,
                             int64_t v_stride, const gdn_state_ref* states, const gdn_ckpt* ckpt,
-                            float* o, void* workspace, size_t workspace_bytes);
+                            float* o, void* workspace, size_t workspace_bytes,
+                            const gdn_staging* staging);
 
 /* One decode token per request ("Hybrid linear attention (gated DeltaNet)", "The part
  * that is easy to get wrong": gdn_decode).  Request r updates the state in slot

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(g.EXPORTED)
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
 
 
 def test_helpers_match_page_figures():
@@ -199,3 +199,42 @@ def test_conv_validation_errors():
                 page_ids=[0, 1, 2], stream=0) == "GDN_ERR_OFF_BOUNDARY"
     assert _err(g.conv_update, layer, x, w, [("slot", None, t)], [0, 20], [4], x,
                 stream=0) == "GDN_ERR_NULL_ARG"
+
+
+# ------------------------------------------------------------------ no library state
+
+def _nm(*args):
+    import subprocess
+    return subprocess.run(["nm", *args, g.LIB_PATH], capture_output=True, text=True, check=True).stdout
+
+
+def test_library_keeps_no_state_and_never_waits():
+    """libgdn holds no memory and no state between calls, so calls on different streams
+    cannot wait for each other: it imports no HIP call that allocates, frees, creates or
+    waits on events, or synchronizes, and its only writable data are the compiler's and
+    the HIP runtime's registration records (no variable of its own)."""
+    imports = {line.split()[-1].split("@")[0] for line in _nm("-D", "--undefined-only").splitlines() if line.strip()}
+    hip = {s for s in imports if s.lower().startswith("hip") or s.startswith("__hip")}
+    forbidden = {s for s in hip if any(w in s for w in ("Synchronize", "Malloc", "Free", "Event", "Wait",
+                                                         "HostRegister", "StreamCreate", "Query"))}
+    assert not forbidden, sorted(forbidden)
+    allowed = {"hipLaunchKernel", "hipGetLastError", "hipMemcpyAsync", "hipGetDevice", "hipGetSymbolAddress",
+               "__hipPushCallConfiguration", "__hipPopCallConfiguration", "__hipRegisterFatBinary",
+               "__hipRegisterFunction", "__hipUnregisterFatBinary", "__hipRegisterVar"}
+    assert hip <= allowed, sorted(hip - allowed)
+    runtime = re.compile(r"^(DW\.ref\.|_DYNAMIC$|_GLOBAL_OFFSET_TABLE_$|__do_(init|fini)\.|__dso_handle$|__(init|fini)$|"
+                         r"__hip_(cuid|fatbin_wrapper|gpubin_handle)|__TMC_END__$|completed\.|__bss_start$|_edata$|_end$)")
+    own = []
+    for line in _nm().splitlines():
+        parts = line.split()
+        if len(parts) < 3 or parts[1] not in "bBdDsSgGvV" or runtime.match(parts[2]):
+            continue
+        # the host-side handle HIP emits for each __global__ function (its address names the
+        # kernel at launch; nothing writes it)
+        if parts[1] == "V" and parts[2].startswith("_ZN3gdn") and "_kernel" in parts[2]:
+            continue
+        own.append(parts[2])
+    # the no-alloc entry point's scratch array and its per-device address table are the one
+    # documented exception
+    own = [s for s in own if "scratch" not in s]
+    assert not own, own

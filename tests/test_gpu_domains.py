@@ -308,3 +308,58 @@ def test_conv_one_row_sequences(g, dtype):
         assert_close_per(yc, oracle.bf16_round(y_ref_all), 1e-3, 0, "one-row conv outputs per sequence")
     else:
         assert_close_per(yc, y_ref_all, 1e-5, 0, "one-row conv outputs per sequence")
+
+
+@pytest.mark.parametrize("dtype,norm", [(BF, True), (torch.float32, False)])
+def test_conv_decode_matches_oracle_and_one_row_conv(g, dtype, norm):
+    """gdn_conv_decode: one new row per request, tails in a slot pool updated in place,
+    rows of a packed batch in permuted order, a padding slot; against the oracle, and
+    bit-identical to gdn_conv_update over the same tokens as one-row sequences."""
+    Hqk, Hv, Dd = 2, 4, 64
+    act = g.ACT_SILU | (g.CONV_QK_L2NORM if norm else 0)
+    layer = g.Layer(Hqk, Hv, Dd, dtype, conv_act=act)
+    C = layer.conv_channels
+    n_req, n_rows, n_slots = 40, 45, 43
+    say(f"conv decode {dtype} norm={norm}")
+    x, w = gi.conv_inputs(n_rows, C, 4, dtype, seed=261)
+    pool0 = gi.conv_tail(n_slots, C, 4, dtype, seed=262)
+    slots = [int(s) for s in gi.permutation(n_slots, 263)[:n_req]]
+    slots[7] = -1
+    rows = [int(r) for r in gi.permutation(n_rows, 264)[:n_req]]
+    xd, wd = x.cuda(), w.cuda()
+    pool = pool0.cuda()
+    y = nan_fill_(torch.empty(n_rows, C, dtype=dtype, device="cuda"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.conv_decode(layer, xd, wd, pool, _i32(slots), y, rows=_i32(rows), status=status)
+    # the same tokens as one-row sequences of conv_update (tails as slot sources)
+    pool_b = pool0.cuda()
+    live = [i for i in range(n_req) if slots[i] >= 0]
+    xs = xd[torch.tensor([rows[i] for i in live], device="cuda")].contiguous()
+    y2 = torch.empty(len(live), C, dtype=dtype, device="cuda")
+    refs = [("slot", pool_b[slots[i]], pool_b[slots[i]]) for i in live]
+    g.conv_update(layer, xs, wd, refs, list(range(len(live) + 1)), [9] * len(live), y2, ckpt=g.no_checkpoints())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert same_bits(pool, pool_b)
+    for j, i in enumerate(live):
+        assert same_bits(y[rows[i]], y2[j]), i
+    untouched = set(range(n_rows)) - {rows[i] for i in live}
+    for r in untouched:
+        assert same_bits(y[r], nan_fill_(torch.empty_like(y[r])))
+    for s in set(range(n_slots)) - {slots[i] for i in live}:
+        assert same_bits(pool[s], pool0[s].cuda())
+    yc = f64(y)
+    for i in live:
+        y_ref, t_ref, _ = oracle.conv(f64(x[rows[i]:rows[i] + 1]), f64(w), f64(pool0[slots[i]]), 1, 9, 0)
+        if norm:
+            y_ref = oracle.l2norm_qk_heads(y_ref, Hqk, Dd)
+        want = oracle.bf16_round(y_ref) if dtype == BF else y_ref
+        from gpu_util import rel_l2
+        assert rel_l2(yc[rows[i]:rows[i] + 1], want) <= TOL[dtype], i
+        assert np.array_equal(f64(pool[slots[i]]), t_ref), i
+    # a slot out of range and a row out of range leave everything untouched
+    before, yb = pool.clone(), y.clone()
+    g.conv_decode(layer, xd, wd, pool, _i32([n_slots, 0]), y, rows=_i32([0, n_rows]), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1 << 8
+    assert same_bits(pool, before) and same_bits(y, yb)

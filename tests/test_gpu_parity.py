@@ -545,3 +545,90 @@ def test_conv_matches_oracle_with_tails_and_checkpoints(g, dtype, act):
         for j in range(n_b[i]):
             assert np.array_equal(f64(pool.tail_view(off + j, layer)), ck_ref[j]), (i, j)
         off += n_b[i]
+
+
+# ------------------------------------------------------------------------- staged tables
+
+def test_staged_tables_match_inline_solo_runs(g):
+    """Batches past the kernel-argument capacity (12 sequences; one sequence with 300
+    block boundaries) copy their tables from a caller-owned pinned staging buffer.  Every
+    sequence's outputs, final state and checkpoints equal its solo run (whose small
+    table travels inline) bit for bit, and the conv over 20 sequences matches too."""
+    D, H, dtype, block = 64, 2, torch.bfloat16, 16
+    layer = g.Layer(H, H, D, dtype)
+    lens = [40, 0, 17, 64, 1, 33, 80, 5, 48, 16, 31, 70]
+    starts = [0, 0, 32, 0, 15, 0, 48, 0, 16, 0, 0, 64]
+    assert len(lens) > g.INLINE_SEQS
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    T = cu[-1]
+    say(f"staged tables: {len(lens)} sequences")
+    q, k, v, a, b = gi.qkvab(T, H, H, D, dtype, seed=301)
+    qd, kd, vd, ad, bd = _dev(q, k, v, a, b)
+    S0 = gi.states(len(lens), H, D, seed=302).cuda()
+    n_b = [oracle.count_boundaries(s, L, block) for s, L in zip(starts, lens)]
+    pool = make_pool(g, layer, 2 * sum(n_b), block)
+    need = g.prefill_staging_bytes(layer, cu, starts, block)
+    assert need > 0
+    staging = g.pinned_staging(need)
+    o = torch.empty(T, H, D, device="cuda")
+    Sf = torch.empty(len(lens), H, D, D, device="cuda")
+    refs = [("zero" if s == 0 else "slot", None if s == 0 else S0[i], Sf[i]) for i, s in enumerate(starts)]
+    g.chunk_prefill(layer, qd, kd, vd, ad, bd, cu, starts, refs, o, ckpt=pool, page_ids=list(range(sum(n_b))),
+                    staging=staging)
+    torch.cuda.synchronize()
+    base = sum(n_b)
+    for i, (s, L) in enumerate(zip(starts, lens)):
+        r0 = cu[i]
+        o1 = torch.empty(max(L, 1), H, D, device="cuda")
+        S1 = torch.empty(H, D, D, device="cuda")
+        ref = ("zero" if s == 0 else "slot", None if s == 0 else S0[i], S1)
+        sl = slice(r0, r0 + L) if L else slice(0, 0)
+        g.chunk_prefill(layer, qd[sl] if L else qd, kd[sl] if L else kd, vd[sl] if L else vd,
+                        ad[sl] if L else ad, bd[sl] if L else bd, [0, L], [s], [ref], o1, ckpt=pool,
+                        page_ids=list(range(base, base + n_b[i])))
+        torch.cuda.synchronize()
+        if L:
+            assert same_bits(o1[:L], o[r0:r0 + L]), i
+        assert same_bits(S1, Sf[i]), i
+        off = sum(n_b[:i])
+        for j in range(n_b[i]):
+            assert torch.equal(pool.pool[base + j, :layer.state_bytes], pool.pool[off + j, :layer.state_bytes])
+
+    # one sequence crossing 300 boundaries: more pages than the arguments carry
+    L = 300 * block + 7
+    q2, k2, v2, a2, b2 = _dev(*gi.qkvab(L, H, H, D, dtype, seed=303))
+    pool2 = make_pool(g, layer, 300, block)
+    assert g.prefill_staging_bytes(layer, [0, L], [0], block) > 0
+    o2 = torch.empty(L, H, D, device="cuda")
+    S2 = torch.empty(H, D, D, device="cuda")
+    st2 = g.pinned_staging(g.prefill_staging_bytes(layer, [0, L], [0], block))
+    ids = [int(p) for p in gi.permutation(300, 304)]
+    g.chunk_prefill(layer, q2, k2, v2, a2, b2, [0, L], [0], [("zero", None, S2)], o2, ckpt=pool2, page_ids=ids,
+                    staging=st2)
+    torch.cuda.synchronize()
+    o_ref, S_ref, ck_ref = oracle.recurrence(f64(q2), f64(k2), f64(v2), f64(a2), f64(b2), 1.0, None, 0, block)
+    assert rel_l2(f64(o2), o_ref) <= TOL[dtype] and rel_l2(f64(S2), S_ref) <= TOL[dtype]
+    errs = [rel_l2(f64(pool2.state_view(ids[i], layer)), ck_ref[i]) for i in range(300)]
+    assert max(errs) <= TOL[dtype], int(np.argmax(errs))
+
+    # the conv over 20 sequences, staged, against the oracle
+    lc = g.Layer(1, 1, 16, dtype)
+    C = lc.conv_channels
+    clens = [(7 * i) % 23 for i in range(20)]
+    ccu = np.concatenate([[0], np.cumsum(clens)]).tolist()
+    x, w = gi.conv_inputs(ccu[-1], C, 4, dtype, seed=305)
+    tails0 = gi.conv_tail(20, C, 4, dtype, seed=306)
+    tout = torch.empty(20, 3, C, dtype=dtype, device="cuda")
+    cst = [5 + i for i in range(20)]
+    y = torch.empty(max(ccu[-1], 1), C, dtype=dtype, device="cuda")
+    need = g.conv_staging_bytes(lc, ccu, cst, 0)
+    assert need > 0
+    g.conv_update(lc, x.cuda(), w.cuda(), [("slot", tails0[i].cuda(), tout[i]) for i in range(20)], ccu, cst, y,
+                  ckpt=g.no_checkpoints(), staging=g.pinned_staging(need))
+    torch.cuda.synchronize()
+    for i in range(20):
+        sl = slice(ccu[i], ccu[i + 1])
+        y_ref, t_ref, _ = oracle.conv(f64(x[sl]), f64(w), f64(tails0[i]), 1, cst[i], 0)
+        if clens[i]:
+            assert rel_l2(f64(y[sl]), oracle.bf16_round(y_ref)) <= 1e-3, i
+        assert np.array_equal(f64(tout[i]), t_ref), i

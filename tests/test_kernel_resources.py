@@ -1,0 +1,32 @@
+"""Kernel resource checks on the CPU (device assembly of the library's own sources):
+every kernel runs without a private (scratch) segment.  A kernel whose argument block
+the compiler copies to private memory would pay a 1.5 KiB per-lane copy at every launch,
+and kernels read their call tables in place in the kernel-argument segment.  The one
+known exception is a two-register spill of the replay kernel for 64-row logs at
+d = 128 (a variant the workloads do not time)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_deltanet_recurrent_chunk_amd", "csrc")
+
+
+@pytest.mark.parametrize("src", ["prefill_kernels.hip", "stream_kernels.hip", "flush_kernel.hip"])
+def test_kernels_use_no_private_segment(src, tmp_path):
+    out = str(tmp_path / "k.s")
+    cmd = ["/opt/rocm/bin/hipcc", "-x", "hip", "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only",
+           "-S", "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form", os.path.join(CSRC, src), "-o", out]
+    if src == "flush_kernel.hip":
+        cmd[-2:-2] = ["-mllvm", "-amdgpu-kernarg-preload-count=4"]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = open(out).read()
+    kernels = re.findall(r"^\t\.amdhsa_kernel (\S+)$", text, re.M)
+    sizes = re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)
+    assert kernels and len(kernels) == len(sizes)
+    allowed = {"_ZN3gdn13replay_kernelItLi128ELi64EEEvNS_10ReplayArgsIT_EE": 16}
+    bad = [(k, int(n)) for k, n in zip(kernels, sizes) if int(n) > allowed.get(k, 0)]
+    assert not bad, bad
