@@ -93,6 +93,8 @@ _decl("gdn_conv_update", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _P(_Stat
 _decl("gdn_conv_decode", _i32, [_P(_Layer), _vp, _i32, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp])
 _decl("gdn_chunk_prefill", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
                                   _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz, _P(_Staging)])
+_decl("gdn_chunk_prefill_noalloc", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
+                                          _P(_StateRef), _P(_Ckpt), _vp])
 _decl("gdn_prefill_factorize", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _i64, _vp, _vp, _i32, _vp, _sz,
                                       _P(_Staging)])
 _decl("gdn_prefill_scan", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _P(_StateRef),
@@ -109,7 +111,7 @@ _decl("gdn_replay_forward", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_state_bytes", "gdn_conv_tail_bytes",
             "gdn_checkpoint_bytes", "gdn_conv_channels", "gdn_cached_prefix_tokens", "gdn_floor_chunk",
             "gdn_count_boundaries", "gdn_block_size_for_state", "gdn_prefill_workspace_bytes",
-            "gdn_prefill_staging_bytes", "gdn_conv_workspace_bytes", "gdn_conv_staging_bytes", "gdn_conv_update", "gdn_conv_decode", "gdn_chunk_prefill", "gdn_prefill_factorize",
+            "gdn_prefill_staging_bytes", "gdn_conv_workspace_bytes", "gdn_conv_staging_bytes", "gdn_conv_update", "gdn_conv_decode", "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc", "gdn_prefill_factorize",
             "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush", "gdn_replay_forward",
             "gdn_gates", "gdn_gated_norm", "gdn_decode_mixed")
 
@@ -429,6 +431,24 @@ def chunk_prefill(layer: Layer, q, k, v, a, b, cu_seqlens, start_pos, states, o,
     if wait:
         _sync(stream)
     return ws
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def chunk_prefill_noalloc(layer: Layer, q, k, v, a, b, cu_seqlens, start_pos, states, o, ckpt=None,
+                          page_ids=None, stream=None, qk_stride=None, v_stride=None):
+    """gdn_chunk_prefill_noalloc: chunk_prefill without a workspace (the library's fixed
+    per-device scratch holds the chunk factors); nothing is allocated for the call."""
+    vl = _Varlens(cu_seqlens, start_pos)
+    qs = qk_stride if qk_stride is not None else layer.n_qk_heads * layer.head_dim
+    vs = v_stride if v_stride is not None else layer.n_v_heads * layer.head_dim
+    _check_prefill_operands(layer, cu_seqlens, start_pos, q, k, v, a, b, o, states, qs, vs)
+    ck, keep = _ckpt_c(ckpt, page_ids)
+    refs = _refs(states)
+    st = _lib.gdn_chunk_prefill_noalloc(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(vl.c), _ptr(q),
+                                        _ptr(k), _ptr(v), qs, vs, _ptr(a), _ptr(b), refs, ctypes.byref(ck), _ptr(o))
+    _check(st, "gdn_chunk_prefill_noalloc")
 
 
 def prefill_factorize(layer: Layer, q, k, a, b, cu_seqlens, start_pos, block, workspace, stream=None,

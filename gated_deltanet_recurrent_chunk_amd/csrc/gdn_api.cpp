@@ -9,6 +9,7 @@
 // never wait for each other.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <vector>
 
@@ -18,7 +19,30 @@
 
 using namespace gdn;
 
+// Device scratch of gdn_chunk_prefill_noalloc (the factor records of one call), for
+// callers that cannot allocate: one array per device, held from the library's load on
+// that device until the process ends.  Host code never uses this name as an address:
+// it is a host-side stand-in, and the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on each device, looked up once per device (with that
+// device current) on the entry point's first call there.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+gdn_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_HIP;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return GDN_OK;
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p) % a == 0; }
 
@@ -354,6 +378,35 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream, const g
   s = do_factorize<float>(P, stream, q, k, qk_stride, a, b, workspace);
   if (s != GDN_OK) return s;
   return do_scan<float>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
+}
+
+gdn_status gdn_chunk_prefill_noalloc(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
+                                     const void* q, const void* k, const void* v, int64_t qk_stride, int64_t v_stride,
+                                     const float* a, const float* b, const gdn_state_ref* states,
+                                     const gdn_ckpt* ckpt, float* o) {
+  if (!ckpt) return GDN_ERR_NULL_ARG;
+  PrefillPrep P;
+  gdn_status s = prep_prefill(layer, varlen, ckpt->block, ckpt, &P);
+  if (s != GDN_OK) return s;
+  s = check_qkv(P.L, q, k, v, qk_stride, v_stride, true, true);
+  if (s != GDN_OK) return s;
+  if (P.plan.n_units > 0 && (!a || !b || !o)) return GDN_ERR_NULL_ARG;
+  s = check_states(P, states, ckpt->block);
+  if (s != GDN_OK) return s;
+  // the scratch holds the records; the tables must travel in the kernel arguments
+  if (P.plan.staged || P.plan.total_bytes > (size_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_CAPACITY;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != GDN_OK) return s;
+  set_state_refs(&P, states);
+  if (P.L.io == GDN_BF16) {
+    s = do_factorize<bf16_bits>(P, stream, q, k, qk_stride, a, b, ws);
+    if (s != GDN_OK) return s;
+    return do_scan<bf16_bits>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, ws);
+  }
+  s = do_factorize<float>(P, stream, q, k, qk_stride, a, b, ws);
+  if (s != GDN_OK) return s;
+  return do_scan<float>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, ws);
 }
 
 gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen, const void* x,

@@ -20,7 +20,8 @@
  *     pointers are device memory of the current HIP device, except a gdn_staging
  *     buffer (pinned host memory, below).  The caller owns all memory; libgdn allocates
  *     and frees nothing and keeps no state between calls, so calls on different streams
- *     never wait for one another.
+ *     never wait for one another.  (gdn_chunk_prefill_noalloc is the one exception: it
+ *     keeps its scratch array's device address, once per device.)
  *   - A call's small tables (one entry per sequence, one page id per crossed block
  *     boundary) travel in the kernel arguments when the batch has at most
  *     GDN_INLINE_SEQS sequences and GDN_INLINE_PAGES boundaries.  Past that, the call
@@ -294,6 +295,27 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream,
                              const float* b, const gdn_state_ref* states, const gdn_ckpt* ckpt,
                              float* o, void* workspace, size_t workspace_bytes,
                              const gdn_staging* staging);
+
+/* gdn_chunk_prefill for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation with the
+ * same results, bit for bit, but no workspace or staging argument.  Its chunk factors go
+ * to a fixed device array of GDN_NOALLOC_SCRATCH_BYTES inside the library, one per GPU
+ * (held from the library's load on that GPU until the process ends); the caller still
+ * passes the inputs and outputs.  A batch whose workspace (gdn_prefill_workspace_bytes)
+ * exceeds that size, or whose tables do not fit the kernel arguments (more than
+ * GDN_INLINE_SEQS sequences or GDN_INLINE_PAGES boundaries), is refused with
+ * GDN_ERR_CAPACITY and nothing is enqueued.  64 MiB holds the records of about 2,600
+ * (chunk, value head) pairs: a 1,792-token step of a 48-head layer needs under 40 MiB.
+ * All calls on one GPU share its array: calls that overlap in time on one GPU (two
+ * streams, two threads) race on it, so order them.  It calls no allocating routine; its
+ * first call on a device looks up the array's device address once (hipGetSymbolAddress)
+ * and keeps it. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64 << 20)
+gdn_status gdn_chunk_prefill_noalloc(const gdn_layer* layer, hipStream_t stream,
+                                     const gdn_varlen* varlen, const void* q, const void* k,
+                                     const void* v, int64_t qk_stride, int64_t v_stride,
+                                     const float* a, const float* b, const gdn_state_ref* states,
+                                     const gdn_ckpt* ckpt, float* o);
 
 /* The two stages of gdn_chunk_prefill, for callers that schedule or time them apart.
  * gdn_prefill_factorize computes, for every chunk and value head, the state-free
