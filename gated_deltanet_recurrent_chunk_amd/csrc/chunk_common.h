@@ -122,9 +122,16 @@ __device__ __forceinline__ void transpose_keys(const bf16_bits* Ks, int KP, bf16
 // global loads, stores and LDS DMA are not waited for).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Barrier that also completes this wave's outstanding vector memory operations (LDS DMA
-// included) before any wave passes it.
+// and stores included) before any wave passes it.  The wait is the builtin, so the
+// compiler's own wait accounting sees it: no memory operation issued before the barrier
+// is waited for again after it (an inline-asm wait is invisible to that accounting, and
+// the compiler would then wait again, for everything pending, at its first read of
+// copied data).  The empty asm statements keep memory accesses on their side.
 __device__ __forceinline__ void full_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0); expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ----------------------------------------------------------------------------------

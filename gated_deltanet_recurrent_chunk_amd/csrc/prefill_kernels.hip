@@ -872,6 +872,13 @@ __device__ __forceinline__ void dma16(rsrc_t r, lds_u8* lds, uint32_t voff) {
 // The work of wave Q of a staged-scan workgroup (slab Q / 2 of the pair, key half
 // Q % 2), compiled once per wave index so that every register index and every copy
 // assignment is a constant.
+// Output row tiles of the key half w of a slab (two waves per slab): rows {0, 3} and
+// {1, 2}, so that both hold the same number of score products (PT'' R' has one k-step
+// for row tiles 0 and 1, two for 2 and 3).
+// (With one wave per slab, the wave holds all four in order.)
+template <int NSP>
+__host__ __device__ constexpr int omt(int w, int i) { return NSP == 1 ? i : i == 0 ? w : 3 - w; }
+
 template <typename IO, int D, int Q>
 __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const int u, const int sg, lds_u8* stage0,
                                                  lds_u8* stage1, lds_u8* kbuf0, lds_u8* kbuf1, lds_u8* qbuf,
@@ -916,7 +923,6 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   const uint32_t blk = (uint32_t)tab->block;
   const size_t head_off = (size_t)h * D * D;
   constexpr int jt0 = DTH * w, s0 = KSH * w;  // first state tile and k-step of this wave
-  constexpr int mt0 = MR * w;                 // first output row tile of this wave
 
   f32x4 S[DTH];
 #pragma unroll
@@ -1045,6 +1051,29 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   stage_chunk(cur, cb, stage0);
   stage_kq(cur, kbuf0);
 
+  // Stores are issued one chunk late, right after the next chunk's barrier: the
+  // barrier's wait for this wave's copies (vmcnt) also counts stores, so a store issued
+  // late in a chunk would hold every wave at the next barrier until it completed.  The
+  // outputs of a chunk wait in registers, and a checkpoint is the state as it stands
+  // until the next chunk's update.
+  f32x4 o_pend[MR];
+  ChunkPos o_chunk = cur;
+  bool o_have = false;
+  int32_t ck_pid = -1;
+  auto flush_pending = [&]() {
+    if (o_have) {
+      const rsrc_t ro =
+          make_rsrc(p.o + o_chunk.row * (int64_t)p.Hv * D + (int64_t)h * D + 16 * sl, (uint32_t)o_chunk.len * osb);
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st4(ro, o_off[r] + 16 * omt<NSP>(w, i) * osb, o_pend[i][r]);
+    }
+    if (ck_pid >= 0)
+      store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)ck_pid * p.page_bytes) + head_off +
+                  (size_t)my_row * D);
+  };
+
   auto step = [&](const int c, const lds_u8* Bc, lds_u8* Bn, const lds_u8* Kc, lds_u8* Kn) {
     const bool more = c + 1 < ce;
     // Every wave's copies of this chunk (into Bc, Kc and the query buffer) have landed once each wave has
@@ -1053,6 +1082,8 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     // data a wave reads itself, not the copies its partners read.  The copies were
     // issued most of a chunk earlier, so the wait rarely stalls.
     full_barrier();
+    // the previous chunk's outputs and checkpoint
+    flush_pending();
     // (the last chunk stages itself again: every path issues the same copies, so the
     // compiler's counts of outstanding loads stay exact)
     stage_chunk(nxt, more ? c + 1 : c, Bn);
@@ -1107,9 +1138,12 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) mine[mt * 64] = X[mt];
 #pragma unroll
-      for (int i = 0; i < MR; ++i) mine[(4 + i) * 64] = Y[MR * (w ^ 1) + i];
-      read_b();  // requested here: the barrier's wait covers their latency
+      for (int i = 0; i < MR; ++i) mine[(4 + i) * 64] = Y[omt<NSP>(w ^ 1, i)];
+      // the barrier waits for this wave's LDS traffic: the partial sums just written,
+      // not the operands of phase B, which are requested after it (measured: issuing
+      // them before the barrier held every wave there for all of them)
       lds_barrier();
+      read_b();
       // every wave has read this chunk's key and query rows: copy the next chunk's
       // (the last chunk copies its own again, so that every path issues the same copies)
       stage_kq(more ? nxt : cur, Kn);
@@ -1123,11 +1157,11 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       for (int i = 0; i < MR; ++i) {
         const f32x4 yo = other[(4 + i) * 64];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Ym[i][r] = Y[mt0 + i][r] + yo[r];
+        for (int r = 0; r < 4; ++r) Ym[i][r] = Y[omt<NSP>(w, i)][r] + yo[r];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < MR; ++i) Ym[i] = Y[mt0 + i];
+      for (int i = 0; i < MR; ++i) Ym[i] = Y[omt<NSP>(w, i)];
       read_b();
       lds_barrier();
       // every wave has read this chunk's key and query rows: copy the next chunk's (the
@@ -1157,7 +1191,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     bf16x8 Pf[MR][2][NTF];
 #pragma unroll
     for (int i = 0; i < MR; ++i) {
-      const int mt = mt0 + i;
+      const int mt = omt<NSP>(w, i);
       vegs[i] = vrow4(Bc, Cfg::V_EGS, mt);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -1167,22 +1201,21 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     }
     issue_point();
 
-    // ---- C: O = scale exp(g) Y + PT'' R' for this wave's row tiles
-    {
-      const rsrc_t ro = make_rsrc(p.o + cur.row * (int64_t)p.Hv * D + (int64_t)h * D + 16 * sl, (uint32_t)cur.len * osb);
+    // ---- C: O = scale exp(g) Y + PT'' R' for this wave's row tiles (stored after the
+    //      next barrier)
 #pragma unroll
-      for (int i = 0; i < MR; ++i) {
-        const int mt = mt0 + i;
-        f32x4 acc;
+    for (int i = 0; i < MR; ++i) {
+      const int mt = omt<NSP>(w, i);
+      f32x4 acc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = Ym[i][r] * vegs[i][r];
+      for (int r = 0; r < 4; ++r) acc[r] = Ym[i][r] * vegs[i][r];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Rop[s]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st4(ro, o_off[r] + 16 * mt * osb, acc[r]);
-      }
+      for (int s = 0; s < 2; ++s)
+        if (s <= (mt >> 1)) mma_terms<NTF, NTF, ORD>(acc, Pf[i][s], Rop[s]);
+      o_pend[i] = acc;
     }
+    o_chunk = cur;
+    o_have = true;
 
     // ---- operands of phase D, requested while the products above run
     bf16x8 KTf[DTH][2][NTI];
@@ -1208,13 +1241,9 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
         for (int j = 0; j < DTH; ++j) mma_terms<NTI, NTF, ORD>(S[j], KTf[j][s], Dtop[s]);
     }
 
-    // ---- checkpoint: the state after this chunk, bit for bit
-    if (cur.page_index >= 0) {
-      const int32_t pid = (int32_t)__builtin_amdgcn_readfirstlane(cur_pid);
-      if (pid >= 0)
-        store_state(reinterpret_cast<float*>(p.ckpt_pool + (size_t)pid * p.page_bytes) + head_off +
-                    (size_t)my_row * D);
-    }
+    // ---- checkpoint: the state after this chunk, bit for bit (stored after the next
+    //      barrier, before the next update changes it)
+    ck_pid = cur.page_index >= 0 ? (int32_t)__builtin_amdgcn_readfirstlane(cur_pid) : -1;
     // advance: the chunk after next (the last chunk stays its own next)
     const uint32_t nnpos = c + 2 < ce ? npos + (uint32_t)nxt.len : npos;
     cur = nxt;
@@ -1229,6 +1258,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     step(c, stage0, stage1, kbuf0, kbuf1);
     if (c + 1 < ce) step(c + 1, stage1, stage0, kbuf1, kbuf0);
   }
+  flush_pending();
   store_state(sq_dst + head_off + (size_t)my_row * D);
 }
 
