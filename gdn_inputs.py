@@ -233,3 +233,17 @@ def collinear_keys(T: int, n_qk: int, d: int, io_dtype=torch.bfloat16, seed: int
     base = _unit_rows(torch.randn(n_runs, n_qk, d, generator=g)).repeat_interleave(run, 0)[:T]
     k = _unit_rows(base + spread * torch.randn(T, n_qk, d, generator=g) / d ** 0.5)
     return k.to(io_dtype)
+
+
+def conv_inputs_device(T: int, channels: int, width: int = 4, io_dtype=torch.bfloat16, seed: int = 0,
+                       device="cuda"):
+    """Same recipe as conv_inputs (x ~ N(0, 1), w ~ 0.5 N(0, 1)), drawn on the device in
+    token blocks (for the long workload, whose host draw would dominate)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 99)
+    w = (0.5 * torch.randn(channels, width, generator=g, device=device)).to(io_dtype)
+    x = torch.empty(T, channels, dtype=io_dtype, device=device)
+    for t0 in range(0, T, TOKEN_BLOCK):
+        n = min(TOKEN_BLOCK, T - t0)
+        x[t0:t0 + n] = torch.randn(n, channels, generator=g, device=device).to(io_dtype)
+    return x, w
