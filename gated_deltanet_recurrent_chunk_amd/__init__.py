@@ -88,9 +88,9 @@ _decl("gdn_prefill_workspace_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
 _decl("gdn_prefill_staging_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
 _decl("gdn_conv_workspace_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
 _decl("gdn_conv_staging_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
-_decl("gdn_conv_update", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz,
-                                _P(_Staging)])
-_decl("gdn_conv_decode", _i32, [_P(_Layer), _vp, _i32, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp])
+_decl("gdn_conv_update", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _i64, _vp, _P(_StateRef), _P(_Ckpt), _vp, _vp,
+                                _sz, _P(_Staging)])
+_decl("gdn_conv_decode", _i32, [_P(_Layer), _vp, _i32, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp])
 _decl("gdn_chunk_prefill", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
                                   _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz, _P(_Staging)])
 _decl("gdn_chunk_prefill_noalloc", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
@@ -105,15 +105,22 @@ _decl("gdn_decode_mixed", _i32, [_P(_Layer), _vp, _i32, _i64, _vp, _vp, _vp, _i6
                                  _vp, _vp, _vp])
 _decl("gdn_gates", _i32, [_P(_Layer), _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp])
 _decl("gdn_gated_norm", _i32, [_P(_Layer), _vp, _i64, _vp, _vp, _i64, _vp, ctypes.c_float, _vp])
+_decl("gdn_core_prefill_workspace_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
+_decl("gdn_core_prefill_staging_bytes", _i64, [_P(_Layer), _P(_Varlen), _i32])
+_decl("gdn_core_prefill", _i32, [_P(_Layer), _vp, _P(_Varlen), _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
+                                 ctypes.c_float, _P(_StateRef), _P(_StateRef), _P(_Ckpt), _vp, _vp, _sz,
+                                 _P(_Staging)])
 _decl("gdn_replay_forward", _i32, [_P(_Layer), _vp, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                    _i32, _vp, _vp])
 
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_state_bytes", "gdn_conv_tail_bytes",
             "gdn_checkpoint_bytes", "gdn_conv_channels", "gdn_cached_prefix_tokens", "gdn_floor_chunk",
             "gdn_count_boundaries", "gdn_block_size_for_state", "gdn_prefill_workspace_bytes",
-            "gdn_prefill_staging_bytes", "gdn_conv_workspace_bytes", "gdn_conv_staging_bytes", "gdn_conv_update", "gdn_conv_decode", "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc", "gdn_prefill_factorize",
+            "gdn_prefill_staging_bytes", "gdn_conv_workspace_bytes", "gdn_conv_staging_bytes", "gdn_conv_update",
+            "gdn_conv_decode", "gdn_chunk_prefill", "gdn_chunk_prefill_noalloc", "gdn_prefill_factorize",
             "gdn_prefill_scan", "gdn_decode_step", "gdn_replay_flush", "gdn_replay_forward",
-            "gdn_gates", "gdn_gated_norm", "gdn_decode_mixed")
+            "gdn_gates", "gdn_gated_norm", "gdn_decode_mixed", "gdn_core_prefill_workspace_bytes",
+            "gdn_core_prefill_staging_bytes", "gdn_core_prefill")
 
 
 class GdnError(RuntimeError):
@@ -246,6 +253,23 @@ def _rows_ok(t, rows, row_elems, dtype, name):
     _need(t.numel() >= rows * row_elems, f"{name}: {t.numel()} elements < {rows} x {row_elems}")
 
 
+def _strided_rows(t, rows, row_elems, dtype, name) -> int:
+    """t: a 2-D [>= rows, >= row_elems] view with unit column stride (dense rows, or the
+    leading columns of wider packed rows); returns its row stride in elements."""
+    if rows == 0 and t is None:
+        return row_elems
+    _need(t is not None, f"{name} is required")
+    _need(t.dtype == dtype, f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.dim() != 2 and t.is_contiguous():
+        t = t.reshape(t.shape[0], -1)
+    _need(t.dim() == 2 and t.stride(1) == 1 and t.shape[1] >= row_elems and t.shape[0] >= rows,
+          f"{name}: [{rows}, >= {row_elems}] rows with unit column stride expected")
+    stride = int(t.stride(0)) if t.shape[0] > 1 else max(int(t.stride(0)), row_elems)
+    span = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    _need(span >= ((rows - 1) * stride + row_elems if rows else 0), f"{name}: storage too small for {rows} rows")
+    return stride
+
+
 def _state_ok(x, layer, name):
     if isinstance(x, int) or x is None:
         return
@@ -340,11 +364,12 @@ def _workspace(nbytes: int, device, workspace):
 
 def conv_update(layer: Layer, x, w, tails, cu_seqlens, start_pos, y, ckpt=None, page_ids=None,
                 workspace=None, stream=None, staging=None):
-    """Causal conv update (gdn_conv_update). tails: per sequence (kind, src, dst)."""
+    """Causal conv update (gdn_conv_update). tails: per sequence (kind, src, dst).  x may be
+    the leading C columns of wider packed rows (its row stride is passed through)."""
     v = _Varlens(cu_seqlens, start_pos)
     rows = int(cu_seqlens[-1]) if len(cu_seqlens) else 0
     C = layer.conv_channels
-    _rows_ok(x, rows, C, layer.io_dtype, "x")
+    xs = _strided_rows(x, rows, C, layer.io_dtype, "x")
     _rows_ok(y, rows, C, layer.io_dtype, "y")
     _rows_ok(w, C, layer.conv_width, layer.io_dtype, "w")
     _need(len(tails) == len(start_pos), "one tail reference per sequence")
@@ -357,7 +382,7 @@ def conv_update(layer: Layer, x, w, tails, cu_seqlens, start_pos, y, ckpt=None, 
     ck, keep = _ckpt_c(ckpt, page_ids)
     refs = _refs(tails)
     sg, sg_keep, wait = _staging(conv_staging_bytes(layer, cu_seqlens, start_pos, block), staging)
-    st = _lib.gdn_conv_update(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(v.c), _ptr(x), _ptr(w),
+    st = _lib.gdn_conv_update(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(v.c), _ptr(x), xs, _ptr(w),
                               refs, ctypes.byref(ck), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0,
                               ctypes.byref(sg) if sg is not None else None)
     _check(st, "gdn_conv_update")
@@ -368,20 +393,20 @@ def conv_update(layer: Layer, x, w, tails, cu_seqlens, start_pos, y, ckpt=None, 
 
 def conv_decode(layer: Layer, x, w, tail_pool, slot_ids, y, rows=None, status=None, stream=None):
     """The conv's decode regime (gdn_conv_decode): request r's new row is row rows[r] (or
-    r) of x [n_rows, C]; its previous rows are slot slot_ids[r] of tail_pool [n_slots,
+    r) of x [n_rows, >= C] (dense or packed rows); its previous rows are slot slot_ids[r] of tail_pool [n_slots,
     conv_width - 1, C], updated in place; y row rows[r] gets the conv output."""
     n_req = int(slot_ids.numel())
     C = layer.conv_channels
     n_rows = int(x.shape[0])
     _need(slot_ids.dtype == torch.int32 and (rows is None or (rows.dtype == torch.int32 and rows.numel() >= n_req)),
           "int32 slot_ids / rows")
-    _rows_ok(x, n_rows, C, layer.io_dtype, "x")
+    xs = _strided_rows(x, n_rows, C, layer.io_dtype, "x")
     _rows_ok(y, n_rows, C, layer.io_dtype, "y")
     _rows_ok(w, C, layer.conv_width, layer.io_dtype, "w")
     _need(rows is not None or n_rows >= n_req, "x: one row per request")
     _need(tail_pool.dtype == layer.io_dtype and tail_pool.is_contiguous()
           and tuple(tail_pool.shape[1:]) == (layer.conv_width - 1, C), "tail_pool: [slots, conv_width - 1, C]")
-    st = _lib.gdn_conv_decode(ctypes.byref(layer.c()), _stream(stream), n_req, n_rows, _ptr(x), _ptr(w),
+    st = _lib.gdn_conv_decode(ctypes.byref(layer.c()), _stream(stream), n_req, n_rows, _ptr(x), xs, _ptr(w),
                               _ptr(tail_pool), int(tail_pool.shape[0]), _ptr(slot_ids), _ptr(rows), _ptr(y),
                               _ptr(status))
     _check(st, "gdn_conv_decode")
@@ -584,6 +609,54 @@ def gated_norm(layer: Layer, o, z, weight, out, eps=1e-6, stream=None):
     st = _lib.gdn_gated_norm(ctypes.byref(layer.c()), _stream(stream), n, _ptr(o), _ptr(z2), int(z2.stride(0)),
                              _ptr(weight), float(eps), _ptr(out))
     _check(st, "gdn_gated_norm")
+
+
+def core_prefill_workspace_bytes(layer: Layer, cu_seqlens, start_pos, block: int) -> int:
+    v = _Varlens(cu_seqlens, start_pos)
+    return int(_lib.gdn_core_prefill_workspace_bytes(ctypes.byref(layer.c()), ctypes.byref(v.c), int(block)))
+
+
+def core_prefill_staging_bytes(layer: Layer, cu_seqlens, start_pos, block: int) -> int:
+    v = _Varlens(cu_seqlens, start_pos)
+    return int(_lib.gdn_core_prefill_staging_bytes(ctypes.byref(layer.c()), ctypes.byref(v.c), int(block)))
+
+
+def core_prefill(layer: Layer, qkvz, ba, conv_w, A_log, dt_bias, norm_weight, cu_seqlens, start_pos, tails, states,
+                 out, ckpt=None, page_ids=None, eps=1e-6, workspace=None, stream=None, staging=None):
+    """The packed core over a varlen batch (gdn_core_prefill): conv (+ q/k norm) over the
+    q|k|v channels of the packed qkvz rows, gates from ba, the chunked prefill, and the
+    gated norm with z from the packed rows.  qkvz [tokens, >= 2 Hqk d + 2 Hv d] and ba
+    [tokens, >= 2 Hv] rows (io dtype, unit column stride); tails / states per sequence
+    (kind, src, dst); out [tokens, Hv, d] io dtype."""
+    vl = _Varlens(cu_seqlens, start_pos)
+    rows = int(cu_seqlens[-1]) if len(cu_seqlens) else 0
+    D, Hv = layer.head_dim, layer.n_v_heads
+    C = layer.conv_channels
+    qs = _strided_rows(qkvz, rows, C + Hv * D, layer.io_dtype, "qkvz")
+    bs = _strided_rows(ba, rows, 2 * Hv, layer.io_dtype, "ba")
+    _rows_ok(conv_w, C, layer.conv_width, layer.io_dtype, "conv_w")
+    _need(A_log.dtype == torch.float32 and A_log.numel() == Hv, "A_log: fp32 [Hv]")
+    _need(dt_bias.dtype == layer.io_dtype and dt_bias.numel() == Hv, "dt_bias: io dtype [Hv]")
+    _need(norm_weight.dtype == layer.io_dtype and norm_weight.numel() == D, "norm_weight: io dtype [d]")
+    _rows_ok(out, rows, Hv * D, layer.io_dtype, "out")
+    _need(len(tails) == len(start_pos) and len(states) == len(start_pos), "one tail and one state per sequence")
+    for kind, src, dst in states:
+        if kind != "checkpoint":
+            _state_ok(src, layer, "state src")
+        _state_ok(dst, layer, "state dst")
+    block = ckpt.block if ckpt is not None else 0
+    ws = _workspace(core_prefill_workspace_bytes(layer, cu_seqlens, start_pos, block), qkvz.device, workspace)
+    ck, keep = _ckpt_c(ckpt, page_ids)
+    trefs, srefs = _refs(tails), _refs(states)
+    sg, sg_keep, wait = _staging(core_prefill_staging_bytes(layer, cu_seqlens, start_pos, block), staging)
+    st = _lib.gdn_core_prefill(ctypes.byref(layer.c()), _stream(stream), ctypes.byref(vl.c), _ptr(qkvz), qs,
+                               _ptr(ba), bs, _ptr(conv_w), _ptr(A_log), _ptr(dt_bias), _ptr(norm_weight),
+                               float(eps), trefs, srefs, ctypes.byref(ck), _ptr(out), _ptr(ws),
+                               ws.numel() if ws is not None else 0, ctypes.byref(sg) if sg is not None else None)
+    _check(st, "gdn_core_prefill")
+    if wait:
+        _sync(stream)
+    return ws
 
 
 def replay_forward(layer: Layer, state_pool, slot_ids, buf_k, buf_v, buf_a, buf_b, n_logged, n_new, q_new, o,

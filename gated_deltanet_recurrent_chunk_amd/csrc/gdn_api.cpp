@@ -203,6 +203,212 @@ gdn_status decode_rows(const LayerInfo& L, hipStream_t stream, int32_t n_req, in
   return hip_status(launch_decode(da, L.D, n_req, stream));
 }
 
+
+// A whole prefill call checked before anything is enqueued (gdn_chunk_prefill and the
+// prefill stage of gdn_core_prefill).
+gdn_status prep_prefill_call(const gdn_layer* layer, const gdn_varlen* varlen, const void* q, const void* k,
+                             const void* v, int64_t qk_stride, int64_t v_stride, const float* a, const float* b,
+                             const gdn_state_ref* states, const gdn_ckpt* ckpt, const float* o,
+                             const void* workspace, size_t workspace_bytes, const gdn_staging* staging,
+                             PrefillPrep* P) {
+  if (!ckpt) return GDN_ERR_NULL_ARG;
+  gdn_status s = prep_prefill(layer, varlen, ckpt->block, ckpt, P);
+  if (s != GDN_OK) return s;
+  s = check_qkv(P->L, q, k, v, qk_stride, v_stride, true, true);
+  if (s != GDN_OK) return s;
+  if (P->plan.n_units > 0 && (!a || !b || !o)) return GDN_ERR_NULL_ARG;
+  s = check_states(*P, states, ckpt->block);
+  if (s != GDN_OK) return s;
+  s = check_workspace(const_cast<void*>(workspace), workspace_bytes, P->plan.total_bytes);
+  if (s != GDN_OK) return s;
+  s = check_staging(P->plan, staging);
+  if (s != GDN_OK) return s;
+  set_state_refs(P, states);
+  return GDN_OK;
+}
+
+gdn_status launch_prefill_call(const PrefillPrep& P, hipStream_t stream, const void* q, const void* k,
+                               const void* v, int64_t qk_stride, int64_t v_stride, const float* a, const float* b,
+                               const gdn_ckpt* ckpt, float* o, void* workspace, const gdn_staging* staging) {
+  gdn_status s = stage_table(P.plan, staging, workspace, stream);
+  if (s != GDN_OK) return s;
+  if (P.L.io == GDN_BF16) {
+    s = do_factorize<bf16_bits>(P, stream, q, k, qk_stride, a, b, workspace);
+    if (s != GDN_OK) return s;
+    return do_scan<bf16_bits>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
+  }
+  s = do_factorize<float>(P, stream, q, k, qk_stride, a, b, workspace);
+  if (s != GDN_OK) return s;
+  return do_scan<float>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
+}
+
+// A conv call checked before anything is enqueued (gdn_conv_update and the conv stage
+// of gdn_core_prefill): the plan's entries carry the tail sources and destinations.
+struct ConvCall {
+  LayerInfo L;
+  std::vector<SeqSpan> spans;
+  CallPlan plan;
+};
+
+gdn_status prep_conv(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block, const gdn_ckpt* ckpt,
+                     LayerInfo* L, std::vector<SeqSpan>* spans, CallPlan* plan) {
+  gdn_status s = check_layer(layer, L);
+  if (s != GDN_OK) return s;
+  s = check_varlen(varlen, spans);
+  if (s != GDN_OK) return s;
+  if (block < 0) return GDN_ERR_BAD_SHAPE;
+  std::vector<int32_t> pages, page_begin;
+  if (ckpt) {
+    s = check_ckpt(ckpt, *L, *spans, &pages, &page_begin);
+    if (s != GDN_OK) return s;
+  }
+  return plan_call(*L, *spans, block, ckpt ? &pages : nullptr, ckpt ? &page_begin : nullptr, false, plan);
+}
+
+gdn_status prep_conv_call(const gdn_layer* layer, const gdn_varlen* varlen, const void* x, int64_t x_stride,
+                          const void* w, const gdn_state_ref* tails, const gdn_ckpt* ckpt, const void* y,
+                          const void* workspace, size_t workspace_bytes, const gdn_staging* staging, ConvCall* c) {
+  if (!ckpt) return GDN_ERR_NULL_ARG;
+  gdn_status s = prep_conv(layer, varlen, ckpt->block, ckpt, &c->L, &c->spans, &c->plan);
+  if (s != GDN_OK) return s;
+  const LayerInfo& L = c->L;
+  s = check_sources(tails, c->spans, ckpt->block);
+  if (s != GDN_OK) return s;
+  const int64_t total_rows = c->spans.empty() ? 0 : c->spans.back().row0 + c->spans.back().len;
+  if (total_rows > 0 && (!x || !y)) return GDN_ERR_NULL_ARG;
+  if (!w && !c->spans.empty()) return GDN_ERR_NULL_ARG;
+  // rows are read 16 bytes at a time: a stride of whole 16-byte groups
+  if (x_stride < L.channels || (x_stride * (int64_t)L.io_bytes) % 16 != 0) return GDN_ERR_BAD_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16)) return GDN_ERR_BAD_SHAPE;
+  for (size_t i = 0; i < c->spans.size(); ++i) {
+    if (tails[i].src_kind != GDN_SRC_ZERO && !aligned(tails[i].src, 16)) return GDN_ERR_BAD_SHAPE;
+    if (!aligned(tails[i].dst, 16)) return GDN_ERR_BAD_SHAPE;
+  }
+  if (c->plan.staged) {
+    s = check_workspace(const_cast<void*>(workspace), workspace_bytes, c->plan.table_bytes);
+    if (s != GDN_OK) return s;
+  }
+  s = check_staging(c->plan, staging);
+  if (s != GDN_OK) return s;
+  for (size_t i = 0; i < c->spans.size(); ++i) {
+    const gdn_state_ref& r = tails[i];
+    const uint8_t* src = static_cast<const uint8_t*>(r.src);
+    if (r.src_kind == GDN_SRC_ZERO) src = nullptr;
+    if (r.src_kind == GDN_SRC_CHECKPOINT) src += L.state_bytes;  // tail region of the page
+    c->plan.seqs[i].src = src;
+    c->plan.seqs[i].dst = r.dst;
+  }
+  return GDN_OK;
+}
+
+gdn_status launch_conv_call(const ConvCall& c, hipStream_t stream, const void* x, int64_t x_stride, const void* w,
+                            const gdn_ckpt* ckpt, void* y, void* workspace, const gdn_staging* staging) {
+  if (c.plan.n_units == 0) return GDN_OK;
+  gdn_status s = stage_table(c.plan, staging, workspace, stream);
+  if (s != GDN_OK) return s;
+  const LayerInfo& L = c.L;
+  auto fill = [&](auto& ca, auto tag) {
+    using IO = decltype(tag);
+    fill_call_table(c.plan, workspace, &ca.tab);
+    ca.x = static_cast<const IO*>(x);
+    ca.x_stride = x_stride;
+    ca.w = static_cast<const IO*>(w);
+    ca.y = static_cast<IO*>(y);
+    ca.ckpt_pool = static_cast<uint8_t*>(ckpt->pool);
+    ca.page_bytes = (size_t)ckpt->page_bytes;
+    ca.tail_offset = (size_t)L.state_bytes;
+    ca.channels = L.channels;
+    ca.qk_channels = 2 * (int64_t)L.Hqk * L.D;
+    ca.head_dim = L.D;
+    ca.act = L.act;
+  };
+  if (L.io == GDN_BF16) {
+    ConvArgs<bf16_bits> ca;
+    fill(ca, bf16_bits{});
+    return hip_status(launch_conv(ca, stream));
+  }
+  ConvArgs<float> ca;
+  fill(ca, float{});
+  return hip_status(launch_conv(ca, stream));
+}
+
+// The gates and the gated norm: checks, then launches.
+gdn_status check_gates(const LayerInfo& L, int64_t n_tokens, const void* ba, int64_t ba_stride, const float* A_log,
+                       const void* dt_bias, const float* a, const float* b) {
+  if (n_tokens < 0 || ba_stride < 2 * (int64_t)L.Hv) return GDN_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return GDN_OK;
+  if (!ba || !A_log || !dt_bias || !a || !b) return GDN_ERR_NULL_ARG;
+  return GDN_OK;
+}
+
+gdn_status launch_gates_call(const LayerInfo& L, hipStream_t stream, int64_t n_tokens, const void* ba,
+                             int64_t ba_stride, const float* A_log, const void* dt_bias, float* a, float* b) {
+  if (n_tokens == 0) return GDN_OK;
+  if (L.io == GDN_BF16) {
+    GateArgs<bf16_bits> ga{static_cast<const bf16_bits*>(ba), A_log, static_cast<const bf16_bits*>(dt_bias), a, b,
+                           n_tokens, ba_stride, L.Hv};
+    return hip_status(launch_gates(ga, stream));
+  }
+  GateArgs<float> ga{static_cast<const float*>(ba), A_log, static_cast<const float*>(dt_bias), a, b, n_tokens,
+                     ba_stride, L.Hv};
+  return hip_status(launch_gates(ga, stream));
+}
+
+gdn_status check_gated_norm(const LayerInfo& L, int64_t n_tokens, const float* o, const void* z, int64_t z_stride,
+                            const void* weight, float eps, const void* out) {
+  // z rows are read 16 bytes at a time: a stride of whole 8-element groups
+  if (n_tokens < 0 || z_stride < (int64_t)L.Hv * L.D || z_stride % 8 != 0 || !(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return GDN_OK;
+  if (!o || !z || !weight || !out) return GDN_ERR_NULL_ARG;
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(weight, 16) || !aligned(out, 16)) return GDN_ERR_BAD_SHAPE;
+  return GDN_OK;
+}
+
+gdn_status launch_gated_norm_call(const LayerInfo& L, hipStream_t stream, int64_t n_tokens, const float* o,
+                                  const void* z, int64_t z_stride, const void* weight, float eps, void* out) {
+  if (n_tokens == 0) return GDN_OK;
+  if (L.io == GDN_BF16) {
+    NormArgs<bf16_bits> na{o, static_cast<const bf16_bits*>(z), static_cast<const bf16_bits*>(weight),
+                           static_cast<bf16_bits*>(out), n_tokens * L.Hv, z_stride, L.Hv, eps};
+    return hip_status(launch_gated_norm(na, L.D, stream));
+  }
+  NormArgs<float> na{o, static_cast<const float*>(z), static_cast<const float*>(weight), static_cast<float*>(out),
+                     n_tokens * L.Hv, z_stride, L.Hv, eps};
+  return hip_status(launch_gated_norm(na, L.D, stream));
+}
+
+// Workspace and staging layout of gdn_core_prefill: the conv's staged table, the
+// prefill's workspace (its staged table, then the factor records), then the stage
+// outputs y [tokens][C] io, a and b [tokens][Hv] fp32, o [tokens][Hv][d] fp32, each
+// region 256-byte aligned.  Staging: the conv's table, then the prefill's.
+struct CoreLayout {
+  ConvCall conv;
+  PrefillPrep pre;
+  int64_t tokens = 0;
+  size_t off_prefill = 0, off_y = 0, off_a = 0, off_b = 0, off_o = 0, total = 0;
+  size_t stage_prefill = 0, stage_total = 0;
+};
+
+gdn_status core_layout(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block, const gdn_ckpt* ckpt,
+                       CoreLayout* c) {
+  gdn_status s = prep_conv(layer, varlen, block, ckpt, &c->conv.L, &c->conv.spans, &c->conv.plan);
+  if (s != GDN_OK) return s;
+  s = prep_prefill(layer, varlen, block, ckpt, &c->pre);
+  if (s != GDN_OK) return s;
+  const LayerInfo& L = c->conv.L;
+  c->tokens = c->conv.spans.empty() ? 0 : c->conv.spans.back().row0 + c->conv.spans.back().len;
+  const size_t T = (size_t)c->tokens;
+  c->off_prefill = align_up(c->conv.plan.staged ? c->conv.plan.table_bytes : 0);
+  c->off_y = align_up(c->off_prefill + c->pre.plan.total_bytes);
+  c->off_a = align_up(c->off_y + T * (size_t)L.channels * L.io_bytes);
+  c->off_b = align_up(c->off_a + T * (size_t)L.Hv * 4);
+  c->off_o = align_up(c->off_b + T * (size_t)L.Hv * 4);
+  c->total = align_up(c->off_o + T * (size_t)L.Hv * L.D * 4);
+  c->stage_prefill = align_up(c->conv.plan.staged ? c->conv.plan.table_bytes : 0);
+  c->stage_total = c->pre.plan.staged || c->conv.plan.staged ? c->stage_prefill + c->pre.plan.table_bytes : 0;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,22 +483,6 @@ int64_t gdn_prefill_staging_bytes(const gdn_layer* layer, const gdn_varlen* varl
   return (int64_t)P.plan.table_bytes;
 }
 
-namespace {
-gdn_status prep_conv(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block, const gdn_ckpt* ckpt,
-                     LayerInfo* L, std::vector<SeqSpan>* spans, CallPlan* plan) {
-  gdn_status s = check_layer(layer, L);
-  if (s != GDN_OK) return s;
-  s = check_varlen(varlen, spans);
-  if (s != GDN_OK) return s;
-  if (block < 0) return GDN_ERR_BAD_SHAPE;
-  std::vector<int32_t> pages, page_begin;
-  if (ckpt) {
-    s = check_ckpt(ckpt, *L, *spans, &pages, &page_begin);
-    if (s != GDN_OK) return s;
-  }
-  return plan_call(*L, *spans, block, ckpt ? &pages : nullptr, ckpt ? &page_begin : nullptr, false, plan);
-}
-}  // namespace
 
 int64_t gdn_conv_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block) {
   LayerInfo L;
@@ -354,30 +544,11 @@ gdn_status gdn_chunk_prefill(const gdn_layer* layer, hipStream_t stream, const g
                              const void* k, const void* v, int64_t qk_stride, int64_t v_stride, const float* a,
                              const float* b, const gdn_state_ref* states, const gdn_ckpt* ckpt, float* o,
                              void* workspace, size_t workspace_bytes, const gdn_staging* staging) {
-  if (!ckpt) return GDN_ERR_NULL_ARG;
   PrefillPrep P;
-  gdn_status s = prep_prefill(layer, varlen, ckpt->block, ckpt, &P);
+  gdn_status s = prep_prefill_call(layer, varlen, q, k, v, qk_stride, v_stride, a, b, states, ckpt, o, workspace,
+                                   workspace_bytes, staging, &P);
   if (s != GDN_OK) return s;
-  s = check_qkv(P.L, q, k, v, qk_stride, v_stride, true, true);
-  if (s != GDN_OK) return s;
-  if (P.plan.n_units > 0 && (!a || !b || !o)) return GDN_ERR_NULL_ARG;
-  s = check_states(P, states, ckpt->block);
-  if (s != GDN_OK) return s;
-  s = check_workspace(workspace, workspace_bytes, P.plan.total_bytes);
-  if (s != GDN_OK) return s;
-  s = check_staging(P.plan, staging);
-  if (s != GDN_OK) return s;
-  set_state_refs(&P, states);
-  s = stage_table(P.plan, staging, workspace, stream);
-  if (s != GDN_OK) return s;
-  if (P.L.io == GDN_BF16) {
-    s = do_factorize<bf16_bits>(P, stream, q, k, qk_stride, a, b, workspace);
-    if (s != GDN_OK) return s;
-    return do_scan<bf16_bits>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
-  }
-  s = do_factorize<float>(P, stream, q, k, qk_stride, a, b, workspace);
-  if (s != GDN_OK) return s;
-  return do_scan<float>(P, stream, q, k, v, qk_stride, v_stride, ckpt, o, workspace);
+  return launch_prefill_call(P, stream, q, k, v, qk_stride, v_stride, a, b, ckpt, o, workspace, staging);
 }
 
 gdn_status gdn_chunk_prefill_noalloc(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
@@ -410,72 +581,23 @@ gdn_status gdn_chunk_prefill_noalloc(const gdn_layer* layer, hipStream_t stream,
 }
 
 gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen, const void* x,
-                           const void* w, const gdn_state_ref* tails, const gdn_ckpt* ckpt, void* y,
-                           void* workspace, size_t workspace_bytes, const gdn_staging* staging) {
-  if (!ckpt) return GDN_ERR_NULL_ARG;
-  LayerInfo L;
-  std::vector<SeqSpan> spans;
-  CallPlan plan;
-  gdn_status s = prep_conv(layer, varlen, ckpt->block, ckpt, &L, &spans, &plan);
+                           int64_t x_stride, const void* w, const gdn_state_ref* tails, const gdn_ckpt* ckpt,
+                           void* y, void* workspace, size_t workspace_bytes, const gdn_staging* staging) {
+  ConvCall c;
+  gdn_status s = prep_conv_call(layer, varlen, x, x_stride, w, tails, ckpt, y, workspace, workspace_bytes, staging,
+                                &c);
   if (s != GDN_OK) return s;
-  s = check_sources(tails, spans, ckpt->block);
-  if (s != GDN_OK) return s;
-  const int64_t total_rows = spans.empty() ? 0 : spans.back().row0 + spans.back().len;
-  if (total_rows > 0 && (!x || !y)) return GDN_ERR_NULL_ARG;
-  if (!w && !spans.empty()) return GDN_ERR_NULL_ARG;
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16)) return GDN_ERR_BAD_SHAPE;
-  for (size_t i = 0; i < spans.size(); ++i) {
-    if (tails[i].src_kind != GDN_SRC_ZERO && !aligned(tails[i].src, 16)) return GDN_ERR_BAD_SHAPE;
-    if (!aligned(tails[i].dst, 16)) return GDN_ERR_BAD_SHAPE;
-  }
-  if (plan.staged) {
-    s = check_workspace(workspace, workspace_bytes, plan.table_bytes);
-    if (s != GDN_OK) return s;
-  }
-  s = check_staging(plan, staging);
-  if (s != GDN_OK) return s;
-  if (plan.n_units == 0) return GDN_OK;
-  for (size_t i = 0; i < spans.size(); ++i) {
-    const gdn_state_ref& r = tails[i];
-    const uint8_t* src = static_cast<const uint8_t*>(r.src);
-    if (r.src_kind == GDN_SRC_ZERO) src = nullptr;
-    if (r.src_kind == GDN_SRC_CHECKPOINT) src += L.state_bytes;  // tail region of the page
-    plan.seqs[i].src = src;
-    plan.seqs[i].dst = r.dst;
-  }
-  s = stage_table(plan, staging, workspace, stream);
-  if (s != GDN_OK) return s;
-  auto fill = [&](auto& ca, auto tag) {
-    using IO = decltype(tag);
-    fill_call_table(plan, workspace, &ca.tab);
-    ca.x = static_cast<const IO*>(x);
-    ca.w = static_cast<const IO*>(w);
-    ca.y = static_cast<IO*>(y);
-    ca.ckpt_pool = static_cast<uint8_t*>(ckpt->pool);
-    ca.page_bytes = (size_t)ckpt->page_bytes;
-    ca.tail_offset = (size_t)L.state_bytes;
-    ca.channels = L.channels;
-    ca.qk_channels = 2 * (int64_t)L.Hqk * L.D;
-    ca.head_dim = L.D;
-    ca.act = L.act;
-  };
-  if (L.io == GDN_BF16) {
-    ConvArgs<bf16_bits> ca;
-    fill(ca, bf16_bits{});
-    return hip_status(launch_conv(ca, stream));
-  }
-  ConvArgs<float> ca;
-  fill(ca, float{});
-  return hip_status(launch_conv(ca, stream));
+  return launch_conv_call(c, stream, x, x_stride, w, ckpt, y, workspace, staging);
 }
 
 gdn_status gdn_conv_decode(const gdn_layer* layer, hipStream_t stream, int32_t n_req, int64_t n_rows,
-                           const void* x, const void* w, void* tail_pool, int64_t n_slots, const int32_t* slot_ids,
-                           const int32_t* rows, void* y, int32_t* status) {
+                           const void* x, int64_t x_stride, const void* w, void* tail_pool, int64_t n_slots,
+                           const int32_t* slot_ids, const int32_t* rows, void* y, int32_t* status) {
   LayerInfo L;
   gdn_status s = check_layer(layer, &L);
   if (s != GDN_OK) return s;
   if (n_req < 0 || n_slots < 0 || n_rows < 0) return GDN_ERR_BAD_SHAPE;
+  if (x_stride < L.channels || (x_stride * (int64_t)L.io_bytes) % 16 != 0) return GDN_ERR_BAD_SHAPE;
   if (n_req == 0) return GDN_OK;
   if (!x || !w || !tail_pool || !slot_ids || !y) return GDN_ERR_NULL_ARG;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(tail_pool, 16) || !aligned(y, 16)) return GDN_ERR_BAD_SHAPE;
@@ -483,6 +605,7 @@ gdn_status gdn_conv_decode(const gdn_layer* layer, hipStream_t stream, int32_t n
   auto fill = [&](auto& ca, auto tag) {
     using IO = decltype(tag);
     ca.x = static_cast<const IO*>(x);
+    ca.x_stride = x_stride;
     ca.w = static_cast<const IO*>(w);
     ca.y = static_cast<IO*>(y);
     ca.tail_pool = static_cast<IO*>(tail_pool);
@@ -570,17 +693,9 @@ gdn_status gdn_gates(const gdn_layer* layer, hipStream_t stream, int64_t n_token
   LayerInfo L;
   gdn_status s = check_layer(layer, &L);
   if (s != GDN_OK) return s;
-  if (n_tokens < 0 || ba_stride < 2 * (int64_t)L.Hv) return GDN_ERR_BAD_SHAPE;
-  if (n_tokens == 0) return GDN_OK;
-  if (!ba || !A_log || !dt_bias || !a || !b) return GDN_ERR_NULL_ARG;
-  if (L.io == GDN_BF16) {
-    GateArgs<bf16_bits> ga{static_cast<const bf16_bits*>(ba), A_log, static_cast<const bf16_bits*>(dt_bias), a, b,
-                           n_tokens, ba_stride, L.Hv};
-    return hip_status(launch_gates(ga, stream));
-  }
-  GateArgs<float> ga{static_cast<const float*>(ba), A_log, static_cast<const float*>(dt_bias), a, b, n_tokens,
-                     ba_stride, L.Hv};
-  return hip_status(launch_gates(ga, stream));
+  s = check_gates(L, n_tokens, ba, ba_stride, A_log, dt_bias, a, b);
+  if (s != GDN_OK) return s;
+  return launch_gates_call(L, stream, n_tokens, ba, ba_stride, A_log, dt_bias, a, b);
 }
 
 gdn_status gdn_gated_norm(const gdn_layer* layer, hipStream_t stream, int64_t n_tokens, const float* o,
@@ -588,19 +703,77 @@ gdn_status gdn_gated_norm(const gdn_layer* layer, hipStream_t stream, int64_t n_
   LayerInfo L;
   gdn_status s = check_layer(layer, &L);
   if (s != GDN_OK) return s;
-  // z rows are read 16 bytes at a time: a stride of whole 8-element groups
-  if (n_tokens < 0 || z_stride < (int64_t)L.Hv * L.D || z_stride % 8 != 0 || !(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
-  if (n_tokens == 0) return GDN_OK;
-  if (!o || !z || !weight || !out) return GDN_ERR_NULL_ARG;
-  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(weight, 16) || !aligned(out, 16)) return GDN_ERR_BAD_SHAPE;
-  if (L.io == GDN_BF16) {
-    NormArgs<bf16_bits> na{o, static_cast<const bf16_bits*>(z), static_cast<const bf16_bits*>(weight),
-                           static_cast<bf16_bits*>(out), n_tokens * L.Hv, z_stride, L.Hv, eps};
-    return hip_status(launch_gated_norm(na, L.D, stream));
+  s = check_gated_norm(L, n_tokens, o, z, z_stride, weight, eps, out);
+  if (s != GDN_OK) return s;
+  return launch_gated_norm_call(L, stream, n_tokens, o, z, z_stride, weight, eps, out);
+}
+
+int64_t gdn_core_prefill_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block) {
+  CoreLayout c;
+  if (core_layout(layer, varlen, block, nullptr, &c) != GDN_OK) return -1;
+  return (int64_t)c.total;
+}
+
+int64_t gdn_core_prefill_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block) {
+  CoreLayout c;
+  if (core_layout(layer, varlen, block, nullptr, &c) != GDN_OK) return -1;
+  return (int64_t)c.stage_total;
+}
+
+gdn_status gdn_core_prefill(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen, const void* qkvz,
+                            int64_t qkvz_stride, const void* ba, int64_t ba_stride, const void* conv_w,
+                            const float* A_log, const void* dt_bias, const void* norm_weight, float eps,
+                            const gdn_state_ref* tails, const gdn_state_ref* states, const gdn_ckpt* ckpt,
+                            void* out, void* workspace, size_t workspace_bytes, const gdn_staging* staging) {
+  if (!ckpt) return GDN_ERR_NULL_ARG;
+  CoreLayout c;
+  gdn_status s = core_layout(layer, varlen, ckpt->block, ckpt, &c);
+  if (s != GDN_OK) return s;
+  const LayerInfo& L = c.conv.L;
+  if (c.tokens > 0 && !qkvz) return GDN_ERR_NULL_ARG;
+  if (qkvz_stride < L.channels + (int64_t)L.Hv * L.D) return GDN_ERR_BAD_SHAPE;
+  s = check_workspace(workspace, workspace_bytes, c.total);
+  if (s != GDN_OK) return s;
+  if (c.stage_total > 0 && (!staging || !staging->host || staging->bytes < c.stage_total)) return GDN_ERR_STAGING;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* y = ws + c.off_y;
+  float* a = reinterpret_cast<float*>(ws + c.off_a);
+  float* b = reinterpret_cast<float*>(ws + c.off_b);
+  float* o = reinterpret_cast<float*>(ws + c.off_o);
+  void* pre_ws = ws + c.off_prefill;
+  gdn_staging conv_stage{}, pre_stage{};
+  if (c.stage_total > 0) {
+    conv_stage = gdn_staging{staging->host, c.stage_prefill};
+    pre_stage = gdn_staging{static_cast<uint8_t*>(staging->host) + c.stage_prefill, staging->bytes - c.stage_prefill};
   }
-  NormArgs<float> na{o, static_cast<const float*>(z), static_cast<const float*>(weight), static_cast<float*>(out),
-                     n_tokens * L.Hv, z_stride, L.Hv, eps};
-  return hip_status(launch_gated_norm(na, L.D, stream));
+  // every stage checked before the first is enqueued
+  const size_t io = L.io_bytes;
+  const uint8_t* row = static_cast<const uint8_t*>(qkvz);
+  const int64_t qk = (int64_t)L.Hqk * L.D;
+  const uint8_t* yb = static_cast<const uint8_t*>(y);
+  ConvCall cc;
+  s = prep_conv_call(layer, varlen, qkvz, qkvz_stride, conv_w, tails, ckpt, y, ws,
+                     c.conv.plan.staged ? c.conv.plan.table_bytes : 0, &conv_stage, &cc);
+  if (s != GDN_OK) return s;
+  s = check_gates(L, c.tokens, ba, ba_stride, A_log, dt_bias, a, b);
+  if (s != GDN_OK) return s;
+  PrefillPrep P;
+  s = prep_prefill_call(layer, varlen, yb, yb + qk * io, yb + 2 * qk * io, L.channels, L.channels, a, b, states,
+                        ckpt, o, pre_ws, c.pre.plan.total_bytes, &pre_stage, &P);
+  if (s != GDN_OK) return s;
+  const void* z = row ? row + L.channels * io : nullptr;
+  s = check_gated_norm(L, c.tokens, o, z, qkvz_stride, norm_weight, eps, out);
+  if (s != GDN_OK) return s;
+  // conv (+ q/k norm) -> gates -> prefill (q, k, v read in place from the conv rows) ->
+  // gated norm (z read in place from the packed rows)
+  s = launch_conv_call(cc, stream, qkvz, qkvz_stride, conv_w, ckpt, y, ws, &conv_stage);
+  if (s != GDN_OK) return s;
+  s = launch_gates_call(L, stream, c.tokens, ba, ba_stride, A_log, dt_bias, a, b);
+  if (s != GDN_OK) return s;
+  s = launch_prefill_call(P, stream, yb, yb + qk * io, yb + 2 * qk * io, L.channels, L.channels, a, b, ckpt, o,
+                          pre_ws, &pre_stage);
+  if (s != GDN_OK) return s;
+  return launch_gated_norm_call(L, stream, c.tokens, o, z, qkvz_stride, norm_weight, eps, out);
 }
 
 gdn_status gdn_replay_forward(const gdn_layer* layer, hipStream_t stream, int32_t n_req, const float* state_pool,

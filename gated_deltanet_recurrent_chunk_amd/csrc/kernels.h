@@ -110,7 +110,8 @@ struct DecodeArgs {
 template <typename IO>
 struct ConvArgs {
   CallTable tab;  // units = tiles of kConvTile rows; src / dst are the tails
-  const IO* x;
+  const IO* x;          // row t at x + t * x_stride
+  int64_t x_stride;     // elements, >= channels (the packed qkvz row width, or channels)
   const IO* w;
   IO* y;
   uint8_t* ckpt_pool;
@@ -124,7 +125,8 @@ struct ConvArgs {
 
 template <typename IO>
 struct ConvDecodeArgs {
-  const IO* x;           // row t at x + t * channels
+  const IO* x;           // row t at x + t * x_stride
+  int64_t x_stride;      // elements, >= channels
   const IO* w;           // [channels][4]
   IO* y;                 // row t at y + t * channels
   IO* tail_pool;         // [n_slots][3][channels], updated in place

@@ -206,13 +206,13 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
   // the tile's sequence, and its rows [rel0, rel0 + n) within it
   const_table* tab = kernarg_table();
   const SeqEntry sq = seq_entry(tab, unit_sequence(tab, tix));
-  const int64_t C = p.channels;
+  const int64_t C = p.channels, XS = p.x_stride;
   const int64_t rel0 = (int64_t)(tix - sq.unit0) * TR;
   const int n = (int)min((int64_t)TR, (int64_t)sq.len - rel0);
   const int64_t tile_row = sq.row0 + rel0;
   const IO* src = reinterpret_cast<const IO*>(sq.src);
   auto row_ptr = [&](int64_t rel) -> const uint4* {
-    if (rel >= 0) return reinterpret_cast<const uint4*>(p.x + (sq.row0 + rel) * C + c0);
+    if (rel >= 0) return reinterpret_cast<const uint4*>(p.x + (sq.row0 + rel) * XS + c0);
     if (src) return reinterpret_cast<const uint4*>(src + (3 + rel) * C + c0);
     return nullptr;  // zero rows: never read
   };
@@ -221,11 +221,11 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs<IO> p) {
   uint4 raw[TR + 3];
   if (rel0 >= 3) {
     // a running row pointer (no 64-bit multiply per row); rows past the tile repeat its last
-    const IO* ptr = p.x + (sq.row0 + rel0 - 3) * C + c0;
+    const IO* ptr = p.x + (sq.row0 + rel0 - 3) * XS + c0;
 #pragma unroll
     for (int i = 0; i < TR + 3; ++i) {
       raw[i] = *reinterpret_cast<const uint4*>(ptr);
-      if (i + 1 < n + 3) ptr += C;
+      if (i + 1 < n + 3) ptr += XS;
     }
   } else {
 #pragma unroll
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void conv_decode_kernel(ConvDecodeArgs<IO> p) 
   const uint4 t0 = *reinterpret_cast<const uint4*>(tail);
   const uint4 t1 = *reinterpret_cast<const uint4*>(tail + C);
   const uint4 t2 = *reinterpret_cast<const uint4*>(tail + 2 * C);
-  const uint4 xr = *reinterpret_cast<const uint4*>(p.x + row * C + c0);
+  const uint4 xr = *reinterpret_cast<const uint4*>(p.x + row * p.x_stride + c0);
   float wr[4 * VEC];
   load_vec<IO, 4 * VEC>(p.w + c0 * 4, wr);
   float x0[VEC], x1[VEC], x2[VEC], x3[VEC], yv[VEC];

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -239,7 +239,9 @@ int64_t gdn_conv_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
 /* Short causal conv update over a varlen batch ("Hybrid linear attention (gated
  * DeltaNet)", section "The part that is easy to get wrong": gdn_conv_prefill /
  * gdn_conv_decode).
- *   x  [tokens][C] io_dtype, C = gdn_conv_channels (packed q | k | v channels)
+ *   x  row t at x + t * x_stride: C io_dtype values, C = gdn_conv_channels (the packed
+ *      q | k | v channels); x_stride >= C elements, x_stride * io bytes a multiple of 16
+ *      (C for dense rows, the packed qkvz row width to read the in-projection in place)
  *   w  [C][conv_width] io_dtype; w[c][conv_width-1] multiplies the current token
  *   y  [tokens][C] io_dtype: act(sum_j w[c][j] * x[t - (W-1) + j][c]), fp32 sums,
  *      rounded to io_dtype with round-to-nearest-even
@@ -250,7 +252,7 @@ int64_t gdn_conv_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen,
  *      to the tail region of that boundary's page.
  * x and y must not overlap.  Errors: see gdn_status. */
 gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
-                           const void* x, const void* w, const gdn_state_ref* tails,
+                           const void* x, int64_t x_stride, const void* w, const gdn_state_ref* tails,
                            const gdn_ckpt* ckpt, void* y, void* workspace,
                            size_t workspace_bytes, const gdn_staging* staging);
 
@@ -261,7 +263,8 @@ gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn
  *   y[t][c] = act(w[c][0] tail[0][c] + w[c][1] tail[1][c] + w[c][2] tail[2][c] + w[c][3] x[t][c])
  * (the GDN_CONV_QK_L2NORM flag normalises the q and k heads as in gdn_conv_update), and
  * the slot becomes (tail[1], tail[2], x[t]).
- *   x, y [n_rows][C] io_dtype (the packed rows of a batch; C = gdn_conv_channels);
+ *   x: row t at x + t * x_stride (x_stride as in gdn_conv_update); y [n_rows][C]
+ *   io_dtype (the packed rows of a batch; C = gdn_conv_channels);
  *   w [C][conv_width]; tail_pool [n_slots][conv_width - 1][C] io_dtype, updated in place;
  *   slot_ids, rows [n_req] int32 (device).  Slot -1 reads and writes nothing; a slot
  *   outside [-1, n_slots) or a row outside [0, n_rows) leaves the request untouched and
@@ -269,8 +272,9 @@ gdn_status gdn_conv_update(const gdn_layer* layer, hipStream_t stream, const gdn
  *   share a slot.  No checkpoint tail is written: after a token that ends a block, the
  *   slot holds exactly that block's tail. */
 gdn_status gdn_conv_decode(const gdn_layer* layer, hipStream_t stream, int32_t n_req, int64_t n_rows,
-                           const void* x, const void* w, void* tail_pool, int64_t n_slots,
-                           const int32_t* slot_ids, const int32_t* rows, void* y, int32_t* status);
+                           const void* x, int64_t x_stride, const void* w, void* tail_pool,
+                           int64_t n_slots, const int32_t* slot_ids, const int32_t* rows, void* y,
+                           int32_t* status);
 
 /* Chunked varlen prefill of the gated delta rule with block checkpoints ("Hybrid
  * linear attention (gated DeltaNet)", "The part that is easy to get wrong":
@@ -411,6 +415,39 @@ gdn_status gdn_gates(const gdn_layer* layer, hipStream_t stream, int64_t n_token
  *   o, z, weight, out 16-byte aligned; eps >= 0. */
 gdn_status gdn_gated_norm(const gdn_layer* layer, hipStream_t stream, int64_t n_tokens, const float* o,
                           const void* z, int64_t z_stride, const void* weight, float eps, void* out);
+
+/* The packed core over a varlen batch ("Hybrid linear attention (gated DeltaNet)",
+ * "Packed-core traces": its input is the packed qkvz rows plus the "ba" projection, its
+ * output the gated-normalized value rows; it owns the conv taps, dt_bias, the fp32 A_log
+ * and the norm scale).  One call enqueues, on `stream`:
+ *   gdn_conv_update over the q | k | v channels of each packed row (the layer's
+ *   activation and q/k norm flags apply) -> gdn_gates over ba -> gdn_chunk_prefill on
+ *   q, k, v read in place from the conv's rows -> gdn_gated_norm with z read in place
+ *   from the packed rows;
+ * each stage exactly as that call defines it.  Everything is checked before the first
+ * stage is enqueued.
+ *   qkvz: row t at qkvz + t * qkvz_stride holds [q (n_qk_heads*d) | k (n_qk_heads*d) |
+ *     v (n_v_heads*d) | z (n_v_heads*d)] io_dtype; qkvz_stride >= C + n_v_heads*d
+ *     (C = gdn_conv_channels), qkvz_stride * io bytes a multiple of 16, qkvz 16-byte
+ *     aligned.  (The pages give no layout inside the packed row; this one is the plain
+ *     concatenation in the order of the name.)
+ *   ba: row t at ba + t * ba_stride, [b (n_v_heads) | a (n_v_heads)] io_dtype.
+ *   conv_w [C][conv_width], A_log [n_v_heads] fp32, dt_bias [n_v_heads] and
+ *     norm_weight [d] io_dtype; eps as in gdn_gated_norm.
+ *   tails, states [host]: per sequence, the conv tail and the state references of
+ *     gdn_conv_update and gdn_chunk_prefill; ckpt: as there (each crossed boundary's
+ *     page receives both the state and the tail).
+ *   out [tokens][n_v_heads][d] io_dtype.
+ *   workspace: gdn_core_prefill_workspace_bytes (256-byte aligned; it holds the stage
+ *     outputs), staging: gdn_core_prefill_staging_bytes (may be NULL when 0). */
+int64_t gdn_core_prefill_workspace_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block);
+int64_t gdn_core_prefill_staging_bytes(const gdn_layer* layer, const gdn_varlen* varlen, int32_t block);
+gdn_status gdn_core_prefill(const gdn_layer* layer, hipStream_t stream, const gdn_varlen* varlen,
+                            const void* qkvz, int64_t qkvz_stride, const void* ba, int64_t ba_stride,
+                            const void* conv_w, const float* A_log, const void* dt_bias,
+                            const void* norm_weight, float eps, const gdn_state_ref* tails,
+                            const gdn_state_ref* states, const gdn_ckpt* ckpt, void* out,
+                            void* workspace, size_t workspace_bytes, const gdn_staging* staging);
 
 /* ReplaySSM verification outputs ("Caching less to serve more requests", section "What
  * we changed": each request keeps one state and a log of the per-token inputs since it,

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert declared == set(g.EXPORTED)
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
 
 
 def test_helpers_match_page_figures():
@@ -199,6 +199,81 @@ def test_conv_validation_errors():
                 page_ids=[0, 1, 2], stream=0) == "GDN_ERR_OFF_BOUNDARY"
     assert _err(g.conv_update, layer, x, w, [("slot", None, t)], [0, 20], [4], x,
                 stream=0) == "GDN_ERR_NULL_ARG"
+
+
+def _aligned_bytes(n):
+    raw = torch.zeros(n + 256, dtype=torch.uint8)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + n]
+
+
+def test_conv_rejects_a_row_stride_below_the_channels_or_off_16_bytes():
+    layer = g.Layer(1, 1, 16, torch.bfloat16)
+    C = layer.conv_channels
+    w = torch.zeros(C, 4, dtype=torch.bfloat16)
+    t = torch.zeros(3, C, dtype=torch.bfloat16)
+    y = torch.zeros(20, C, dtype=torch.bfloat16)
+    wide = torch.zeros(20, C + 4, dtype=torch.bfloat16)  # 8-byte row padding: loads would straddle
+    assert _err(g.conv_update, layer, wide[:, :C], w, [("zero", None, t)], [0, 20], [0], y,
+                stream=0) == "GDN_ERR_BAD_SHAPE"
+    pool = torch.zeros(2, 3, C, dtype=torch.bfloat16)
+    slots = torch.zeros(2, dtype=torch.int32)
+    assert _err(g.conv_decode, layer, wide[:, :C], w, pool, slots, y, stream=0) == "GDN_ERR_BAD_SHAPE"
+
+
+def test_core_prefill_validation_errors():
+    """The packed core checks all four stages before anything is enqueued."""
+    Hqk, Hv, D = 1, 2, 16
+    layer = g.Layer(Hqk, Hv, D, torch.bfloat16, conv_act=g.ACT_SILU | g.CONV_QK_L2NORM)
+    C = layer.conv_channels
+    T = 40
+    qkvz = torch.zeros(T, C + Hv * D, dtype=torch.bfloat16)
+    ba = torch.zeros(T, 2 * Hv, dtype=torch.bfloat16)
+    w = torch.zeros(C, 4, dtype=torch.bfloat16)
+    A_log = torch.zeros(Hv)
+    dtb = torch.zeros(Hv, dtype=torch.bfloat16)
+    wn = torch.ones(D, dtype=torch.bfloat16)
+    S = torch.zeros(Hv, D, D)
+    tl = torch.zeros(3, C, dtype=torch.bfloat16)
+    out = torch.zeros(T, Hv, D, dtype=torch.bfloat16)
+    ck = _aligned_pool(4, layer.checkpoint_bytes, 16)
+    ws = _aligned_bytes(g.core_prefill_workspace_bytes(layer, [0, T], [0], 16))
+    args = (layer, qkvz, ba, w, A_log, dtb, wn)
+    zero = ([("zero", None, tl)], [("zero", None, S)])
+    # a checkpoint resume off the block grid (the conv stage's tail source is checked first)
+    src = ck.page_ptr(3)
+    assert _err(g.core_prefill, *args, [0, T], [8], [("checkpoint", src, tl)], [("checkpoint", src, S)], out,
+                ckpt=ck, page_ids=[0, 1, 2], workspace=ws, stream=0) == "GDN_ERR_OFF_BOUNDARY"
+    # a zero state source at a non-zero position (the prefill stage's check)
+    assert _err(g.core_prefill, *args, [0, T], [16], [("slot", tl, tl)], [("zero", None, S)], out,
+                ckpt=ck, page_ids=[0, 1, 2], workspace=ws, stream=0) == "GDN_ERR_OFF_BOUNDARY"
+    # workspace too small
+    assert _err(g.core_prefill, *args, [0, T], [0], *zero, out, ckpt=ck, page_ids=[0, 1],
+                workspace=ws[:-256], stream=0) == "GDN_ERR_WORKSPACE"
+    # a negative norm epsilon (the gated-norm stage's check)
+    assert _err(g.core_prefill, *args, [0, T], [0], *zero, out, ckpt=ck, page_ids=[0, 1], eps=-1.0,
+                workspace=ws, stream=0) == "GDN_ERR_BAD_SHAPE"
+    # ten sequences need staging: an empty buffer is refused
+    cu = list(range(0, 41, 4))
+    assert _err(g.core_prefill, *args, cu, [0] * 10, [("zero", None, tl)] * 10, [("zero", None, S)] * 10, out,
+                ckpt=ck, page_ids=[], workspace=_aligned_bytes(g.core_prefill_workspace_bytes(layer, cu, [0] * 10, 16)),
+                staging=torch.empty(0, dtype=torch.uint8), stream=0) == "GDN_ERR_STAGING"
+    # packed rows too narrow for q | k | v | z (the binding refuses them)
+    with pytest.raises(ValueError):
+        g.core_prefill(layer, qkvz[:, :C], ba, w, A_log, dtb, wn, [0, T], [0], *zero, out, ckpt=ck, page_ids=[0, 1],
+                       workspace=ws, stream=0)
+    assert not out.any() and not S.any() and not tl.any() and not ck.pool.any()
+
+
+def test_core_prefill_workspace_holds_every_stage_output():
+    layer = g.Layer(2, 4, 128, torch.bfloat16)
+    cu, sp, block = [0, 300, 301], [0, 896], 896
+    need = g.core_prefill_workspace_bytes(layer, cu, sp, block)
+    T, C, Hv, D = 301, layer.conv_channels, 4, 128
+    stage_outputs = T * C * 2 + 2 * T * Hv * 4 + T * Hv * D * 4
+    assert need >= g.prefill_workspace_bytes(layer, cu, sp, block) + stage_outputs
+    assert need <= g.prefill_workspace_bytes(layer, cu, sp, block) + stage_outputs + 5 * 256
+    assert g.core_prefill_staging_bytes(layer, cu, sp, block) == 0
 
 
 # ------------------------------------------------------------------ no library state
