@@ -32,7 +32,14 @@ using namespace chunk;
 // at once.  (A 16-row block measured slower than this 32-row one, and a 64-row block,
 // at 256 VGPRs and twice the LDS, ran in two rounds of workgroups.)  The state is read
 // non-temporal and written through to device scope (store16_through).
-template <typename IO, int D>
+//
+// Logs of more than 32 slots (TWO): a second block's factorization does not depend on
+// the state, so its keys and gates are loaded with the first block's; wave 1 factorizes
+// it into its own LDS while wave 0 factorizes the first, and the other waves transpose
+// its keys meanwhile.  Its values are requested once the first block's are staged and
+// are written, as bf16, over its A once the factorizations are done, so its products
+// follow the first block's after a single barrier.
+template <typename IO, int D, bool TWO>
 __global__ __launch_bounds__(64 * (D / 16), (sizeof(IO) == 2 && D >= 64) ? 4 : 1)
 void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<IO> p) {
   constexpr int CT = 32;
@@ -44,6 +51,8 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int PER_ROW = D / VEC;
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + NTH - 1) / NTH;
+  // TWO puts three roles on the waves: wave 0, wave 1 and the rest
+  static_assert(!TWO || NW >= 3, "the two-block form needs head dim >= 64");
 
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
   __shared__ __attribute__((aligned(16))) bf16_bits KTs[NTI * D * TP];
@@ -52,6 +61,20 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
   __shared__ __attribute__((aligned(16))) float vec[4 * CT];
   __shared__ float vec_tmp[2 * CT];
+  // the second block's keys, factorization and gate vectors (TWO)
+  constexpr int C2 = TWO ? CT : 1;
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks2[NTI * C2 * KP];
+  __shared__ __attribute__((aligned(16))) bf16_bits KTs2[NTI * (TWO ? D : 1) * TP];
+  // As2 holds the second block's A until its factorization is done, then its values
+  // (bf16 rows of V2P elements, padded so that rows four apart fall in other banks)
+  constexpr int V2P = D + 2;
+  constexpr int A2W = (CT * V2P / 2 > CT * (CT + 4)) ? CT * V2P / 2 : CT * (CT + 4);
+  __shared__ __attribute__((aligned(16))) float As2buf[TWO ? A2W : CT + 4];
+  float(*const As2)[CT + 4] = reinterpret_cast<float(*)[CT + 4]>(As2buf);
+  bf16_bits* const V2 = reinterpret_cast<bf16_bits*>(As2buf);
+  __shared__ __attribute__((aligned(16))) bf16_bits Ts2[NTF * C2 * TP];
+  __shared__ __attribute__((aligned(16))) float vec2[4 * C2];
+  __shared__ float vec_tmp2[2 * C2];
 
   // head-major grid: consecutive workgroups take consecutive heads of one request, so
   // they sweep that request's contiguous state block in address order
@@ -75,6 +98,7 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   const int my_row = wave * 16 + col;
   float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
   if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), tid, NTH);  // padding columns, never written
+  if constexpr (D < 32 && TWO) zero_lds(Ks2, sizeof(Ks2), tid, NTH);
 
   // rows c0 .. c0 + nc - 1 of the slot's log: the gates (wave 0) first, since the
   // factorization waits for them, then keys and values
@@ -99,6 +123,31 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
     }
   };
   load_rows(0, n < CT ? n : CT);
+  // TWO: the second block's keys (all waves) and gates (wave 1), with the first block's
+  const int n2 = TWO && n > CT ? n - CT : 0;
+  uint4 kv2[TWO ? PER_THR : 1];
+  float a2_row = 0.f, b2 = 0.f;
+  if constexpr (TWO) {
+    if (n2 > 0) {
+    if (wave == 1 && lane < n2) {
+      const size_t ai = (row0 + CT + lane) * p.Hv + h;
+      a2_row = p.buf_a[ai];
+      b2 = p.buf_b[ai];
+    }
+#pragma unroll
+    for (int i = 0; i < PER_THR; ++i) {
+      const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+      kv2[i] = load16(kb + (size_t)(CT + t) * p.Hqk * D + j0, idx < PIECES && t < n2);
+    }
+    }
+  }
+  auto load_values = [&](int c0, int nc) {
+#pragma unroll
+    for (int i = 0; i < PER_THR; ++i) {
+      const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+      vv[i] = load16(vb + (size_t)(c0 + t) * p.Hv * D + j0, idx < PIECES && t < nc);
+    }
+  };
   // then the state: loads complete in issue order, so waiting for the rows (to stage
   // them) leaves the state loads in flight until the products need them
   f32x4 S[DT];
@@ -109,35 +158,74 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   // one block of rows c0 .. c0 + nc - 1; written out twice below rather than as a loop,
   // which would hoist every LDS address of the products out of it and hold them all in
   // registers
-  auto apply_block = [&](const int c0, const int nc) {
+  auto apply_block = [&](const int c0, const int nc, auto pre_) {
+    // PRE: the second block of TWO, factorized with the first; its keys are in Ks2
+    constexpr bool PRE = decltype(pre_)::value;
+    const bf16_bits* Kb = PRE ? Ks2 : Ks;
+    const bf16_bits* Tb = PRE ? Ts2 : Ts;
+    const float* vb_ = PRE ? vec2 : vec;
     // the previous block's readers are done with the LDS (first block: the zero fill,
-    // d < 32, precedes the row stores)
+    // d < 32, precedes the row stores; PRE: the second block's values are in V2)
     lds_barrier();
+    if constexpr (!PRE) {
 #pragma unroll
-    for (int i = 0; i < PER_THR; ++i) {
-      const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-      if (idx < PIECES) {
-        store_row_terms<IO, NTI>(kv[i], Ks, CT * KP, KP, t, j0);
+      for (int i = 0; i < PER_THR; ++i) {
+        const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+        if (idx < PIECES) {
+          store_row_terms<IO, NTI>(kv[i], Ks, CT * KP, KP, t, j0);
+          if constexpr (TWO) {
+            if (n2 > 0) store_row_terms<IO, NTI>(kv2[i], Ks2, CT * KP, KP, t, j0);
+          }
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv[i], e);
+          for (int e = 0; e < VEC; ++e) Vs[t * VP + j0 + e] = elem<IO>(vv[i], e);
+        }
+      }
+      const float a_cur = a_row, b_cur = bb;
+      // TWO: the second block's values, into the registers just staged from
+      if constexpr (TWO) {
+        if (n2 > 0) load_values(CT, n2);
+      }
+      lds_barrier();
+      transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
+      if (wave == 0) {
+        const float g = wave_inclusive_scan(lane < nc ? __logf(a_cur) : 0.f);
+        factorize_chunk<CT, D, NTI, NTF, ORD, false, true>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP, vec,
+                                                            vec_tmp);
+      } else if (TWO && wave == 1 && n2 > 0) {
+        // the second block, at the same time
+        const float g = wave_inclusive_scan(lane < n2 ? __logf(a2_row) : 0.f);
+        factorize_chunk<CT, D, NTI, NTF, ORD, false, true>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
+                                                            vec_tmp2);
+      } else {
+        // the other waves transpose the second block's keys meanwhile
+        if constexpr (TWO) {
+          if (n2 > 0) transpose_keys<CT, D, NTI>(Ks2, KP, KTs2, D * TP, TP, tid - 128, NTH - 128);
+        }
+        // match the barriers inside factorize_chunk
+        lds_barrier();
+        lds_barrier();
+      }
+      lds_barrier();
+      if constexpr (TWO) {
+        // the second block's values over its A (no longer read); read after the next
+        // block's opening barrier
+        if (n2 > 0) {
+#pragma unroll
+          for (int i = 0; i < PER_THR; ++i) {
+            const int idx = tid + NTH * i, t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
+            if (idx < PIECES) {
+              const uint32_t w[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(V2 + t * V2P + j0 + 2 * e) = w[e];
+            }
+          }
+        }
+      } else {
+        // the next block's rows (n <= 2 CT), requested after the factorization, whose
+        // registers they would otherwise add to, and in flight during the products
+        if (c0 + CT < n) load_rows(c0 + CT, n - c0 - CT);
       }
     }
-    const float a_cur = a_row, b_cur = bb;
-    lds_barrier();
-    transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
-    if (wave == 0) {
-      const float g = wave_inclusive_scan(lane < nc ? __logf(a_cur) : 0.f);
-      factorize_chunk<CT, D, NTI, NTF, ORD, false, true>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP, vec,
-                                                          vec_tmp);
-    } else {
-      // match the barriers inside factorize_chunk
-      lds_barrier();
-      lds_barrier();
-    }
-    lds_barrier();
-    // the next block's rows (n <= 2 CT), requested after the factorization, whose
-    // registers they would otherwise add to, and in flight during the products
-    if (c0 + CT < n) load_rows(c0 + CT, n - c0 - CT);
 
     // X = K S^T, R = b (V - e^g X), Dt = e^(g_n - g) T R, S^T <- e^(g_n) S^T + K^T Dt
     bf16x8 Sop[KSD][NTF];
@@ -152,14 +240,17 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
 #pragma unroll
       for (int s = 0; s < KSD; ++s) {
         bf16x8 a[NTI];
-        op_terms<NTI>(Ks, CT * KP, KP, 16 * mt + col, s, grp, a);
+        op_terms<NTI>(Kb, CT * KP, KP, 16 * mt + col, s, grp, a);
         mma_terms<NTI, NTF, ORD>(acc, a, Sop[s]);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * mt + 4 * grp + r;
         float val = 0.f;
-        if (t < nc) val = vec[2 * CT + t] * (Vs[t * VP + my_row] - vec[CT + t] * acc[r]);
+        if (t < nc) {
+          const float vt = PRE ? bf16_to_f32(V2[t * V2P + my_row]) : Vs[t * VP + my_row];
+          val = vb_[2 * CT + t] * (vt - vb_[CT + t] * acc[r]);
+        }
         R[mt][r] = val;
       }
     }
@@ -175,16 +266,16 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
 #pragma unroll
       for (int s = 0; s <= (mt >> 1); ++s) {
         bf16x8 a[NTF];
-        op_terms<NTF>(Ts, CT * TP, TP, 16 * mt + col, s, grp, a);
+        op_terms<NTF>(Tb, CT * TP, TP, 16 * mt + col, s, grp, a);
         mma_terms<NTF, NTF, ORD>(acc, a, Rop[s]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Dt[mt][r] = vec[3 * CT + 16 * mt + 4 * grp + r] * acc[r];
+      for (int r = 0; r < 4; ++r) Dt[mt][r] = vb_[3 * CT + 16 * mt + 4 * grp + r] * acc[r];
     }
     bf16x8 Dtop[KST][NTF];
 #pragma unroll
     for (int s = 0; s < KST; ++s) reg_operand<NTF>(Dt[2 * s], Dt[2 * s + 1], Dtop[s]);
-    const float egn = vec[CT + nc - 1];
+    const float egn = vb_[CT + nc - 1];
 #pragma unroll
     for (int jt = 0; jt < DT; ++jt) {
       f32x4 acc;
@@ -193,15 +284,15 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
         bf16x8 a[NTI];
-        op_terms<NTI>(KTs, D * TP, TP, 16 * jt + col, s, grp, a);
+        op_terms<NTI>(PRE ? KTs2 : KTs, D * TP, TP, 16 * jt + col, s, grp, a);
         mma_terms<NTI, NTF, ORD>(acc, a, Dtop[s]);
       }
       S[jt] = acc;
     }
   };
   static_assert(kMaxBufRows <= 2 * CT, "a log holds at most two blocks");
-  apply_block(0, n < CT ? n : CT);
-  if (n > CT) apply_block(CT, n - CT);
+  apply_block(0, n < CT ? n : CT, std::false_type{});
+  if (n > CT) apply_block(CT, n - CT, std::integral_constant<bool, TWO>{});
 #pragma unroll
   for (int jt = 0; jt < DT; ++jt) store16_through(state + (size_t)my_row * D + 16 * jt + 4 * grp, S[jt]);
 }
@@ -448,7 +539,16 @@ template <typename IO, int D>
 static hipError_t launch_flush_t(const FlushArgs<IO>& a, int n_req, hipStream_t st) {
   if (n_req == 0) return hipSuccess;
   dim3 grid(a.Hv, n_req);
-  hipLaunchKernelGGL((flush_kernel<IO, D>), grid, dim3(64 * (D / 16)), 0, st, a.slot_ids, a.n_accepted, a);
+  // a log of more than one 32-row block takes the form that factorizes both at once
+  // (head dim >= 64: it needs three waves; bf16: two such workgroups still share a CU)
+  if constexpr (D >= 64 && sizeof(IO) == 2) {
+    if (a.buf_rows > 32) {
+      hipLaunchKernelGGL((flush_kernel<IO, D, true>), grid, dim3(64 * (D / 16)), 0, st, a.slot_ids, a.n_accepted,
+                         a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((flush_kernel<IO, D, false>), grid, dim3(64 * (D / 16)), 0, st, a.slot_ids, a.n_accepted, a);
   return hipGetLastError();
 }
 

@@ -99,12 +99,13 @@ def _log(domain, n_slots, rows, Hqk, Hv, seed):
     return torch.stack(kk), torch.stack(vv), torch.stack(aa), torch.stack(bb)
 
 
-@pytest.mark.parametrize("domain", DOMAINS)
-def test_flush_edge_domains(g, domain):
-    Hqk, Hv, rows = 2, 4, 32
+@pytest.mark.parametrize("domain,rows", [(d, 32) for d in DOMAINS] + [("all", 64)])
+def test_flush_edge_domains(g, domain, rows):
+    """64-slot logs take two 32-row blocks (both factorized at once at head dim >= 64)."""
+    Hqk, Hv = 2, 4
     layer = g.Layer(Hqk, Hv, D, BF)
-    slots, acc = [3, 0, 2, 1], [32, 17, 16, 5]
-    say(f"flush domain={domain}")
+    slots, acc = [3, 0, 2, 1], ([32, 17, 16, 5] if rows == 32 else [64, 33, 40, 5])
+    say(f"flush domain={domain} rows={rows}")
     pool0 = gi.states(4, Hv, D, seed=211)
     bk, bv, ba, bb = _log(domain, 4, rows, Hqk, Hv, seed=212)
     pool = pool0.cuda()

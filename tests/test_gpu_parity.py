@@ -211,7 +211,9 @@ def test_decode_rejects_bad_slot_on_device(g):
 # ------------------------------------------------------------------------- flush
 
 @pytest.mark.parametrize("D,dtype,rows", [(128, torch.bfloat16, 32), (16, torch.float32, 32),
-                                          (64, torch.bfloat16, 64), (32, torch.bfloat16, 16)])
+                                          (64, torch.bfloat16, 64), (32, torch.bfloat16, 16),
+                                          (128, torch.bfloat16, 64), (32, torch.bfloat16, 64),
+                                          (64, torch.float32, 64)])
 def test_flush_matches_sequential_oracle(g, D, dtype, rows):
     Hqk, Hv, n_slots = 2, 4, 6
     layer = g.Layer(Hqk, Hv, D, dtype)
