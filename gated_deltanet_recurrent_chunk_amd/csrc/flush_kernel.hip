@@ -40,7 +40,7 @@ using namespace chunk;
 // are written, as bf16, over its A once the factorizations are done, so its products
 // follow the first block's after a single barrier.
 template <typename IO, int D, bool TWO>
-__global__ __launch_bounds__(64 * (D / 16), (sizeof(IO) == 2 && D >= 64) ? 4 : 1)
+__global__ __launch_bounds__(64 * (D / 16), (sizeof(IO) == 2 && D >= 64) ? (TWO ? 2 : 4) : 1)
 void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<IO> p) {
   constexpr int CT = 32;
   constexpr int NTI = Prec<IO>::NTI, NTF = Prec<IO>::NTF, ORD = Prec<IO>::ORD;
@@ -510,10 +510,14 @@ template <typename IO, int D>
 static hipError_t launch_replay_t(const ReplayArgs<IO>& a, int n_req, int ct, hipStream_t st) {
   if (n_req == 0) return hipSuccess;
   dim3 grid(a.Hv, n_req);
-  if (ct <= 32)
+  if (ct <= 32) {
     hipLaunchKernelGGL((replay_kernel<IO, D, 32>), grid, dim3(64 * (D / 16)), 0, st, a);
-  else
-    hipLaunchKernelGGL((replay_kernel<IO, D, 64>), grid, dim3(64 * (D / 16)), 0, st, a);
+  } else {
+    // a 64-row block of fp32 rows at head dim 128 does not fit a CU's LDS (refused by
+    // gdn_replay_forward before the launch)
+    if constexpr (sizeof(IO) == 4 && D >= 128) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((replay_kernel<IO, D, 64>), grid, dim3(64 * (D / 16)), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -531,6 +535,7 @@ hipError_t launch_replay(const ReplayArgs<float>& a, int D, int n_req, int ct, h
     case 16: return launch_replay_t<float, 16>(a, n_req, ct, st);
     case 32: return launch_replay_t<float, 32>(a, n_req, ct, st);
     case 64: return launch_replay_t<float, 64>(a, n_req, ct, st);
+    case 128: return launch_replay_t<float, 128>(a, n_req, ct, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -566,6 +571,7 @@ hipError_t launch_flush(const FlushArgs<float>& a, int D, int n_req, hipStream_t
     case 16: return launch_flush_t<float, 16>(a, n_req, st);
     case 32: return launch_flush_t<float, 32>(a, n_req, st);
     case 64: return launch_flush_t<float, 64>(a, n_req, st);
+    case 128: return launch_flush_t<float, 128>(a, n_req, st);
     default: return hipErrorInvalidValue;
   }
 }

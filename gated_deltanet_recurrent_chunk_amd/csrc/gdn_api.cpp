@@ -56,9 +56,6 @@ gdn_status check_qkv(const LayerInfo& L, const void* q, const void* k, const voi
   if (!aligned(k, 16) || (need_q && !aligned(q, 16)) || (need_v && !aligned(v, 16))) return GDN_ERR_BAD_SHAPE;
   if (qk_stride < (int64_t)L.Hqk * L.D || qk_stride % vec != 0) return GDN_ERR_BAD_SHAPE;
   if (need_v && (v_stride < (int64_t)L.Hv * L.D || v_stride % vec != 0)) return GDN_ERR_BAD_SHAPE;
-  // fp32 inputs enter the matrix products as three bf16 terms; the registers of the
-  // chunk kernels hold them for head_dim <= 64
-  if (L.io == GDN_F32 && L.D > 64) return GDN_ERR_BAD_SHAPE;
   // the scan addresses one chunk of rows with 32-bit byte offsets
   const int64_t lim = (int64_t)INT32_MAX / kChunk;
   if (qk_stride * (int64_t)L.io_bytes > lim || (need_v && v_stride * (int64_t)L.io_bytes > lim) ||
@@ -671,7 +668,6 @@ gdn_status gdn_replay_flush(const gdn_layer* layer, hipStream_t stream, int32_t 
   if (s != GDN_OK) return s;
   if (n_req < 0 || n_slots < 0) return GDN_ERR_BAD_SHAPE;
   if (buf_rows < 1 || buf_rows > kMaxBufRows) return GDN_ERR_CAPACITY;
-  if (L.io == GDN_F32 && L.D > 64) return GDN_ERR_BAD_SHAPE;
   if (n_req == 0) return GDN_OK;
   if (!state_pool || !slot_ids || !buf_k || !buf_v || !buf_a || !buf_b || !n_accepted) return GDN_ERR_NULL_ARG;
   if (!aligned(state_pool, 16) || !aligned(buf_k, 16) || !aligned(buf_v, 16)) return GDN_ERR_BAD_SHAPE;
@@ -785,7 +781,9 @@ gdn_status gdn_replay_forward(const gdn_layer* layer, hipStream_t stream, int32_
   if (s != GDN_OK) return s;
   if (n_req < 0 || n_slots < 0 || max_new < 0) return GDN_ERR_BAD_SHAPE;
   if (buf_rows < 1 || buf_rows > kMaxBufRows) return GDN_ERR_CAPACITY;
-  if (L.io == GDN_F32 && L.D > 64) return GDN_ERR_BAD_SHAPE;
+  // a 64-row log block of fp32 rows at head_dim 128 (keys, values, their transposes and
+  // the new queries) needs more LDS than one CU holds; such logs take at most 32 rows
+  if (L.io == GDN_F32 && L.D >= 128 && buf_rows > 32) return GDN_ERR_CAPACITY;
   if (n_req == 0 || max_new == 0) return GDN_OK;
   if (!state_pool || !slot_ids || !buf_k || !buf_v || !buf_a || !buf_b || !n_logged || !n_new || !q_new || !o)
     return GDN_ERR_NULL_ARG;

@@ -1348,6 +1348,7 @@ hipError_t launch_factorize(const FactorizeArgs<float>& a, int D, hipStream_t st
     case 16: return launch_factorize_t<float, 16>(a, st);
     case 32: return launch_factorize_t<float, 32>(a, st);
     case 64: return launch_factorize_t<float, 64>(a, st);
+    case 128: return launch_factorize_t<float, 128>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1365,6 +1366,7 @@ hipError_t launch_scan(const ScanArgs<float>& a, int D, hipStream_t st) {
     case 16: return launch_scan_t<float, 16>(a, st);
     case 32: return launch_scan_t<float, 32>(a, st);
     case 64: return launch_scan_t<float, 64>(a, st);
+    case 128: return launch_scan_t<float, 128>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -457,7 +457,8 @@ gdn_status gdn_core_prefill(const gdn_layer* layer, hipStream_t stream, const gd
  * over log rows 0 .. m + n - 1, and o[r][i] = scale * S_{m+i} q_new[r][i] for i < n,
  * with S_t the state after log row t.  Nothing is written to the state or the log: a
  * later gdn_replay_flush accepts rows, a smaller count rolls them back.
- *   state_pool, buf_k, buf_v, buf_a, buf_b, buf_rows (<= 64) as for gdn_replay_flush.
+ *   state_pool, buf_k, buf_v, buf_a, buf_b, buf_rows (<= 64) as for gdn_replay_flush;
+ *   with fp32 inputs at d = 128, buf_rows <= 32 (GDN_ERR_CAPACITY otherwise).
  *   q_new [n_req][max_new][n_qk_heads][d] io_dtype; o [n_req][max_new][n_v_heads][d]
  *   fp32, rows at or past n_new[r] not written.  n_logged, n_new [n_req] int32
  *   (device).  Slot -1 or n = 0 writes nothing.  m < 0, n < 0, m + n > buf_rows,

@@ -127,8 +127,10 @@ def test_prefill_validation_errors():
     # workspace too small
     ws = torch.zeros(256, dtype=torch.uint8)
     assert _err(_prefill, ok_layer, [0, 100], [0], zero, workspace=ws) == "GDN_ERR_WORKSPACE"
-    # fp32 inputs are staged as three bf16 terms: head_dim <= 64
-    assert _err(_prefill, g.Layer(2, 2, 128, torch.float32), [0, 100], [0], zero) == "GDN_ERR_BAD_SHAPE"
+    # fp32 rows at head_dim 128 pass the shape checks like bf16 rows: without a GPU both
+    # stop only at the workspace, which the binding cannot place on the device
+    for dt in (torch.float32, torch.bfloat16):
+        assert _err(_prefill, g.Layer(2, 2, 128, dt), [0, 100], [0], zero) == "GDN_ERR_WORKSPACE"
 
 
 def test_binding_rejects_undersized_operands():
@@ -145,7 +147,9 @@ def test_flush_and_decode_validation_errors():
     ab = torch.zeros(2, 65, 2)
     ids = torch.zeros(2, dtype=torch.int32)
     assert _err(g.replay_flush, layer, pool, ids, buf, buf, ab, ab, ids, stream=0) == "GDN_ERR_CAPACITY"
-    assert _err(g.replay_flush, g.Layer(2, 2, 128, torch.float32), torch.zeros(2, 2, 128, 128), ids,
+    # a state pool off the 16-byte grid
+    pool32 = torch.zeros(2 * 2 * 128 * 128 + 1)[1:].view(2, 2, 128, 128)
+    assert _err(g.replay_flush, g.Layer(2, 2, 128, torch.float32), pool32, ids,
                 torch.zeros(2, 32, 2, 128), torch.zeros(2, 32, 2, 128), torch.zeros(2, 32, 2),
                 torch.zeros(2, 32, 2), ids, stream=0) == "GDN_ERR_BAD_SHAPE"
     q = torch.zeros(2, 2, 32, dtype=torch.bfloat16)
@@ -163,11 +167,11 @@ def test_replay_gates_norm_and_mixed_validation_errors():
     o = torch.zeros(2, 4, 2, 32)
     # a log longer than 64 rows
     assert _err(g.replay_forward, layer, pool, ids, buf, buf, ab, ab, ids, ids, qn, o, stream=0) == "GDN_ERR_CAPACITY"
-    # fp32 inputs with d = 128
+    # fp32 inputs with d = 128: logs of more than 32 rows do not fit the verify kernel's LDS
     l32 = g.Layer(2, 2, 128, torch.float32)
-    assert _err(g.replay_forward, l32, torch.zeros(2, 2, 128, 128), ids, torch.zeros(2, 32, 2, 128),
-                torch.zeros(2, 32, 2, 128), torch.zeros(2, 32, 2), torch.zeros(2, 32, 2), ids, ids,
-                torch.zeros(2, 4, 2, 128), torch.zeros(2, 4, 2, 128), stream=0) == "GDN_ERR_BAD_SHAPE"
+    assert _err(g.replay_forward, l32, torch.zeros(2, 2, 128, 128), ids, torch.zeros(2, 33, 2, 128),
+                torch.zeros(2, 33, 2, 128), torch.zeros(2, 33, 2), torch.zeros(2, 33, 2), ids, ids,
+                torch.zeros(2, 4, 2, 128), torch.zeros(2, 4, 2, 128), stream=0) == "GDN_ERR_CAPACITY"
     # an unknown flag in the activation field
     bad = g.Layer(2, 2, 32, conv_act=0x200)
     ba = torch.zeros(5, 4, dtype=torch.bfloat16)

@@ -35,6 +35,7 @@ PREFILL_CASES = [
     (100, 1, 2, 32, torch.float32, 48),
     (257, 1, 1, 128, torch.bfloat16, 64),
     (90, 2, 2, 16, torch.bfloat16, 32),
+    (200, 2, 4, 128, torch.float32, 96),    # fp32 rows at the full head dim
 ]
 
 
@@ -161,7 +162,8 @@ def test_identity_gate_is_bitwise_identity(g):
 
 # ------------------------------------------------------------------------- decode
 
-@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (16, torch.float32), (64, torch.bfloat16)])
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (16, torch.float32), (64, torch.bfloat16),
+                                     (128, torch.float32)])
 def test_decode_matches_oracle_and_skips_padding(g, D, dtype):
     Hqk, Hv, n_slots = 2, 4, 5
     layer = g.Layer(Hqk, Hv, D, dtype, scale=0.7)
@@ -213,7 +215,8 @@ def test_decode_rejects_bad_slot_on_device(g):
 @pytest.mark.parametrize("D,dtype,rows", [(128, torch.bfloat16, 32), (16, torch.float32, 32),
                                           (64, torch.bfloat16, 64), (32, torch.bfloat16, 16),
                                           (128, torch.bfloat16, 64), (32, torch.bfloat16, 64),
-                                          (64, torch.float32, 64)])
+                                          (64, torch.float32, 64), (128, torch.float32, 32),
+                                          (128, torch.float32, 64)])
 def test_flush_matches_sequential_oracle(g, D, dtype, rows):
     Hqk, Hv, n_slots = 2, 4, 6
     layer = g.Layer(Hqk, Hv, D, dtype)
@@ -275,7 +278,8 @@ def test_flush_rejects_bad_count_on_device(g):
 # ------------------------------------------------------------------------- packed-core steps
 
 @pytest.mark.parametrize("Hqk,Hv,D,dtype", [(2, 4, 128, torch.bfloat16), (1, 2, 16, torch.float32),
-                                            (3, 3, 32, torch.bfloat16), (2, 2, 64, torch.float32)])
+                                            (3, 3, 32, torch.bfloat16), (2, 2, 64, torch.float32),
+                                            (1, 2, 128, torch.float32)])
 def test_conv_with_qk_l2norm_matches_oracle(g, Hqk, Hv, D, dtype):
     """The conv with the post-conv step fused: q and k heads of every output row at unit
     norm, value channels and tails as without it."""
@@ -350,7 +354,8 @@ def test_gated_norm_matches_oracle(g, Hv, D, dtype):
 
 # ------------------------------------------------------------------------- mixed batches
 
-@pytest.mark.parametrize("Hqk,Hv,D,dtype", [(2, 4, 128, torch.bfloat16), (1, 2, 32, torch.float32)])
+@pytest.mark.parametrize("Hqk,Hv,D,dtype", [(2, 4, 128, torch.bfloat16), (1, 2, 32, torch.float32),
+                                            (1, 2, 128, torch.float32)])
 def test_mixed_batch_decode_rows_and_prefill(g, Hqk, Hv, D, dtype):
     """One packed batch: 5 decode tokens (rows 0..4, in permuted order, one padding slot)
     and two prefill sequences behind them.  The decode tokens go to decode_mixed, the
@@ -433,6 +438,7 @@ REPLAY_CASES = [
     (16, torch.float32, 32, [(1, 5, 11), (0, 0, 1), (3, 31, 1), (2, 12, 17)]),
     (64, torch.bfloat16, 64, [(0, 40, 17), (2, 0, 3), (1, 63, 1), (3, 47, 17)]),
     (32, torch.float32, 64, [(3, 30, 17), (0, 1, 16), (2, 0, 0)]),
+    (128, torch.float32, 32, [(1, 20, 12), (0, 0, 17), (3, 31, 1), (2, 9, 0), (4, 15, 16)]),
 ]
 
 
