@@ -842,15 +842,21 @@ __global__ __launch_bounds__(64 * ScanSplit<D>::NSP) void scan_kernel(ScanArgs<I
 // operands that all slabs of a head share -- the factor record (T, P, K^T, the row
 // vectors, exp(g_n)) -- and the value columns of the pair are copied into LDS once
 // per workgroup by LDS DMA (buffer loads that write LDS directly), a chunk ahead, into
-// two alternating buffers; each wave reads its operands from there one phase before
-// it needs them.  Key and query rows go straight to registers, as in scan_kernel.
-// Compared with one workgroup per slab, a compute unit moves about half the bytes per
-// chunk and issues a quarter of the vector memory instructions.
+// two alternating buffers, and so are the chunk's key and query rows; each wave reads
+// its operands from there one phase before it needs them.  Compared with one
+// workgroup per slab, a compute unit moves about half the bytes per chunk and issues a
+// quarter of the vector memory instructions.
 //
 // Per chunk c, with buffers Bc (chunk c) and Bn (chunk c + 1):
 //   wait for this wave's copies into Bc; barrier (all copies landed, every wave is
-//   done with chunk c - 1, so Bn and the exchange slots are free); start the copies
-//   of chunk c + 1 into Bn; then phases A-D of scan_kernel with LDS operands.
+//   done with chunk c - 1, so every buffer of chunk c + 1 and the exchange slots are
+//   free); then phases A-D of scan_kernel with LDS operands, with the copies of chunk
+//   c + 1 issued in three parts: the key rows at the top, the query rows after phase
+//   A, the record and value rows after the exchange.  The copies share the compute
+//   unit's path from L2 (about 60 bytes per cycle) and the LDS with the waves' own
+//   reads; issued in one part (at the top, or all after the exchange) they cost
+//   15-20% more time, and issued late in the chunk they held every wave at the next
+//   barrier.
 template <typename IO, int D>
 struct ScanStaged {
   static constexpr bool OK = sizeof(IO) == 2 && D >= 64;
@@ -881,8 +887,8 @@ __host__ __device__ constexpr int omt(int w, int i) { return NSP == 1 ? i : i ==
 
 template <typename IO, int D, int Q>
 __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const int u, const int sg, lds_u8* stage0,
-                                                 lds_u8* stage1, lds_u8* kbuf0, lds_u8* kbuf1, lds_u8* qbuf,
-                                                 f32x4* xch) {
+                                                 lds_u8* stage1, lds_u8* kbuf0, lds_u8* kbuf1, lds_u8* qbuf0,
+                                                 lds_u8* qbuf1, f32x4* xch) {
   using Cfg = PrefillCfg<IO, D>;
   using Shp = ScanStaged<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
@@ -900,15 +906,13 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   constexpr int GPW = (G + NW - 1) / NW;  // copies per wave at most
   constexpr int BUF = GPW * NW * 1024;
   constexpr int XCH = NSP == 2 ? SP * NSP * 6 * 64 : 1;  // f32x4 exchange slots
-  // key rows of a chunk (two buffers, alternating: a chunk's keys serve its state update
-  // at the end of the chunk, after the next chunk's keys are requested) and query rows
-  // (one buffer, refilled once every wave has read them): rows of RB bytes whose 16-byte
-  // pieces are permuted by an XOR with the row index, so that the 16 rows of one operand
-  // read land in distinct banks
+  // key and query rows of a chunk (two buffers each, alternating like the record's):
+  // rows of RB bytes whose 16-byte pieces are permuted by an XOR with the row index, so
+  // that the 16 rows of one operand read land in distinct banks
   constexpr int RB = D * ESZ, PPR = RB / 16, RPG = 1024 / RB, KQG = 64 / RPG, KQPW = 2 * KQG / NW;
   static_assert(KSH * NSP == KSD && DTH * NSP == DT && (VNP == 4 || VNP == 8) && VG * 1024 == 64 * VRB, "shape");
   static_assert(RPG * RB == 1024 && KQPW * NW == 2 * KQG, "key/query staging");
-  static_assert(2 * BUF + 16 * XCH + 3 * 64 * RB <= 160 * 1024, "LDS budget");
+  static_assert(2 * BUF + 16 * XCH + 4 * 64 * RB <= 160 * 1024, "LDS budget");
   const int seq = u / p.Hv, h = u - seq * p.Hv;
   const int hk = h / p.group;
   constexpr int q = Q, jj = Q / NSP, w = Q % NSP;  // slab within the pair, key half
@@ -990,29 +994,31 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
 
   // copies of the chunk's key rows (into Kd) and query rows: KQPW granules per wave,
   // same on every path
-  auto stage_kq = [&](const ChunkPos& cd, lds_u8* Kd) {
+  // which: 0 the key rows, 1 the query rows, 2 both
+  auto stage_kq = [&](const ChunkPos& cd, lds_u8* Kd, lds_u8* Qd, const int which) {
     const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
     const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)cd.len * qsb);
 #pragma unroll
     for (int gi = 0; gi < KQPW; ++gi) {
       const int g = q + gi * NW;  // wave-uniform: granules 0 .. KQG-1 keys, then queries
+      if (which != 2 && which != (g < KQG ? 0 : 1)) continue;
       const uint32_t r = RPG * (uint32_t)(g % KQG) + (uint32_t)lane / PPR;
       const uint32_t lp = ((uint32_t)lane % PPR) ^ (r % PPR);
       if (g < KQG)
         dma16(rk, Kd + 1024 * g, r * qsb + 16u * lp);
       else
-        dma16(rq, qbuf + 1024 * (g - KQG), r * qsb + 16u * lp);
+        dma16(rq, Qd + 1024 * (g - KQG), r * qsb + 16u * lp);
     }
   };
   // this wave's A operands of X and Y: row 16 mt + col, key columns 32 (s0 + s) + 8 grp ..
   RowOp<IO> Kop[4][KSH], Qop[4][KSH];
-  auto read_kq = [&](const lds_u8* Kb, int s) {  // k-step s0 + s
+  auto read_kq = [&](const lds_u8* Kb, const lds_u8* Qb, int s) {  // k-step s0 + s
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int r = 16 * mt + col;
       const int off = r * RB + 16 * ((grp + 4 * (s0 + s)) ^ (r % PPR));
       Kop[mt][s].v = lds_load<bf16x8>(Kb + off);
-      Qop[mt][s].v = lds_load<bf16x8>(qbuf + off);
+      Qop[mt][s].v = lds_load<bf16x8>(Qb + off);
     }
   };
   // A operands of K^T for the state update (state tile jt0 + j, k-step s over the chunk
@@ -1049,7 +1055,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   ChunkPos nxt = chunk_at(se, npos, blk);
   uint32_t cur_pid = page_raw(cur);
   stage_chunk(cur, cb, stage0);
-  stage_kq(cur, kbuf0);
+  stage_kq(cur, kbuf0, qbuf0, 2);
 
   // Stores are issued one chunk late, right after the next chunk's barrier: the
   // barrier's wait for this wave's copies (vmcnt) also counts stores, so a store issued
@@ -1074,9 +1080,10 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
                   (size_t)my_row * D);
   };
 
-  auto step = [&](const int c, const lds_u8* Bc, lds_u8* Bn, const lds_u8* Kc, lds_u8* Kn) {
+  auto step = [&](const int c, const lds_u8* Bc, lds_u8* Bn, const lds_u8* Kc, lds_u8* Kn, const lds_u8* Qc,
+                  lds_u8* Qn) {
     const bool more = c + 1 < ce;
-    // Every wave's copies of this chunk (into Bc, Kc and the query buffer) have landed once each wave has
+    // Every wave's copies of this chunk (into Bc, Kc and Qc) have landed once each wave has
     // waited for all of its own vector memory operations and passed the barrier.  The
     // wait is explicit: the compiler's own count of outstanding LDS DMA follows the
     // data a wave reads itself, not the copies its partners read.  The copies were
@@ -1084,12 +1091,13 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     full_barrier();
     // the previous chunk's outputs and checkpoint
     flush_pending();
-    // (the last chunk stages itself again: every path issues the same copies, so the
-    // compiler's counts of outstanding loads stay exact)
-    stage_chunk(nxt, more ? c + 1 : c, Bn);
+    // copies of the next chunk's key rows (the last chunk stages itself again: every
+    // path issues the same copies, so the compiler's counts of outstanding loads stay
+    // exact)
+    stage_kq(nxt, Kn, Qn, 0);
     const uint32_t nxt_pid = page_raw(nxt);
 
-    read_kq(Kc, 0);
+    read_kq(Kc, Qc, 0);
     issue_point();
 
     // ---- A: X = K S^T and Y = Q S^T (this wave's k-steps), eight accumulator chains;
@@ -1099,7 +1107,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
     for (int mt = 0; mt < 4; ++mt) X[mt] = Y[mt] = zero4();
 #pragma unroll
     for (int s = 0; s < KSH; ++s) {
-      if (s + 1 < KSH) read_kq(Kc, s + 1);
+      if (s + 1 < KSH) read_kq(Kc, Qc, s + 1);
       issue_point();
       bf16x8 sop[NTF];
       reg_operand<NTF>(S[2 * s], (2 * s + 1 < DTH) ? S[2 * s + 1] : zero4(), sop);
@@ -1113,6 +1121,8 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       }
     }
     issue_point();
+    // the next chunk's query rows
+    stage_kq(nxt, Kn, Qn, 1);
     // with two waves per slab, add the partner's partial sums (X for all rows, Y for
     // this wave's output rows) through LDS
     f32x4 Ym[MR];
@@ -1144,9 +1154,8 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
       // them before the barrier held every wave there for all of them)
       lds_barrier();
       read_b();
-      // every wave has read this chunk's key and query rows: copy the next chunk's
-      // (the last chunk copies its own again, so that every path issues the same copies)
-      stage_kq(more ? nxt : cur, Kn);
+      // the next chunk's record and value rows
+      stage_chunk(nxt, more ? c + 1 : c, Bn);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 xo = other[mt * 64];
@@ -1163,10 +1172,7 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
 #pragma unroll
       for (int i = 0; i < MR; ++i) Ym[i] = Y[omt<NSP>(w, i)];
       read_b();
-      lds_barrier();
-      // every wave has read this chunk's key and query rows: copy the next chunk's (the
-      // last chunk copies its own again, so that every path issues the same copies)
-      stage_kq(more ? nxt : cur, Kn);
+      stage_chunk(nxt, more ? c + 1 : c, Bn);
     }
 
     // ---- B: R' = V - exp(g) X, Dt = T'' R' over the nonzero k-steps
@@ -1255,8 +1261,8 @@ __device__ __forceinline__ void scan_staged_wave(const ScanArgs<IO>& p, const in
   // two steps per trip, so that each step's buffers are fixed LDS objects
 #pragma unroll 1
   for (int c = cb; c < ce; c += 2) {
-    step(c, stage0, stage1, kbuf0, kbuf1);
-    if (c + 1 < ce) step(c + 1, stage1, stage0, kbuf1, kbuf0);
+    step(c, stage0, stage1, kbuf0, kbuf1, qbuf0, qbuf1);
+    if (c + 1 < ce) step(c + 1, stage1, stage0, kbuf1, kbuf0, qbuf1, qbuf0);
   }
   flush_pending();
   store_state(sq_dst + head_off + (size_t)my_row * D);
@@ -1280,12 +1286,12 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   constexpr int NG = ScanStaged<IO, D>::NG;
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[L::BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[L::BUF];
-  // two key buffers and the query buffer as separate objects: the compiler tracks
-  // outstanding LDS DMA per object, and a chunk's keys are read after the next chunk's
-  // keys and queries are requested
+  // the key and query buffers as separate objects: the compiler tracks outstanding LDS
+  // DMA per object, and a chunk's rows are read after the next chunk's are requested
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::KR];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::KR];
-  __shared__ __attribute__((aligned(1024))) uint8_t qbuf[L::KR];
+  __shared__ __attribute__((aligned(1024))) uint8_t qbuf0[L::KR];
+  __shared__ __attribute__((aligned(1024))) uint8_t qbuf1[L::KR];
   // [slab][wave][X tiles 0..3, partner's Y tiles][lane]
   __shared__ __attribute__((aligned(16))) f32x4 xch[L::XCH];
 
@@ -1297,13 +1303,13 @@ __global__ __launch_bounds__(256) void scan_staged_kernel(ScanArgs<IO> p) {
   if (u >= kernarg_table()->n_seqs * p.Hv) return;
   switch (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))) {
     case 0: scan_staged_wave<IO, D, 0>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
-                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf0, (lds_u8*)qbuf1, xch); break;
     case 1: scan_staged_wave<IO, D, 1>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
-                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf0, (lds_u8*)qbuf1, xch); break;
     case 2: scan_staged_wave<IO, D, 2>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
-                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf0, (lds_u8*)qbuf1, xch); break;
     default: scan_staged_wave<IO, D, 3>(p, u, sg, (lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)kbuf0,
-                                                (lds_u8*)kbuf1, (lds_u8*)qbuf, xch); break;
+                                                (lds_u8*)kbuf1, (lds_u8*)qbuf0, (lds_u8*)qbuf1, xch); break;
   }
 }
 
