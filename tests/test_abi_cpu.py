@@ -127,10 +127,10 @@ def test_prefill_validation_errors():
     # workspace too small
     ws = torch.zeros(256, dtype=torch.uint8)
     assert _err(_prefill, ok_layer, [0, 100], [0], zero, workspace=ws) == "GDN_ERR_WORKSPACE"
-    # fp32 rows at head_dim 128 pass the shape checks like bf16 rows: without a GPU both
-    # stop only at the workspace, which the binding cannot place on the device
+    # fp32 rows at head_dim 128 pass the shape checks like bf16 rows: both stop only at the
+    # (too small) workspace, which is checked after every shape
     for dt in (torch.float32, torch.bfloat16):
-        assert _err(_prefill, g.Layer(2, 2, 128, dt), [0, 100], [0], zero) == "GDN_ERR_WORKSPACE"
+        assert _err(_prefill, g.Layer(2, 2, 128, dt), [0, 100], [0], zero, workspace=ws) == "GDN_ERR_WORKSPACE"
 
 
 def test_binding_rejects_undersized_operands():
