@@ -144,7 +144,11 @@ __device__ __forceinline__ void full_barrier() {
 // row j = column j of T) to Ttr in the same plane format.
 // SPLIT (32-row chunks, no FOLD): the substitution runs on both halves of the wave, see
 // below; it holds half the registers of the one-half form.
-template <int CT, int D, int NTI, int NTF, int ORD, bool FOLD = false, bool SPLIT = false>
+// Barriers: the first publishes the row vectors to the whole workgroup.  The second
+// orders this wave's A tiles before its own substitution reads them: with LOCAL_A it
+// is a wait for this wave's LDS traffic only, so the other waves match one barrier and
+// are not held while the A tiles are formed.
+template <int CT, int D, int NTI, int NTF, int ORD, bool FOLD = false, bool SPLIT = false, bool LOCAL_A = false>
 __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n,
                                                 float g, float bb, bf16_bits* Tout, int tps, int tld,
                                                 float* vec_out, float* vec_lds, bf16_bits* Ttr = nullptr) {
@@ -206,7 +210,10 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
       }
     }
   }
-  lds_barrier();
+  if constexpr (LOCAL_A)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  else
+    lds_barrier();
 
   if constexpr (SPLIT) {
     // Lane (h, j) = (lane >> 5, lane & 31) owns column j of T at the rows s = 2k + h and

@@ -352,9 +352,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
     zero_lds(Qs, sizeof(Qs), tid, NTH);
   }
 
-  // log rows 0 .. L-1 of this slot (keys, values) and the queries of the new rows, then
-  // the state, whose loads stay in flight while the rows are staged and factorized
-  // (loads complete in issue order)
+  // log rows 0 .. L-1 of this slot (keys, values) and the queries of the new rows; the
+  // state is requested only once the factorization no longer waits for this wave (see
+  // below)
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + NTH - 1) / NTH;
   const size_t row0 = (size_t)slot * p.buf_rows;
   // the rows' gates (wave 0) go first: the factorization waits for them
@@ -377,9 +377,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
     vv[i] = load16(vb + (size_t)t * p.Hv * D + j0, in && t < L);
   }
   f32x4 S[DT];
-#pragma unroll
-  for (int jt = 0; jt < DT; ++jt)
-    S[jt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp));
   lds_barrier();  // the zero fills (d < 32) precede the row stores
 #pragma unroll
   for (int i = 0; i < PER_THR; ++i) {
@@ -423,18 +420,31 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
     }
   }
   };
+  // The state (64 KiB per workgroup at d = 128) is requested by each wave once its part
+  // of the factorization is done: wave 0 after the factorization, the others after
+  // their P tiles.  Requested at the start instead, the second workgroup of a CU waited
+  // for its rows and its waves stalled issuing loads while the first workgroup's state
+  // streamed in (measured: 15.0 us, the second workgroups finishing ~4 us after the
+  // first; now 13.0 us).
+  auto load_state = [&]() {
+#pragma unroll
+    for (int jt = 0; jt < DT; ++jt)
+      S[jt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp));
+  };
   if (wave == 0) {
     const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec, vec_tmp);
+    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32, true>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec,
+                                                                  vec_tmp);
     if constexpr (NW == 1) {
       lds_barrier();
       p_tiles(0, 1);
     }
+    load_state();
   } else {
-    // match the barriers inside factorize_chunk; the first publishes the gate vectors
+    // match the barrier inside factorize_chunk that publishes the gate vectors
     lds_barrier();
     p_tiles(wave - 1, NW - 1);
-    lds_barrier();
+    load_state();
   }
   lds_barrier();
 
