@@ -135,32 +135,24 @@ __device__ __forceinline__ void full_barrier() {
 }
 
 // ----------------------------------------------------------------------------------
-// Chunk factorization shared by the prefill pre-pass and the replay flush.  One wave.
+// Chunk factorization of the replay kernels (flush and outputs).  One wave.
 //   Ks: NTI swizzled planes (row stride KP) of the chunk's key rows (rows >= n zero).
 //   g, bb: this lane's g_t and b_t for t = lane (t >= n: g_t = g_{n-1}, b_t = 0).
 // Writes T = (I + A)^-1 as NTF swizzled bf16 planes (row stride tld, plane stride
 // tps) and the four per-row vectors g, exp(g), b, exp(g_n - g) into vec_out.
-// FOLD: writes T'' = diag(exp(g_n - g)) T diag(b) to Tout instead, and T^T (unscaled,
-// row j = column j of T) to Ttr in the same plane format.
-// SPLIT (32-row chunks, no FOLD): the substitution runs on both halves of the wave, see
-// below; it holds half the registers of the one-half form.
+// BLOCKED (32-row chunks): T by 16-row blocks, see below.
 // Barriers: the first publishes the row vectors to the whole workgroup.  The second
 // orders this wave's A tiles before its own substitution reads them: with LOCAL_A it
 // is a wait for this wave's LDS traffic only, so the other waves match one barrier and
 // are not held while the A tiles are formed.
-template <int CT, int D, int NTI, int NTF, int ORD, bool FOLD = false, bool SPLIT = false, bool LOCAL_A = false>
+template <int CT, int D, int NTI, int NTF, int ORD, bool BLOCKED = false, bool LOCAL_A = false>
 __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n,
                                                 float g, float bb, bf16_bits* Tout, int tps, int tld,
-                                                float* vec_out, float* vec_lds, bf16_bits* Ttr = nullptr) {
+                                                float* vec_out, float* vec_lds) {
   constexpr int KP = row_stride(D);
   constexpr int KSD = (D + 31) / 32;
   constexpr int MT = CT / 16;
-  static_assert(!SPLIT || (CT == 32 && !FOLD), "the split substitution covers 32-row chunks");
-  // SPLIT layout of A: two planes by the parity of the column s, A[t][s] at
-  // (s & 1) * SPL + t * (CT / 2) + (s >> 1); plane 1 starts 4 words further so that the
-  // two halves' row reads fall in different banks
-  constexpr int HS = CT / 2, SPL = CT * HS + 4;
-  float* const A2 = &As[0][0];
+  static_assert(!BLOCKED || CT == 32, "the blocked inverse covers 32-row chunks");
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
 
@@ -181,8 +173,13 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   // A = strict lower part of diag(b) exp(g_t - g_s) K K^T
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    // SPLIT: the substitution never reads rows t >= n, so their tiles are not formed
-    if (SPLIT && 16 * mt >= n) break;
+    // BLOCKED: with n <= 16 the second row tile of A is zero; the diagonal tile is
+    // stored as zeros (the substitution reads it) and the other is not read
+    if (BLOCKED && 16 * mt >= n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) As[16 + 4 * grp + r][16 + col] = 0.f;
+      break;
+    }
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
       f32x4 acc = zero4();
@@ -202,11 +199,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
         // reads into a branch per element) and kept or dropped by the select
         float dec = __expf(vec_lds[t] - gs), bt = vec_lds[CT + t];
         asm volatile("" : "+v"(dec), "+v"(bt));
-        const float val = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
-        if constexpr (SPLIT)
-          A2[(sc & 1) * SPL + t * HS + (sc >> 1)] = val;
-        else
-          As[t][sc] = val;
+        As[t][sc] = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
       }
     }
   }
@@ -215,60 +208,102 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   else
     lds_barrier();
 
-  if constexpr (SPLIT) {
-    // Lane (h, j) = (lane >> 5, lane & 31) owns column j of T at the rows s = 2k + h and
-    // sums A[t][s] T[s][j] over those rows; one swap of the wave's halves adds the other
-    // parity's sum (own + other in both halves: the same value).  The own-parity row t + 1
-    // of A is requested before the sums of row t run.  Row t's count is the even
-    // parity's, ceil(t / 2); for the odd parity its last term is A[t][t] = 0 times a
-    // not yet computed (zero) T entry.  Rows t >= n of A are zero, so T's rows there are
-    // those of the identity: with n <= 16 only the first 16 rows are substituted (one
-    // uniform branch between two unrolled forms; a branch per row would hold more
-    // registers).
-    const int hf = lane >> 5, j = lane & 31;
-    const float* Ah = A2 + hf * SPL;
-    float Tc[HS];
+  if constexpr (BLOCKED) {
+    // With A = [A00 0; A10 A11] in 16-row blocks, T = [T00 0; -T11 A10 T00 T11],
+    // Tii = (I + Aii)^-1.
+    // Diagonal blocks, both at once: lane (grp, c) owns column c of block bi = grp & 1
+    // (groups 2 and 3 repeat 0 and 1), forward substitution over the block's 16 rows,
+    // T[r][c] = [r == c] - sum_{s<r} A[r][s] T[s][c], as four interleaved partial sums.
+    // The coefficients of row r are the same for the block's 16 lanes (LDS broadcast
+    // reads), requested one row ahead.
+    const int bi = grp & 1;
+    const float(*Ab)[CT + 4] = reinterpret_cast<const float(*)[CT + 4]>(&As[16 * bi][16 * bi]);
+    float X[16];
+    f32x4 arow[2][4];
 #pragma unroll
-    for (int k = 0; k < HS; ++k) Tc[k] = 0.f;
-    auto substitute = [&](auto nr_) {
-      constexpr int NR = decltype(nr_)::value;
-      f32x4 arow[2][HS / 4];
+    for (int r = 0; r < 16; ++r) {
+      if (r + 1 < 16) {
 #pragma unroll
-      for (int t = 0; t < NR; ++t) {
-        if (t + 1 < NR) {
-#pragma unroll
-          for (int i = 0; i < ((t + 2) / 2 + 3) / 4; ++i)
-            arow[(t + 1) & 1][i] = *reinterpret_cast<const f32x4*>(Ah + (t + 1) * HS + 4 * i);
-        }
-        asm volatile("" ::: "memory");
-        float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-        for (int k = 0; k < (t + 1) / 2; ++k) {
-          const float av = arow[t & 1][k >> 2][k & 3];
-          if ((k & 1) == 0) p0 = fmaf(av, Tc[k], p0);
-          else p1 = fmaf(av, Tc[k], p1);
-        }
-        const float own = p0 + p1;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own), false, false);
-        const float val = (t == j ? 1.f : 0.f) - (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
-        if ((t & 1) == hf) Tc[t >> 1] = val;
-        asm volatile("" : "+v"(Tc[t >> 1]) : : "memory");
+        for (int i = 0; i < (r + 4) / 4; ++i) arow[(r + 1) & 1][i] = *reinterpret_cast<const f32x4*>(&Ab[r + 1][4 * i]);
       }
+      asm volatile("" ::: "memory");
+      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
-      for (int t = NR; t < CT; ++t)
-        if ((t & 1) == hf) Tc[t >> 1] = t == j ? 1.f : 0.f;
-    };
-    if (n <= CT / 2)
-      substitute(std::integral_constant<int, CT / 2>{});
-    else
-      substitute(std::integral_constant<int, CT>{});
-    const int pc = swz(j);
+      for (int sv = 0; sv < r; ++sv) {
+        const float av = arow[r & 1][sv >> 2][sv & 3];
+        if ((sv & 3) == 0) p0 = fmaf(av, X[sv], p0);
+        if ((sv & 3) == 1) p1 = fmaf(av, X[sv], p1);
+        if ((sv & 3) == 2) p2 = fmaf(av, X[sv], p2);
+        if ((sv & 3) == 3) p3 = fmaf(av, X[sv], p3);
+      }
+      X[r] = (r == col ? 1.f : 0.f) - ((p0 + p1) + (p2 + p3));
+      // row r is finished before the requests for row r + 2 are issued
+      asm volatile("" : "+v"(X[r]) : : "memory");
+    }
+    if (grp < 2) {
+      const int pc = swz(16 * bi + col);
 #pragma unroll
-    for (int k = 0; k < HS; ++k) {
-      bf16_bits tt[NTF];
-      split_terms<NTF>(Tc[k], tt);
+      for (int r = 0; r < 16; ++r) {
+        bf16_bits tt[NTF];
+        split_terms<NTF>(X[r], tt);
 #pragma unroll
-      for (int i = 0; i < NTF; ++i) Tout[i * tps + (2 * k + hf) * tld + pc] = tt[i];
+        for (int q = 0; q < NTF; ++q) Tout[q * tps + (16 * bi + r) * tld + pc] = tt[q];
+      }
+    } else {
+      // groups 2 and 3: zeros into the upper right block and, with n <= 16, the lower
+      // left one (lane u: row u / 2, eight columns from 8 (u % 2), two runs of four)
+      const int u = lane - 32, zr = u >> 1, zc = 8 * (u & 1);
+      const uint2 z{0u, 0u};
+#pragma unroll
+      for (int q = 0; q < NTF; ++q) {
+        bf16_bits* p = Tout + q * tps;
+        *reinterpret_cast<uint2*>(p + zr * tld + swz(16 + zc)) = z;
+        *reinterpret_cast<uint2*>(p + zr * tld + swz(16 + zc + 4)) = z;
+        if (n <= 16) {
+          *reinterpret_cast<uint2*>(p + (16 + zr) * tld + swz(zc)) = z;
+          *reinterpret_cast<uint2*>(p + (16 + zr) * tld + swz(zc + 4)) = z;
+        }
+      }
+    }
+    if (n > 16) {
+      // T00 and T11 as written above, read back by other lanes of this wave
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // U = A10 T00 in C layout (lane (col, grp): U[4 grp + r][col]); the contraction
+      // runs over 16 elements, so elements 4..7 of both operands are zero
+      bf16x8 a10[NTF], t00[NTF];
+      reg_operand<NTF>(*reinterpret_cast<const f32x4*>(&As[16 + col][4 * grp]), zero4(), a10);
+#pragma unroll
+      for (int q = 0; q < NTF; ++q) {
+        bf16_bits v8[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v8[r] = Tout[q * tps + (4 * grp + r) * tld + swz(col)];
+#pragma unroll
+        for (int r = 4; r < 8; ++r) v8[r] = 0;
+        t00[q] = pack8(v8);
+      }
+      f32x4 u = zero4();
+      mma_terms<NTF, NTF, ORD>(u, a10, t00);
+      // T10 = T11 (-U): the C layout of U is the B operand; A = rows of T11
+      bf16x8 t11[NTF], mu[NTF];
+      typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+#pragma unroll
+      for (int q = 0; q < NTF; ++q) {
+        const uint2 w = *reinterpret_cast<const uint2*>(Tout + q * tps + (16 + col) * tld + swz(16 + 4 * grp));
+        t11[q] = __builtin_bit_cast(bf16x8, u32x4_t{w.x, w.y, 0u, 0u});
+      }
+      f32x4 nu;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nu[r] = -u[r];
+      reg_operand<NTF>(nu, zero4(), mu);
+      f32x4 t10 = zero4();
+      mma_terms<NTF, NTF, ORD>(t10, t11, mu);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bf16_bits tt[NTF];
+        split_terms<NTF>(t10[r], tt);
+#pragma unroll
+        for (int q = 0; q < NTF; ++q) Tout[q * tps + (16 + 4 * grp + r) * tld + swz(col)] = tt[q];
+      }
     }
     return;
   }
@@ -304,24 +339,9 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
 #pragma unroll
     for (int t = 0; t < CT; ++t) {
       bf16_bits tt[NTF];
-      float x = Tc[t];
-      if constexpr (FOLD) x = (x * vec_out[3 * CT + t]) * bb;
-      split_terms<NTF>(x, tt);
+      split_terms<NTF>(Tc[t], tt);
 #pragma unroll
       for (int i = 0; i < NTF; ++i) Tout[i * tps + t * tld + pc] = tt[i];
-    }
-    if constexpr (FOLD) {
-      // row `lane` of T^T: runs of four columns are contiguous in the swizzled order
-#pragma unroll
-      for (int t0 = 0; t0 < CT; t0 += 4) {
-        bf16_bits tt[4][NTF];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_terms<NTF>(Tc[t0 + e], tt[e]);
-#pragma unroll
-        for (int i = 0; i < NTF; ++i)
-          *reinterpret_cast<uint2*>(Ttr + i * tps + lane * tld + swz(t0)) =
-              uint2{(uint32_t)tt[0][i] | ((uint32_t)tt[1][i] << 16), (uint32_t)tt[2][i] | ((uint32_t)tt[3][i] << 16)};
-      }
     }
   }
 }

@@ -26,8 +26,10 @@ using namespace chunk;
 // loads stay in flight through the staging of the first block and its factorization,
 // and the next block's rows are requested while the current one is applied.
 //
-// One 32-row block covers the common case (a few accepted rows); its substitution runs
-// on both halves of the wave and, with at most 16 rows, skips the empty half.  The
+// One 32-row block covers the common case (a few accepted rows); its inverse is formed
+// by 16-row blocks (two diagonal substitutions at once, then one off-diagonal block by
+// two products), and with at most 16 rows only the first diagonal block is not the
+// identity.  The
 // kernel fits in 128 VGPRs, so two workgroups share a CU and the whole grid is resident
 // at once.  (A 16-row block measured slower than this 32-row one, and a 64-row block,
 // at 256 VGPRs and twice the LDS, ran in two rounds of workgroups.)  The state is read
@@ -57,7 +59,7 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
   __shared__ __attribute__((aligned(16))) bf16_bits KTs[NTI * D * TP];
   __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
-  __shared__ float As[CT][CT + 4];
+  __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
   __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
   __shared__ __attribute__((aligned(16))) float vec[4 * CT];
   __shared__ float vec_tmp[2 * CT];
@@ -189,12 +191,12 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
       transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
       if (wave == 0) {
         const float g = wave_inclusive_scan(lane < nc ? __logf(a_cur) : 0.f);
-        factorize_chunk<CT, D, NTI, NTF, ORD, false, true>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP, vec,
+        factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP, vec,
                                                             vec_tmp);
       } else if (TWO && wave == 1 && n2 > 0) {
         // the second block, at the same time
         const float g = wave_inclusive_scan(lane < n2 ? __logf(a2_row) : 0.f);
-        factorize_chunk<CT, D, NTI, NTF, ORD, false, true>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
+        factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
                                                             vec_tmp2);
       } else {
         // the other waves transpose the second block's keys meanwhile
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
   __shared__ __attribute__((aligned(16))) bf16_bits Qs[NTI * CT * KP];
   __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
-  __shared__ float As[CT][CT + 4];
+  __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
   __shared__ __attribute__((aligned(16))) bf16_bits Ts[NTF * CT * TP];
   __shared__ __attribute__((aligned(16))) bf16_bits Ps[NTF * CT * TP];
   __shared__ __attribute__((aligned(16))) float vec[4 * CT];
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   };
   if (wave == 0) {
     const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD, false, CT == 32, true>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec,
+    factorize_chunk<CT, D, NTI, NTF, ORD, CT == 32, true>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec,
                                                                   vec_tmp);
     if constexpr (NW == 1) {
       lds_barrier();
