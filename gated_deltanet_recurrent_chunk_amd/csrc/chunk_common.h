@@ -156,7 +156,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
 
-  const float gn = __shfl(g, n - 1, 64);
+  const float gn = lane_value(g, n - 1);
   const bool live = lane < n;
   const float eg = __expf(g);
   const float edec = live ? __expf(gn - g) : 0.f;

@@ -171,15 +171,39 @@ __device__ __forceinline__ float row_bcast(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + S, 0xF, 0xF, true));
 }
 
-// Wave-wide inclusive prefix sum (64 lanes), fixed combination order.
+// Wave-wide inclusive prefix sum (64 lanes), fixed combination order, in DPP moves (no
+// LDS round trips): within each 16-lane row by right shifts of 1, 2, 4 and 8 lanes,
+// then the total of rows 0 and 2 (their lane 15) into rows 1 and 3, then the total of
+// rows 0-1 (lane 31) into rows 2 and 3.  Lanes a shift leaves without a source add 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
+  x = dpp_add<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// The same prefix sum through LDS lane permutes (ds_bpermute), doubling the shift from
+// 1 to 32 lanes.
+__device__ __forceinline__ float wave_inclusive_scan_lds(float x) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    float y = __shfl_up(x, off, 64);
+    const float y = __shfl_up(x, off, 64);
     if (lane >= off) x = x + y;
   }
   return x;
+}
+
+// Value of x in lane i (i wave-uniform).
+__device__ __forceinline__ float lane_value(float x, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
 }
 
 }  // namespace gdn

@@ -18,6 +18,15 @@ namespace gdn {
 
 using namespace chunk;
 
+// The gates' running log-decay of a block of nc rows.  Blocks of more than 16 rows use
+// the DPP form; for shorter blocks the LDS form measured faster in this kernel (the
+// flush of at most 16 rows ran 0.6-1.5 us slower with the DPP form, longer blocks
+// 0.1-0.3 us faster; the cause was not found).
+__device__ __forceinline__ float flush_log_decay(float a, int nc) {
+  const float la = (int)(threadIdx.x & 63) < nc ? __logf(a) : 0.f;
+  return nc > 16 ? wave_inclusive_scan(la) : wave_inclusive_scan_lds(la);
+}
+
 // ==================================================================================
 // Replay flush: one workgroup per (request, value head), one wave per 16-row slab of
 // the state.  Reads the state once, applies the accepted rows 32 at a time as blocks of
@@ -190,12 +199,12 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
       lds_barrier();
       transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
       if (wave == 0) {
-        const float g = wave_inclusive_scan(lane < nc ? __logf(a_cur) : 0.f);
+        const float g = flush_log_decay(a_cur, nc);
         factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP, vec,
                                                             vec_tmp);
       } else if (TWO && wave == 1 && n2 > 0) {
         // the second block, at the same time
-        const float g = wave_inclusive_scan(lane < n2 ? __logf(a2_row) : 0.f);
+        const float g = flush_log_decay(a2_row, n2);
         factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
                                                             vec_tmp2);
       } else {

@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   if (wave == 0) {
     const float la = lane < n ? __logf(av) : 0.f;  // rows past n: b = 0, log-decay 0
     const float g = wave_inclusive_scan(la);        // rows past n keep g_{n-1}
-    const float gn = __shfl(g, n - 1, 64);
+    const float gn = lane_value(g, n - 1);
     const float eg = __expf(g);
     rowvec(As, 0, lane) = g;
     rowvec(As, 1, lane) = eg;
