@@ -134,6 +134,38 @@ __device__ __forceinline__ void full_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Column c of Tb = (I + Ab)^-1 for the 16 x 16 diagonal block Ab of a strictly lower
+// triangular fp32 matrix (rows of stride CT + 4, the block's first row and column at
+// 16 bi), by forward substitution X[r] = [r == c] - sum_{s<r} Ab[r][s] X[s] as four
+// interleaved partial sums added in a fixed order.  The coefficients of row r are the
+// same for every lane that works on block bi (LDS broadcast reads), requested one row
+// ahead.
+template <int CT>
+__device__ __forceinline__ void diag_inverse_column(const float (*As)[CT + 4], int bi, int c, float (&X)[16]) {
+  const float(*Ab)[CT + 4] = reinterpret_cast<const float(*)[CT + 4]>(&As[16 * bi][16 * bi]);
+  f32x4 arow[2][4];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r + 1 < 16) {
+#pragma unroll
+      for (int i = 0; i < (r + 4) / 4; ++i) arow[(r + 1) & 1][i] = *reinterpret_cast<const f32x4*>(&Ab[r + 1][4 * i]);
+    }
+    asm volatile("" ::: "memory");
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+    for (int sv = 0; sv < r; ++sv) {
+      const float av = arow[r & 1][sv >> 2][sv & 3];
+      if ((sv & 3) == 0) p0 = fmaf(av, X[sv], p0);
+      if ((sv & 3) == 1) p1 = fmaf(av, X[sv], p1);
+      if ((sv & 3) == 2) p2 = fmaf(av, X[sv], p2);
+      if ((sv & 3) == 3) p3 = fmaf(av, X[sv], p3);
+    }
+    X[r] = (r == c ? 1.f : 0.f) - ((p0 + p1) + (p2 + p3));
+    // row r is finished before the requests for row r + 2 are issued
+    asm volatile("" : "+v"(X[r]) : : "memory");
+  }
+}
+
 // ----------------------------------------------------------------------------------
 // Chunk factorization of the replay kernels (flush and outputs).  One wave.
 //   Ks: NTI swizzled planes (row stride KP) of the chunk's key rows (rows >= n zero).
@@ -212,34 +244,10 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
     // With A = [A00 0; A10 A11] in 16-row blocks, T = [T00 0; -T11 A10 T00 T11],
     // Tii = (I + Aii)^-1.
     // Diagonal blocks, both at once: lane (grp, c) owns column c of block bi = grp & 1
-    // (groups 2 and 3 repeat 0 and 1), forward substitution over the block's 16 rows,
-    // T[r][c] = [r == c] - sum_{s<r} A[r][s] T[s][c], as four interleaved partial sums.
-    // The coefficients of row r are the same for the block's 16 lanes (LDS broadcast
-    // reads), requested one row ahead.
+    // (groups 2 and 3 repeat 0 and 1).
     const int bi = grp & 1;
-    const float(*Ab)[CT + 4] = reinterpret_cast<const float(*)[CT + 4]>(&As[16 * bi][16 * bi]);
     float X[16];
-    f32x4 arow[2][4];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r + 1 < 16) {
-#pragma unroll
-        for (int i = 0; i < (r + 4) / 4; ++i) arow[(r + 1) & 1][i] = *reinterpret_cast<const f32x4*>(&Ab[r + 1][4 * i]);
-      }
-      asm volatile("" ::: "memory");
-      float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-      for (int sv = 0; sv < r; ++sv) {
-        const float av = arow[r & 1][sv >> 2][sv & 3];
-        if ((sv & 3) == 0) p0 = fmaf(av, X[sv], p0);
-        if ((sv & 3) == 1) p1 = fmaf(av, X[sv], p1);
-        if ((sv & 3) == 2) p2 = fmaf(av, X[sv], p2);
-        if ((sv & 3) == 3) p3 = fmaf(av, X[sv], p3);
-      }
-      X[r] = (r == col ? 1.f : 0.f) - ((p0 + p1) + (p2 + p3));
-      // row r is finished before the requests for row r + 2 are issued
-      asm volatile("" : "+v"(X[r]) : : "memory");
-    }
+    diag_inverse_column<CT>(As, bi, col, X);
     if (grp < 2) {
       const int pc = swz(16 * bi + col);
 #pragma unroll

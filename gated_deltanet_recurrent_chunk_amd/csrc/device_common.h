@@ -165,12 +165,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Lane S of each 16-lane row of the wave, broadcast to the whole row (DPP row_newbcast).
-template <int S>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + S, 0xF, 0xF, true));
-}
-
 // Wave-wide inclusive prefix sum (64 lanes), fixed combination order, in DPP moves (no
 // LDS round trips): within each 16-lane row by right shifts of 1, 2, 4 and 8 lanes,
 // then the total of rows 0 and 2 (their lane 15) into rows 1 and 3, then the total of

@@ -327,23 +327,12 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
   // T_ii = (I + A_ii)^-1.
   //
   // P2a (one wave; which one rotates with the workgroup): the four T_ii at once, lane
-  // 16 bi + c owning column c of T_bi,bi, forward substitution over 16 rows whose
-  // coefficients A[16 bi + r][16 bi + s] come from lane (bi, s) of the same 16-lane row
-  // (a DPP broadcast within the row).  Written as bf16 terms, row-major, to Td.
+  // 16 bi + c owning column c of T_bi,bi (forward substitution over 16 rows, the shared
+  // diag_inverse_column).  Written as bf16 terms, row-major, to Td.
   if (W == p2_wave) {
     const int bi = lane >> 4, c = lane & 15;
-    float R[16], X[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) R[r] = As[16 * bi + r][16 * bi + c];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
-      static_for<16>([&](auto sc) {
-        constexpr int sv = decltype(sc)::value;
-        if (sv < r) ps[sv & 3] = fmaf(row_bcast<sv>(R[r]), X[sv], ps[sv & 3]);
-      });
-      X[r] = (r == c ? 1.f : 0.f) - ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-    }
+    float X[16];
+    diag_inverse_column<CT>(As, bi, c, X);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       bf16_bits tt[NTF];
