@@ -18,10 +18,8 @@ namespace gdn {
 
 using namespace chunk;
 
-// The gates' running log-decay of a block of nc rows.  Blocks of more than 16 rows use
-// the DPP form; for shorter blocks the LDS form measured faster in this kernel (the
-// flush of at most 16 rows ran 0.6-1.5 us slower with the DPP form, longer blocks
-// 0.1-0.3 us faster; the cause was not found).
+// The gates' running log-decay of a block of nc rows: the DPP form for blocks of more
+// than 16 rows, the LDS form for shorter ones (see short_req in the kernel).
 __device__ __forceinline__ float flush_log_decay(float a, int nc) {
   const float la = (int)(threadIdx.x & 63) < nc ? __logf(a) : 0.f;
   return nc > 16 ? wave_inclusive_scan(la) : wave_inclusive_scan_lds(la);
@@ -44,10 +42,12 @@ __device__ __forceinline__ float flush_log_decay(float a, int nc) {
 // at 256 VGPRs and twice the LDS, ran in two rounds of workgroups.)  The state is read
 // non-temporal and written through to device scope (store16_through).
 //
+// The state update reads its K^T operands from the key rows by transposing LDS reads,
+// or, for requests of at most 16 rows, from a transposed copy (short_req below).
+//
 // Logs of more than 32 slots (TWO): a second block's factorization does not depend on
 // the state, so its keys and gates are loaded with the first block's; wave 1 factorizes
-// it into its own LDS while wave 0 factorizes the first, and the other waves transpose
-// its keys meanwhile.  Its values are requested once the first block's are staged and
+// it into its own LDS while wave 0 factorizes the first.  Its values are requested once the first block's are staged and
 // are written, as bf16, over its A once the factorizations are done, so its products
 // follow the first block's after a single barrier.
 template <typename IO, int D, bool TWO>
@@ -66,6 +66,7 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   static_assert(!TWO || NW >= 3, "the two-block form needs head dim >= 64");
 
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
+  // the first block's keys transposed (requests of at most 16 rows, see short_req)
   __shared__ __attribute__((aligned(16))) bf16_bits KTs[NTI * D * TP];
   __shared__ __attribute__((aligned(16))) float Vs[CT * VP];
   __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
@@ -75,7 +76,6 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   // the second block's keys, factorization and gate vectors (TWO)
   constexpr int C2 = TWO ? CT : 1;
   __shared__ __attribute__((aligned(16))) bf16_bits Ks2[NTI * C2 * KP];
-  __shared__ __attribute__((aligned(16))) bf16_bits KTs2[NTI * (TWO ? D : 1) * TP];
   // As2 holds the second block's A until its factorization is done, then its values
   // (bf16 rows of V2P elements, padded so that rows four apart fall in other banks)
   constexpr int V2P = D + 2;
@@ -107,6 +107,15 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
 
   const int hk = h / p.group;
   const int my_row = wave * 16 + col;
+  // Requests of at most 16 rows take two slower-looking steps before the factorization:
+  // all waves copy the keys transposed (the state update reads K^T from that copy) and
+  // the gates' prefix sum runs through LDS.  Longer requests read K^T from the key rows by
+  // transposing reads and take the DPP prefix sum.  Measured both ways on both forms of
+  // the kernel: the short forms made requests of at most 16 rows 0.3-1.1 us faster and
+  // longer ones 0.2-0.8 us slower.  Per-workgroup timestamps show the difference in the
+  // load and store phases, not in the changed steps: the first workgroups' state stores,
+  // issued earlier, compete with the state reads of the rest.
+  const bool short_req = n <= 16;
   float* state = p.state_pool + ((size_t)slot * p.Hv + h) * D * D;
   if constexpr (D < 32) zero_lds(Ks, sizeof(Ks), tid, NTH);  // padding columns, never written
   if constexpr (D < 32 && TWO) zero_lds(Ks2, sizeof(Ks2), tid, NTH);
@@ -166,6 +175,28 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   for (int jt = 0; jt < DT; ++jt)
     S[jt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (size_t)my_row * D + 16 * jt + 4 * grp));
 
+  // A operand of K^T (state tile jt, k-step s over the block's rows) from a key-row plane,
+  // by transposing LDS reads: in each 16-lane group, ds_read_b64_tr_b16 gives lane i, as
+  // its element e, the 16-bit value at lane 4 e + i / 4's address plus i % 4 elements.
+  // Lane 4 e + c of group grp names row 32 s + 16 h + 4 grp + e (read h = 0, 1) at the
+  // run of four key columns 16 jt + 4 c (contiguous in the swizzled order), so lane
+  // (col, grp) receives K[32 s + 16 h + 4 grp + e][16 jt + col]: elements 4 h + e of the
+  // operand under the contraction order kappa.
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
+  typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+  auto kt_operand = [&](const bf16_bits* plane, int jt, int s) {
+    const int e = (lane >> 2) & 3, c4 = lane & 3;
+    u32x2_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16_bits* a = plane + (32 * s + 16 * h + 4 * grp + e) * KP + swz(16 * jt + 4 * c4);
+      w[h] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (__attribute__((address_space(3))) v4s*)a));
+    }
+    return __builtin_bit_cast(bf16x8, u32x4_t{w[0][0], w[0][1], w[1][0], w[1][1]});
+  };
+
   // one block of rows c0 .. c0 + nc - 1; written out twice below rather than as a loop,
   // which would hoist every LDS address of the products out of it and hold them all in
   // registers
@@ -197,21 +228,18 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
         if (n2 > 0) load_values(CT, n2);
       }
       lds_barrier();
-      transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
+      if (short_req) transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
       if (wave == 0) {
         const float g = flush_log_decay(a_cur, nc);
         factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP, vec,
                                                             vec_tmp);
       } else if (TWO && wave == 1 && n2 > 0) {
-        // the second block, at the same time
-        const float g = flush_log_decay(a2_row, n2);
+        // the second block, at the same time (its prefix sum in DPP moves at any length:
+        // every wave waits for it at the first barrier)
+        const float g = wave_inclusive_scan(lane < n2 ? __logf(a2_row) : 0.f);
         factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
                                                             vec_tmp2);
       } else {
-        // the other waves transpose the second block's keys meanwhile
-        if constexpr (TWO) {
-          if (n2 > 0) transpose_keys<CT, D, NTI>(Ks2, KP, KTs2, D * TP, TP, tid - 128, NTH - 128);
-        }
         // match the barriers inside factorize_chunk
         lds_barrier();
         lds_barrier();
@@ -295,7 +323,12 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
         bf16x8 a[NTI];
-        op_terms<NTI>(PRE ? KTs2 : KTs, D * TP, TP, 16 * jt + col, s, grp, a);
+        if (!PRE && short_req) {
+          op_terms<NTI>(KTs, D * TP, TP, 16 * jt + col, s, grp, a);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NTI; ++i) a[i] = kt_operand(Kb + i * CT * KP, jt, s);
+        }
         mma_terms<NTI, NTF, ORD>(acc, a, Dtop[s]);
       }
       S[jt] = acc;
