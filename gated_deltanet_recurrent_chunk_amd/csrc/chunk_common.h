@@ -172,7 +172,7 @@ __device__ __forceinline__ void diag_inverse_column(const float (*As)[CT + 4], i
 //   g, bb: this lane's g_t and b_t for t = lane (t >= n: g_t = g_{n-1}, b_t = 0).
 // Writes T = (I + A)^-1 as NTF swizzled bf16 planes (row stride tld, plane stride
 // tps) and the four per-row vectors g, exp(g), b, exp(g_n - g) into vec_out.
-// BLOCKED (32-row chunks): T by 16-row blocks, see below.
+// BLOCKED (32- and 64-row chunks): T by 16-row blocks, see below.
 // Barriers: the first publishes the row vectors to the whole workgroup.  The second
 // orders this wave's A tiles before its own substitution reads them: with LOCAL_A it
 // is a wait for this wave's LDS traffic only, so the other waves match one barrier and
@@ -184,7 +184,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   constexpr int KP = row_stride(D);
   constexpr int KSD = (D + 31) / 32;
   constexpr int MT = CT / 16;
-  static_assert(!BLOCKED || CT == 32, "the blocked inverse covers 32-row chunks");
+  static_assert(!BLOCKED || CT == 32 || CT == 64, "the blocked inverse covers 32- and 64-row chunks");
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
 
@@ -205,11 +205,13 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   // A = strict lower part of diag(b) exp(g_t - g_s) K K^T
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    // BLOCKED: with n <= 16 the second row tile of A is zero; the diagonal tile is
-    // stored as zeros (the substitution reads it) and the other is not read
+    // BLOCKED: row tiles at or past n are zero; their diagonal tiles are stored as zeros
+    // (the substitution reads them) and the others are not read
     if (BLOCKED && 16 * mt >= n) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) As[16 + 4 * grp + r][16 + col] = 0.f;
+      for (int m2 = mt; m2 < MT; ++m2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) As[16 * m2 + 4 * grp + r][16 * m2 + col] = 0.f;
       break;
     }
 #pragma unroll
@@ -240,7 +242,94 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   else
     lds_barrier();
 
-  if constexpr (BLOCKED) {
+  if constexpr (BLOCKED && CT == 64) {
+    // Block forward substitution over four 16-row blocks: block row i of T's column tile
+    // W is Tii (E - U), U = A[block i, 0 : 16 i] T[0 : 16 i, tile W], Tii = (I + Aii)^-1
+    // (E: the identity's block, zero off the diagonal).  Lane group grp inverts diagonal
+    // block grp; the off-diagonal blocks follow on the matrix cores, column tile by
+    // column tile, each block row's C layout serving as the B operand of the next ones.
+    float X[16];
+    diag_inverse_column<CT>(As, grp, col, X);
+    {
+      const int pc = swz(16 * grp + col);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bf16_bits tt[NTF];
+        split_terms<NTF>(X[r], tt);
+#pragma unroll
+        for (int q = 0; q < NTF; ++q) Tout[q * tps + (16 * grp + r) * tld + pc] = tt[q];
+      }
+      // zeros above the diagonal: tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3), as runs of
+      // eight columns (192 runs, three per lane)
+      const uint2 z{0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int task = lane + 64 * k, ti = task >> 5, zr = (task & 31) >> 1, zc = 8 * (task & 1);
+        const int tr = ti < 3 ? 0 : ti < 5 ? 1 : 2, tc = ti < 3 ? ti + 1 : ti < 5 ? ti - 1 : 3;
+#pragma unroll
+        for (int q = 0; q < NTF; ++q) {
+          bf16_bits* p = Tout + q * tps + (16 * tr + zr) * tld;
+          *reinterpret_cast<uint2*>(p + swz(16 * tc + zc)) = z;
+          *reinterpret_cast<uint2*>(p + swz(16 * tc + zc + 4)) = z;
+        }
+      }
+    }
+    // the diagonal blocks, read back by other lanes of this wave
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+#pragma unroll
+    for (int W = 0; W < 3; ++W) {
+      f32x4 Tb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Tb[i] = zero4();
+        if (i < W) continue;
+        if (i > W && 16 * i >= n) {
+          // rows at or past n: identity rows, zero off the diagonal
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int q = 0; q < NTF; ++q) Tout[q * tps + (16 * i + 4 * grp + r) * tld + swz(16 * W + col)] = 0;
+          continue;
+        }
+        f32x4 u = zero4();
+        if (i > W) {
+#pragma unroll
+          for (int sp = 0; sp < (16 * i + 31) / 32; ++sp) {
+            // A rows 16 i + col; contraction elements at or past 16 i are dropped
+            const bool keep_hi = 32 * sp + 16 < 16 * i;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 4 * grp]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(&As[16 * i + col][32 * sp + 16 + 4 * grp]);
+            bf16x8 a[NTF], b[NTF];
+            reg_operand<NTF>(lo, keep_hi ? hi : zero4(), a);
+            reg_operand<NTF>(Tb[2 * sp], keep_hi ? Tb[2 * sp + 1] : zero4(), b);
+            mma_terms<NTF, NTF, ORD>(u, a, b);
+          }
+        }
+        f32x4 em;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) em[r] = (16 * i + 4 * grp + r == 16 * W + col ? 1.f : 0.f) - u[r];
+        bf16x8 tii[NTF], e_op[NTF];
+#pragma unroll
+        for (int q = 0; q < NTF; ++q) {
+          const uint2 w = *reinterpret_cast<const uint2*>(Tout + q * tps + (16 * i + col) * tld + swz(16 * i + 4 * grp));
+          tii[q] = __builtin_bit_cast(bf16x8, u32x4_t{w.x, w.y, 0u, 0u});
+        }
+        reg_operand<NTF>(em, zero4(), e_op);
+        mma_terms<NTF, NTF, ORD>(Tb[i], tii, e_op);
+        if (i > W) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bf16_bits tt[NTF];
+            split_terms<NTF>(Tb[i][r], tt);
+#pragma unroll
+            for (int q = 0; q < NTF; ++q) Tout[q * tps + (16 * i + 4 * grp + r) * tld + swz(16 * W + col)] = tt[q];
+          }
+        }
+      }
+    }
+    return;
+  } else if constexpr (BLOCKED) {
     // With A = [A00 0; A10 A11] in 16-row blocks, T = [T00 0; -T11 A10 T00 T11],
     // Tii = (I + Aii)^-1.
     // Diagonal blocks, both at once: lane (grp, c) owns column c of block bi = grp & 1

@@ -477,7 +477,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   };
   if (wave == 0) {
     const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD, CT == 32, true>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec,
+    factorize_chunk<CT, D, NTI, NTF, ORD, true, true>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec,
                                                                   vec_tmp);
     if constexpr (NW == 1) {
       lds_barrier();

@@ -439,6 +439,8 @@ REPLAY_CASES = [
     (64, torch.bfloat16, 64, [(0, 40, 17), (2, 0, 3), (1, 63, 1), (3, 47, 17)]),
     (32, torch.float32, 64, [(3, 30, 17), (0, 1, 16), (2, 0, 0)]),
     (128, torch.float32, 32, [(1, 20, 12), (0, 0, 17), (3, 31, 1), (2, 9, 0), (4, 15, 16)]),
+    # 64-row logs at d = 128: blocks of 14, 32, 57 and 64 rows (one to four 16-row blocks)
+    (128, torch.bfloat16, 64, [(0, 40, 17), (2, 5, 9), (1, 47, 17), (3, 16, 16)]),
 ]
 
 

@@ -1,9 +1,7 @@
 """Kernel resource checks on the CPU (device assembly of the library's own sources):
 every kernel runs without a private (scratch) segment.  A kernel whose argument block
 the compiler copies to private memory would pay a 1.5 KiB per-lane copy at every launch,
-and kernels read their call tables in place in the kernel-argument segment.  The one
-known exception is a two-register spill of the replay kernel for 64-row logs at
-d = 128 (a variant the workloads do not time)."""
+and kernels read their call tables in place in the kernel-argument segment."""
 import os
 import re
 import subprocess
@@ -27,6 +25,5 @@ def test_kernels_use_no_private_segment(src, tmp_path):
     kernels = re.findall(r"^\t\.amdhsa_kernel (\S+)$", text, re.M)
     sizes = re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)
     assert kernels and len(kernels) == len(sizes)
-    allowed = {"_ZN3gdn13replay_kernelItLi128ELi64EEEvNS_10ReplayArgsIT_EE": 16}
-    bad = [(k, int(n)) for k, n in zip(kernels, sizes) if int(n) > allowed.get(k, 0)]
+    bad = [(k, int(n)) for k, n in zip(kernels, sizes) if int(n) > 0]
     assert not bad, bad
