@@ -47,9 +47,10 @@ __device__ __forceinline__ float flush_log_decay(float a, int nc) {
 //
 // Logs of more than 32 slots (TWO): a second block's factorization does not depend on
 // the state, so its keys and gates are loaded with the first block's; wave 1 factorizes
-// it into its own LDS while wave 0 factorizes the first.  Its values are requested once the first block's are staged and
-// are written, as bf16, over its A once the factorizations are done, so its products
-// follow the first block's after a single barrier.
+// it into its own LDS while wave 0 factorizes the first.  Its values are requested once
+// the first block's are staged and written, as bf16, to their own buffer before the
+// barrier that ends the factorizations, so its products follow the first block's with
+// no barrier between them.
 template <typename IO, int D, bool TWO>
 __global__ __launch_bounds__(64 * (D / 16), (sizeof(IO) == 2 && D >= 64) ? (TWO ? 2 : 4) : 1)
 void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<IO> p) {
@@ -76,13 +77,12 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   // the second block's keys, factorization and gate vectors (TWO)
   constexpr int C2 = TWO ? CT : 1;
   __shared__ __attribute__((aligned(16))) bf16_bits Ks2[NTI * C2 * KP];
-  // As2 holds the second block's A until its factorization is done, then its values
-  // (bf16 rows of V2P elements, padded so that rows four apart fall in other banks)
+  // the second block's A, and its values (bf16 rows of V2P elements, padded so that rows
+  // four apart fall in other banks)
   constexpr int V2P = D + 2;
-  constexpr int A2W = (CT * V2P / 2 > CT * (CT + 4)) ? CT * V2P / 2 : CT * (CT + 4);
-  __shared__ __attribute__((aligned(16))) float As2buf[TWO ? A2W : CT + 4];
+  __shared__ __attribute__((aligned(16))) float As2buf[TWO ? CT * (CT + 4) : CT + 4];
   float(*const As2)[CT + 4] = reinterpret_cast<float(*)[CT + 4]>(As2buf);
-  bf16_bits* const V2 = reinterpret_cast<bf16_bits*>(As2buf);
+  __shared__ __attribute__((aligned(16))) bf16_bits V2[TWO ? CT * V2P : 2];
   __shared__ __attribute__((aligned(16))) bf16_bits Ts2[NTF * C2 * TP];
   __shared__ __attribute__((aligned(16))) float vec2[4 * C2];
   __shared__ float vec_tmp2[2 * C2];
@@ -207,8 +207,10 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
     const bf16_bits* Tb = PRE ? Ts2 : Ts;
     const float* vb_ = PRE ? vec2 : vec;
     // the previous block's readers are done with the LDS (first block: the zero fill,
-    // d < 32, precedes the row stores; PRE: the second block's values are in V2)
-    lds_barrier();
+    // d < 32, precedes the row stores).  PRE reads only what the first block's barrier
+    // after the factorizations published (its keys, factors, gate vectors and values),
+    // and nothing the first block's products write: no barrier.
+    if constexpr (!PRE) lds_barrier();
     if constexpr (!PRE) {
 #pragma unroll
       for (int i = 0; i < PER_THR; ++i) {
@@ -244,10 +246,9 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
         lds_barrier();
         lds_barrier();
       }
-      lds_barrier();
       if constexpr (TWO) {
-        // the second block's values over its A (no longer read); read after the next
-        // block's opening barrier
+        // the second block's values (requested with the first block's staging), published
+        // by the barrier below
         if (n2 > 0) {
 #pragma unroll
           for (int i = 0; i < PER_THR; ++i) {
@@ -259,7 +260,9 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
             }
           }
         }
-      } else {
+      }
+      lds_barrier();
+      if constexpr (!TWO) {
         // the next block's rows (n <= 2 CT), requested after the factorization, whose
         // registers they would otherwise add to, and in flight during the products
         if (c0 + CT < n) load_rows(c0 + CT, n - c0 - CT);
