@@ -166,6 +166,36 @@ __device__ __forceinline__ void diag_inverse_column(const float (*As)[CT + 4], i
   }
 }
 
+// Tile (mt, nt) of A = strict lower part of diag(b) exp(g_t - g_s) K K^T (one wave):
+// Ks holds NTI swizzled key-row planes, vec_lds the rows' g (first CT) and b (next CT).
+template <int CT, int D, int NTI, int ORD>
+__device__ __forceinline__ void form_a_tile(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n, int mt, int nt,
+                                            const float* vec_lds) {
+  constexpr int KP = row_stride(D);
+  constexpr int KSD = (D + 31) / 32;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int s = 0; s < KSD; ++s) {
+    bf16x8 a[NTI], b[NTI];
+    op_terms<NTI>(Ks, kps, KP, 16 * mt + col, s, grp, a);
+    op_terms<NTI>(Ks, kps, KP, 16 * nt + col, s, grp, b);
+    mma_terms<NTI, NTI, ORD>(acc, a, b);
+  }
+  const int sc = 16 * nt + col;
+  const float gs = vec_lds[sc];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 16 * mt + 4 * grp + r;
+    // computed for every element (pinned, so that the compiler does not move the LDS
+    // reads into a branch per element) and kept or dropped by the select
+    float dec = __expf(vec_lds[t] - gs), bt = vec_lds[CT + t];
+    asm volatile("" : "+v"(dec), "+v"(bt));
+    As[t][sc] = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
+  }
+}
+
 // ----------------------------------------------------------------------------------
 // Chunk factorization of the replay kernels (flush and outputs).  One wave.
 //   Ks: NTI swizzled planes (row stride KP) of the chunk's key rows (rows >= n zero).
@@ -176,13 +206,13 @@ __device__ __forceinline__ void diag_inverse_column(const float (*As)[CT + 4], i
 // Barriers: the first publishes the row vectors to the whole workgroup.  The second
 // orders this wave's A tiles before its own substitution reads them: with LOCAL_A it
 // is a wait for this wave's LDS traffic only, so the other waves match one barrier and
-// are not held while the A tiles are formed.
-template <int CT, int D, int NTI, int NTF, int ORD, bool BLOCKED = false, bool LOCAL_A = false>
+// are not held while the A tiles are formed.  HELPED (not with LOCAL_A): this wave forms
+// only the first row tile of A; the caller's other waves form the rest between the two
+// barriers.
+template <int CT, int D, int NTI, int NTF, int ORD, bool BLOCKED = false, bool LOCAL_A = false, bool HELPED = false>
 __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n,
                                                 float g, float bb, bf16_bits* Tout, int tps, int tld,
                                                 float* vec_out, float* vec_lds) {
-  constexpr int KP = row_stride(D);
-  constexpr int KSD = (D + 31) / 32;
   constexpr int MT = CT / 16;
   static_assert(!BLOCKED || CT == 32 || CT == 64, "the blocked inverse covers 32- and 64-row chunks");
   const int lane = threadIdx.x & 63;
@@ -214,28 +244,11 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
         for (int r = 0; r < 4; ++r) As[16 * m2 + 4 * grp + r][16 * m2 + col] = 0.f;
       break;
     }
+    // HELPED: row tiles past the first are formed by other waves (form_a_tile) between
+    // this function's two barriers
+    if (HELPED && mt >= 1) break;
 #pragma unroll
-    for (int nt = 0; nt <= mt; ++nt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < KSD; ++s) {
-        bf16x8 a[NTI], b[NTI];
-        op_terms<NTI>(Ks, kps, KP, 16 * mt + col, s, grp, a);
-        op_terms<NTI>(Ks, kps, KP, 16 * nt + col, s, grp, b);
-        mma_terms<NTI, NTI, ORD>(acc, a, b);
-      }
-      const int sc = 16 * nt + col;
-      const float gs = vec_lds[sc];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mt + 4 * grp + r;
-        // computed for every element (pinned, so that the compiler does not move the LDS
-        // reads into a branch per element) and kept or dropped by the select
-        float dec = __expf(vec_lds[t] - gs), bt = vec_lds[CT + t];
-        asm volatile("" : "+v"(dec), "+v"(bt));
-        As[t][sc] = (sc < t && t < n) ? bt * dec * acc[r] : 0.f;
-      }
-    }
+    for (int nt = 0; nt <= mt; ++nt) form_a_tile<CT, D, NTI, ORD>(Ks, kps, As, n, mt, nt, vec_lds);
   }
   if constexpr (LOCAL_A)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
