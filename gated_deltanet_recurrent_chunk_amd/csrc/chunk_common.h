@@ -202,19 +202,20 @@ __device__ __forceinline__ void form_a_tile(const bf16_bits* Ks, int kps, float 
 //   g, bb: this lane's g_t and b_t for t = lane (t >= n: g_t = g_{n-1}, b_t = 0).
 // Writes T = (I + A)^-1 as NTF swizzled bf16 planes (row stride tld, plane stride
 // tps) and the four per-row vectors g, exp(g), b, exp(g_n - g) into vec_out.
-// BLOCKED (32- and 64-row chunks): T by 16-row blocks, see below.
+// T is formed by 16-row blocks (32- and 64-row chunks), see below.
 // Barriers: the first publishes the row vectors to the whole workgroup.  The second
 // orders this wave's A tiles before its own substitution reads them: with LOCAL_A it
 // is a wait for this wave's LDS traffic only, so the other waves match one barrier and
 // are not held while the A tiles are formed.  HELPED (not with LOCAL_A): this wave forms
 // only the first row tile of A; the caller's other waves form the rest between the two
 // barriers.
-template <int CT, int D, int NTI, int NTF, int ORD, bool BLOCKED = false, bool LOCAL_A = false, bool HELPED = false>
+template <int CT, int D, int NTI, int NTF, int ORD, bool LOCAL_A = false, bool HELPED = false>
 __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n,
                                                 float g, float bb, bf16_bits* Tout, int tps, int tld,
                                                 float* vec_out, float* vec_lds) {
   constexpr int MT = CT / 16;
-  static_assert(!BLOCKED || CT == 32 || CT == 64, "the blocked inverse covers 32- and 64-row chunks");
+  static_assert(CT == 32 || CT == 64, "the blocked inverse covers 32- and 64-row chunks");
+  static_assert(!(HELPED && LOCAL_A), "helper waves need the full second barrier");
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
 
@@ -235,9 +236,9 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   // A = strict lower part of diag(b) exp(g_t - g_s) K K^T
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    // BLOCKED: row tiles at or past n are zero; their diagonal tiles are stored as zeros
+    // row tiles at or past n are zero; their diagonal tiles are stored as zeros
     // (the substitution reads them) and the others are not read
-    if (BLOCKED && 16 * mt >= n) {
+    if (16 * mt >= n) {
 #pragma unroll
       for (int m2 = mt; m2 < MT; ++m2)
 #pragma unroll
@@ -255,7 +256,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   else
     lds_barrier();
 
-  if constexpr (BLOCKED && CT == 64) {
+  if constexpr (CT == 64) {
     // Block forward substitution over four 16-row blocks: block row i of T's column tile
     // W is Tii (E - U), U = A[block i, 0 : 16 i] T[0 : 16 i, tile W], Tii = (I + Aii)^-1
     // (E: the identity's block, zero off the diagonal).  Lane group grp inverts diagonal
@@ -342,7 +343,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
       }
     }
     return;
-  } else if constexpr (BLOCKED) {
+  } else {
     // With A = [A00 0; A10 A11] in 16-row blocks, T = [T00 0; -T11 A10 T00 T11],
     // Tii = (I + Aii)^-1.
     // Diagonal blocks, both at once: lane (grp, c) owns column c of block bi = grp & 1
@@ -416,43 +417,6 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
       }
     }
     return;
-  }
-
-  // Forward substitution, lane j owns column j:  T[t][j] = [t == j] - sum_{s<t} A[t][s] T[s][j].
-  // The sum runs as four interleaved partial sums (s mod 4) added in a fixed order.  Row
-  // t + 1 of A is requested from LDS before the sums of row t run, so the LDS latency
-  // overlaps them; two rows of A are live in registers.
-  float Tc[CT];
-  f32x4 arow[2][CT / 4];
-#pragma unroll
-  for (int t = 0; t < CT; ++t) {
-    if (t + 1 < CT) {
-#pragma unroll
-      for (int i = 0; i < (t + 4) / 4; ++i) arow[(t + 1) & 1][i] = *reinterpret_cast<const f32x4*>(&As[t + 1][4 * i]);
-    }
-    asm volatile("" ::: "memory");
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-    for (int s = 0; s < t; ++s) {
-      const float av = arow[t & 1][s >> 2][s & 3];
-      if ((s & 3) == 0) p0 = fmaf(av, Tc[s], p0);
-      if ((s & 3) == 1) p1 = fmaf(av, Tc[s], p1);
-      if ((s & 3) == 2) p2 = fmaf(av, Tc[s], p2);
-      if ((s & 3) == 3) p3 = fmaf(av, Tc[s], p3);
-    }
-    Tc[t] = (t == lane ? 1.f : 0.f) - ((p0 + p1) + (p2 + p3));
-    // row t is finished before the requests for row t + 2 are issued
-    asm volatile("" : "+v"(Tc[t]) : : "memory");
-  }
-  if (lane < CT) {
-    const int pc = swz(lane);
-#pragma unroll
-    for (int t = 0; t < CT; ++t) {
-      bf16_bits tt[NTF];
-      split_terms<NTF>(Tc[t], tt);
-#pragma unroll
-      for (int i = 0; i < NTF; ++i) Tout[i * tps + t * tld + pc] = tt[i];
-    }
   }
 }
 

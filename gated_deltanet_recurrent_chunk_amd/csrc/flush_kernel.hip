@@ -236,13 +236,13 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
       if (short_req) transpose_keys<CT, D, NTI>(Ks, KP, KTs, D * TP, TP, tid, NTH);
       if (wave == 0) {
         const float g = flush_log_decay(a_cur, nc);
-        factorize_chunk<CT, D, NTI, NTF, ORD, true, false, HELP>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP,
+        factorize_chunk<CT, D, NTI, NTF, ORD, false, HELP>(Ks, CT * KP, As, nc, g, b_cur, Ts, CT * TP, TP,
                                                                    vec, vec_tmp);
       } else if (TWO && wave == 1 && n2 > 0) {
         // the second block, at the same time (its prefix sum in DPP moves at any length:
         // every wave waits for it at the first barrier)
         const float g = wave_inclusive_scan(lane < n2 ? __logf(a2_row) : 0.f);
-        factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
+        factorize_chunk<CT, D, NTI, NTF, ORD>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
                                                             vec_tmp2);
       } else {
         // match the barriers inside factorize_chunk; in between, waves 2 and 3 form the
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   };
   if (wave == 0) {
     const float g = wave_inclusive_scan(lane < L ? __logf(a_row) : 0.f);
-    factorize_chunk<CT, D, NTI, NTF, ORD, true, true>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec,
+    factorize_chunk<CT, D, NTI, NTF, ORD, true>(Ks, CT * KP, As, L, g, bb, Ts, CT * TP, TP, vec,
                                                                   vec_tmp);
     if constexpr (NW == 1) {
       lds_barrier();
