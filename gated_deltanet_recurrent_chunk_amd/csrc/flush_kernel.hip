@@ -28,19 +28,19 @@ __device__ __forceinline__ float flush_log_decay(float a, int nc) {
 // ==================================================================================
 // Replay flush: one workgroup per (request, value head), one wave per 16-row slab of
 // the state.  Reads the state once, applies the accepted rows 32 at a time as blocks of
-// the chunked rule (each block factorized by wave 0, the state carried in registers from
-// block to block), writes the state once.  The barriers order LDS only, so the state
-// loads stay in flight through the staging of the first block and its factorization,
-// and the next block's rows are requested while the current one is applied.
+// the chunked rule (each block factorized by wave 0, with waves 2 and 3 forming part of
+// its A; the state carried in registers from block to block), writes the state once.
+// The barriers order LDS only, so the state loads stay in flight through the staging of
+// the first block and its factorization, and the next block's rows are requested while
+// the current one is applied.
 //
 // One 32-row block covers the common case (a few accepted rows); its inverse is formed
 // by 16-row blocks (two diagonal substitutions at once, then one off-diagonal block by
 // two products), and with at most 16 rows only the first diagonal block is not the
-// identity.  The
-// kernel fits in 128 VGPRs, so two workgroups share a CU and the whole grid is resident
-// at once.  (A 16-row block measured slower than this 32-row one, and a 64-row block,
-// at 256 VGPRs and twice the LDS, ran in two rounds of workgroups.)  The state is read
-// non-temporal and written through to device scope (store16_through).
+// identity.  The kernel fits in 128 VGPRs, so two workgroups share a CU and the whole
+// grid is resident at once.  (A 16-row block measured slower than this 32-row one, and a
+// 64-row block, at 256 VGPRs and twice the LDS, ran in two rounds of workgroups.)  The
+// state is read non-temporal and written through to device scope (store16_through).
 //
 // The state update reads its K^T operands from the key rows by transposing LDS reads,
 // or, for requests of at most 16 rows, from a transposed copy (short_req below).
@@ -477,8 +477,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void replay_kernel(ReplayArgs<IO> p)
   // of the factorization is done: wave 0 after the factorization, the others after
   // their P tiles.  Requested at the start instead, the second workgroup of a CU waited
   // for its rows and its waves stalled issuing loads while the first workgroup's state
-  // streamed in (measured: 15.0 us, the second workgroups finishing ~4 us after the
-  // first; now 13.0 us).
+  // streamed in (measured: 14.6 us, the second workgroups finishing ~4 us after the
+  // first; 11.6 us with the requests placed here and the factorization's wave-local
+  // second barrier).
   auto load_state = [&]() {
 #pragma unroll
     for (int jt = 0; jt < DT; ++jt)
