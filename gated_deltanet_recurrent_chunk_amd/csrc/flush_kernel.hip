@@ -68,6 +68,8 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
   // waves 2 and 3 form the second row tile of the first block's A while wave 0 forms the
   // first (measured: 17 rows 14.5 -> 13.7 us, 32 rows 14.5 -> 14.2 us)
   constexpr bool HELP = NW >= 4;
+  // the same for the second block of TWO (waves 4 and 5)
+  constexpr bool HELP2 = TWO && NW >= 6;
 
   __shared__ __attribute__((aligned(16))) bf16_bits Ks[NTI * CT * KP];
   // the first block's keys transposed (requests of at most 16 rows, see short_req)
@@ -242,14 +244,17 @@ void flush_kernel(const int32_t* slot_ids, const int32_t* n_accepted, FlushArgs<
         // the second block, at the same time (its prefix sum in DPP moves at any length:
         // every wave waits for it at the first barrier)
         const float g = wave_inclusive_scan(lane < n2 ? __logf(a2_row) : 0.f);
-        factorize_chunk<CT, D, NTI, NTF, ORD>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
-                                                            vec_tmp2);
+        factorize_chunk<CT, D, NTI, NTF, ORD, false, HELP2>(Ks2, CT * KP, As2, n2, g, b2, Ts2, CT * TP, TP, vec2,
+                                                               vec_tmp2);
       } else {
         // match the barriers inside factorize_chunk; in between, waves 2 and 3 form the
-        // tiles (1, 0) and (1, 1) of the first block's A (more than 16 rows)
+        // tiles (1, 0) and (1, 1) of the first block's A (more than 16 rows), and waves 4
+        // and 5 those of the second block's (TWO, more than 16 rows there)
         lds_barrier();
         if (HELP && nc > 16 && (wave == 2 || wave == 3))
           form_a_tile<CT, D, NTI, ORD>(Ks, CT * KP, As, nc, 1, wave - 2, vec_tmp);
+        if (HELP2 && n2 > 16 && (wave == 4 || wave == 5))
+          form_a_tile<CT, D, NTI, ORD>(Ks2, CT * KP, As2, n2, 1, wave - 4, vec_tmp2);
         lds_barrier();
       }
       if constexpr (TWO) {
