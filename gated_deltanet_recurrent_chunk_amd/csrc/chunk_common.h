@@ -206,9 +206,9 @@ __device__ __forceinline__ void form_a_tile(const bf16_bits* Ks, int kps, float 
 // Barriers: the first publishes the row vectors to the whole workgroup.  The second
 // orders this wave's A tiles before its own substitution reads them: with LOCAL_A it
 // is a wait for this wave's LDS traffic only, so the other waves match one barrier and
-// are not held while the A tiles are formed.  HELPED (not with LOCAL_A): this wave forms
-// only the first row tile of A; the caller's other waves form the rest between the two
-// barriers.
+// are not held while the A tiles are formed.  HELPED (32-row chunks, not with LOCAL_A):
+// this wave forms only the first row tile of A; the caller's other waves form the second
+// (tiles (1, 0) and (1, 1), form_a_tile) between the two barriers.
 template <int CT, int D, int NTI, int NTF, int ORD, bool LOCAL_A = false, bool HELPED = false>
 __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, float (*As)[CT + 4], int n,
                                                 float g, float bb, bf16_bits* Tout, int tps, int tld,
@@ -216,6 +216,7 @@ __device__ __forceinline__ void factorize_chunk(const bf16_bits* Ks, int kps, fl
   constexpr int MT = CT / 16;
   static_assert(CT == 32 || CT == 64, "the blocked inverse covers 32- and 64-row chunks");
   static_assert(!(HELPED && LOCAL_A), "helper waves need the full second barrier");
+  static_assert(!HELPED || CT == 32, "helper waves form the second row tile of a 32-row chunk");
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
 
