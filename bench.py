@@ -350,6 +350,10 @@ def main():
     for n in list(range(1, 33)) + [33]:
         sweep[str(n)] = round(statistics.median(flush_us(torch.full((n_req,), n), log32 if n <= 32 else log64,
                                                          batches=5)), 2)
+    # the 64-slot log (the two-block form) at every length class: short, one block, two
+    sweep64 = {str(n): round(statistics.median(flush_us(torch.full((n_req,), n), log64, batches=5)), 2)
+               for n in (8, 16, 32, 48, 64)}
+    sweep64["u1_16"] = round(statistics.median(flush_us(acc_u, log64, batches=5)), 2)
 
     # ------------------------------------------------------------ replay outputs (4B layer)
     note("replay outputs")
@@ -361,6 +365,11 @@ def main():
     replay = batches_us(lambda i: g.replay_forward(fl_layer, fpools[i % n_pools], slots, *log32, logged_d, new_d,
                                                    rq_new, r_out))
     rb = replay_bytes(acc_u.tolist(), n_new)
+    # a 64-slot log: 25..40 logged rows, 16 new (blocks of 41..56 rows)
+    logged64 = (acc_u + 24).to(torch.int32).to(dev)
+    replay64 = batches_us(lambda i: g.replay_forward(fl_layer, fpools[i % n_pools], slots, *log64, logged64, new_d,
+                                                     rq_new, r_out), batches=10)
+    rb64 = replay_bytes((acc_u + 24).tolist(), n_new)
 
     # ------------------------------------------------------------ decode (27B layer, 256 requests)
     note("decode")
@@ -548,14 +557,18 @@ def main():
         "long_prefill": long_res,
         "flush_us_per_layer": {"accepted_u1_16": pct(flush_u), "all_16": sweep["16"], "all_17": sweep["17"],
                                "sweep_all_n": sweep,
-                               "workload": "flush_4b_16req_H32_d128_32slots (64 slots for n = 33)",
+                               "sweep_64slot_log": sweep64,
+                               "workload": "flush_4b_16req_H32_d128_32slots (64 slots for n = 33 and sweep_64slot_log)",
                                "hbm_gbs_u1_16": round(fb_u / (flush_med * 1e-6) / 1e9, 1),
                                "roof_us_u1_16": round(fb_u / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
                                "frac_u1_16": round(fb_u / (flush_med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)},
         "replay_forward_us": {"value": pct(replay),
                               "workload": "replay_4b_16req_H32_d128_32slots_logged_u1_16_new16",
                               "hbm_gbs": round(rb / (replay_med * 1e-6) / 1e9, 1),
-                              "roof_us": round(rb / (PEAK_HBM_GBS * 1e9) * 1e6, 2)},
+                              "roof_us": round(rb / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
+                              "log64": {"value": pct(replay64),
+                                        "workload": "replay_4b_16req_H32_d128_64slots_logged_25_40_new16",
+                                        "roof_us": round(rb64 / (PEAK_HBM_GBS * 1e9) * 1e6, 2)}},
         "decode_us": {"value": pct(decode), "workload": "decode_27b_256req_H48_d128",
                       "hbm_gbs": round(dec_bytes / (decode_med * 1e-6) / 1e9, 1),
                       "roof_us": round(dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
