@@ -161,11 +161,14 @@ __device__ __forceinline__ void row_terms(const RowOp<float>& o, bf16x8 (&t)[NT]
 }  // namespace
 
 // ==================================================================================
-// Pre-pass: one 4-wave workgroup per (chunk, value head).  Two workgroups fit a compute
-// unit (about 75 KiB of LDS each), so every SIMD runs two of these waves.
+// Pre-pass: one 4-wave workgroup per (chunk, value head).  Four workgroups fit a compute
+// unit (34 KiB of LDS each at d = 128 with bf16 inputs), so every SIMD runs four of these
+// waves.
 //
-//   P0 (all waves)  key and query rows into LDS; wave 0 forms the gates g, exp(g), b,
-//                   exp(g_n - g) and writes the record's row vectors.
+//   P0 (all waves)  key rows into LDS; each wave loads the query rows of its own row tile
+//                   straight into registers (they are only ever the B operand of P);
+//                   wave 0 forms the gates g, exp(g), b, exp(g_n - g) and writes the
+//                   record's row vectors.
 //   P1 (per wave)   its share of A = strict-lower(b exp(g_t - g_s) K K^T) into LDS (five
 //                   tiles of the ten lower 16 x 16 tiles per wave, counting P's below),
 //                   the P fragments of its own row tile ut = W (kept in registers), and
@@ -174,24 +177,23 @@ __device__ __forceinline__ void row_terms(const RowOp<float>& o, bf16x8 (&t)[NT]
 //                   diagonal blocks at once; then each wave forms block row i of its 16
 //                   columns as T_ii (E_i - U_i), U_i = A[block i, 0 : 16 i] T[0 : 16 i, :],
 //                   both products on MFMA with the earlier blocks kept in registers.
-//                   Writes T^T rows and T'' (bf16 terms).
-//   P3 (per wave)   T'' fragments and the PT'' fragments of row tile W.
+//                   Writes T^T rows, and the record's T'' fragments from registers.
+//   P3 (per wave)   the PT'' fragments of row tile W.
 //
 // The blocked product runs on split bf16 terms like every other product (fp32 class for
 // bf16 inputs: two terms, order <= 1; fp32 inputs: three terms, order <= 2).
 template <typename IO, int D>
 struct FactorLds {
   using Cfg = PrefillCfg<IO, D>;
-  // T planes unpadded (rows of 64 elements, 128 bytes), in the xor layout (16-byte pieces
-  // permuted by row) so that 16-row operand reads stay free of bank conflicts: with
-  // padded rows the two plane arrays took 18,432 bytes each and the workgroup 54,272
-  // bytes, which LDS allocation granules round past a third of the CU's 160 KiB, so only
-  // two workgroups were resident (measured: 512 at once over 256 CUs).  Now 52,224
-  // bytes, three.
+  // T^T planes unpadded (rows of 64 elements, 128 bytes), in the xor layout (16-byte
+  // pieces permuted by row) so that 16-row operand reads stay free of bank conflicts.
+  // The query rows and T'' need no LDS: the queries are loaded as operands, and T''
+  // leaves through registers.  34,816 bytes at d = 128 with bf16 inputs (113 VGPRs):
+  // four workgroups per CU.
   static constexpr int KP = row_stride(D), TP = CT;
-  static constexpr int KS = Cfg::NTI * CT * KP;  // bf16 elements of the key (or query) planes
-  static constexpr int TT = Cfg::NTF * CT * TP;  // bf16 elements of T^T (or T'') planes
-  static constexpr int QT = KS > TT ? KS : TT;   // query planes, later T''; key planes, later T^T
+  static constexpr int KS = Cfg::NTI * CT * KP;  // bf16 elements of the key planes
+  static constexpr int TT = Cfg::NTF * CT * TP;  // bf16 elements of the T^T planes
+  static constexpr int KT = KS > TT ? KS : TT;   // key planes, later T^T
   // The T_ii planes (NTF terms x 16 bf16 per row of a diagonal block) fit in the
   // diagonal 16 x 16 fp32 blocks of A for NTF <= 2; A is not read there once they exist.
   static constexpr bool TD_IN_A = Cfg::NTF <= 2;
@@ -216,10 +218,56 @@ __host__ __device__ constexpr int a_tile_mt(int i) { return i < 1 ? 0 : i < 3 ? 
 __host__ __device__ constexpr int a_tile_nt(int i) { return i - (i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 3 : 6); }
 __host__ __device__ constexpr int a_tiles_begin(int w) { return w == 0 ? 0 : w == 1 ? 4 : w == 2 ? 7 : w == 3 ? 9 : 10; }
 
+// The query rows of one row tile as B operands of P, straight from memory: lane (col,
+// grp) holds row col of the tile at the contraction elements kappa(s, grp, 0..7), i.e.
+// the runs of four columns 32 s + 4 grp and 32 s + 16 + 4 grp (the order of the key
+// planes).  Rows past the chunk read as zeros (the descriptor ends at the last row);
+// columns past a short row (d = 16) are zero.
+template <typename IO, int D>
+struct QRows {
+  static constexpr int KSD = (D + 31) / 32;
+  using Run = std::conditional_t<sizeof(IO) == 2, u32x2, u32x4>;
+  Run run[KSD][2];
+};
+template <typename IO, int D>
+__device__ __forceinline__ QRows<IO, D> load_q_rows(rsrc_t rq, uint32_t row_off, int grp) {
+  QRows<IO, D> o;
+#pragma unroll
+  for (int s = 0; s < QRows<IO, D>::KSD; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c0 = 32 * s + 16 * h + 4 * grp;
+      if constexpr (sizeof(IO) == 2)
+        o.run[s][h] = c0 < D ? ld8(rq, row_off + (uint32_t)c0 * 2u) : u32x2{0u, 0u};
+      else
+        o.run[s][h] = c0 < D ? ld16(rq, row_off + (uint32_t)c0 * 4u, 0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  return o;
+}
+// Operand terms of k-step s (the same splits the key planes hold).
+template <typename IO, int D, int NT>
+__device__ __forceinline__ void q_terms(const QRows<IO, D>& q, int s, bf16x8 (&out)[NT]) {
+  if constexpr (sizeof(IO) == 2) {
+    static_assert(NT == 1, "bf16 rows are one term");
+    out[0] = __builtin_bit_cast(bf16x8, u32x4{q.run[s][0][0], q.run[s][0][1], q.run[s][1][0], q.run[s][1][1]});
+  } else {
+    bf16_bits tt[8][NT];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split_terms<NT>(__uint_as_float(q.run[s][e >> 2][e & 3]), tt[e]);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      bf16_bits v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
+      out[i] = pack8(v8);
+    }
+  }
+}
+
 template <typename IO, int D, int W>
 __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const int n, uint8_t* rec,
-                                               bf16_bits* Ks, bf16_bits* QT, float (*As)[CT + 4], float (*Ub)[24],
-                                               const int p2_wave) {
+                                               bf16_bits* Ks, const QRows<IO, D>& qrows, float (*As)[CT + 4],
+                                               float (*Ub)[24], const int p2_wave) {
   using Cfg = PrefillCfg<IO, D>;
   using L = FactorLds<IO, D>;
   constexpr int NTI = Cfg::NTI, NTF = Cfg::NTF, ORD = Cfg::ORD;
@@ -227,8 +275,6 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
   constexpr int KSD = (D + 31) / 32, DT = D / 16;
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
   constexpr bool TDA = L::TD_IN_A;
-  const bf16_bits* Qs = QT;
-  bf16_bits* Tl = QT;  // T'' planes, once P1 has read the query rows
   bf16_bits* Tt = Ks;  // T^T planes, once P1 has read the key rows
 
   // ---------------------------------------------------------------- P1
@@ -270,7 +316,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
       bf16x8 bq[NTI], a0[NTI], a1[NTI];
-      op_terms<NTI>(Qs, CT * KP, KP, 16 * W + col, ks, grp, bq);
+      q_terms<IO, D, NTI>(qrows, ks, bq);
       op_terms<NTI>(Ks, CT * KP, KP, 32 * s + col, ks, grp, a0);
       mma_terms<NTI, NTI, ORD>(acc0, a0, bq);
       if (two) {
@@ -348,6 +394,12 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
   // of the B operand over its 16 rows, so the earlier blocks feed U_i and E_i - U_i
   // feeds the product by T_ii without leaving registers.
   {
+    // unit B operand of the transposing products below: element e of lane (col, grp) is
+    // one where 4 grp + e == col (e < 4)
+    bf16_bits u8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u8[e] = (e < 4 && 4 * grp + e == col) ? (bf16_bits)0x3F80 : (bf16_bits)0;
+    const bf16x8 unit = pack8(u8);
     f32x4 Tb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -378,37 +430,37 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       Tb[i] = zero4();
       mma_terms<NTF, NTF, ORD>(Tb[i], tii, e_op);
       // row 16 W + col of T^T (columns 16 i + 4 grp .. + 3, contiguous in the swizzled
-      // order), and T''[t][j] = exp(g_n - g_t) T[t][j] b_j into the T'' planes
+      // order)
       bf16_bits tt[4][NTF];
       const float bj = rowvec(As, 2, 16 * W + col);
-      const int pc = swz(16 * W + col);
 #pragma unroll
       for (int r = 0; r < 4; ++r) split_terms<NTF>(Tb[i][r], tt[r]);
 #pragma unroll
       for (int q = 0; q < NTF; ++q)
         *reinterpret_cast<uint2*>(Tt + q * CT * TP + xrun<2 * TP>(16 * W + col, swz(16 * i + 4 * grp))) =
             uint2{(uint32_t)tt[0][q] | ((uint32_t)tt[1][q] << 16), (uint32_t)tt[2][q] | ((uint32_t)tt[3][q] << 16)};
+      // T''[t][j] = exp(g_n - g_t) T[t][j] b_j: this block's 16 x 16 values, transposed,
+      // are half of the record's T'' fragment (i, W / 2) (lane (col, grp): row 16 i + col,
+      // kappa elements 4 (W % 2) .. + 3).  A product with the unit operand moves each term
+      // exactly from this C layout to the transposed one, and the lane stores it from
+      // there.  Blocks i < 2 (W / 2) lie above the diagonal of every fragment.
+      if (i >= 2 * (W >> 1)) {
+        bf16_bits t2[4][NTF];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * i + 4 * grp + r;
-        bf16_bits t2[NTF];
-        split_terms<NTF>((Tb[i][r] * rowvec(As, 3, t)) * bj, t2);
+        for (int r = 0; r < 4; ++r) split_terms<NTF>((Tb[i][r] * rowvec(As, 3, 16 * i + 4 * grp + r)) * bj, t2[r]);
 #pragma unroll
-        for (int q = 0; q < NTF; ++q) Tl[q * CT * TP + xoff<2 * TP>(t, pc >> 3) + (pc & 7)] = t2[q];
+        for (int q = 0; q < NTF; ++q) {
+          const bf16_bits v8[8] = {t2[0][q], t2[1][q], t2[2][q], t2[3][q], 0, 0, 0, 0};
+          const f32x4 tr = mfma(pack8(v8), unit, zero4());
+          *reinterpret_cast<uint2*>(rec + Cfg::T_OFF + (frag_combo(i, W >> 1) * NTF + q) * 1024 + lane * 16 +
+                                    8 * (W & 1)) = uint2{pack_bf16x2(tr[0], tr[1]), pack_bf16x2(tr[2], tr[3])};
+        }
       }
     }
   }
-  __syncthreads();  // T'' and T^T complete
+  __syncthreads();  // T^T complete
 
   // ---------------------------------------------------------------- P3
-  // T'' fragments: combo f, term q for items W, W + 4, ...
-#pragma unroll
-  for (int it = W; it < kFragCombos * NTF; it += 4) {
-    const int f = it / NTF, q = it % NTF;
-    const int mt = f < 2 ? f : 2 + (f - 2) / 2, s = f < 2 ? 0 : (f - 2) % 2;
-    const bf16x8 v = xop_read<2 * TP>(Tl + q * CT * TP, 16 * mt + col, s, grp);
-    *reinterpret_cast<bf16x8*>(rec + Cfg::T_OFF + it * 1024 + lane * 16) = v;
-  }
   // PT'' = (scale P) T diag(b) for row tile ut = W, through its transpose: tile (jt, W)
   // of PT^T = T^T P^T, A = T^T rows (planes Tt), B = P^T, whose B operand at k-step s' is
   // the A operand of P for (W, s').  Its C layout "lane (col, grp) holds
@@ -454,9 +506,8 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   constexpr int VEC = 16 / sizeof(IO);
   constexpr int PER_ROW = D / VEC;
   constexpr int PIECES = CT * PER_ROW, PER_THR = (PIECES + 255) / 256;
-  // 52,224 bytes at d = 128 with bf16 inputs: three workgroups per CU
-  __shared__ __attribute__((aligned(16))) bf16_bits Ks[L::QT];  // key rows, later T^T
-  __shared__ __attribute__((aligned(16))) bf16_bits QT[L::QT];  // query rows, later T''
+  // 34,816 bytes at d = 128 with bf16 inputs: four workgroups per CU
+  __shared__ __attribute__((aligned(16))) bf16_bits Ks[L::KT];  // key rows, later T^T
   // A; its diagonal blocks later hold the T_ii planes, its padding columns the row vectors
   __shared__ __attribute__((aligned(16))) float As[CT][CT + 4];
   __shared__ __attribute__((aligned(16))) float Ub[L::TD_IN_A ? 1 : CT][24];  // T_ii planes otherwise
@@ -475,7 +526,6 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   // For d < 32 the kappa groups past a 16-wide key row are contracted: keep them zero.
   if constexpr (D < 32) {
     zero_lds(Ks, sizeof(Ks), tid, 256);
-    zero_lds(QT, sizeof(QT), tid, 256);
     __syncthreads();
   }
 
@@ -485,7 +535,7 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
   const uint32_t qsb = (uint32_t)p.qk_stride * sizeof(IO);
   const rsrc_t rk = make_rsrc(p.k + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
   const rsrc_t rq = make_rsrc(p.q + cd.row * p.qk_stride + (int64_t)hk * D, (uint32_t)n * qsb);
-  u32x4 kv[PER_THR], qv[PER_THR];
+  u32x4 kv[PER_THR];
 #pragma unroll
   for (int i = 0; i < PER_THR; ++i) {
     const int idx = tid + 256 * i;
@@ -493,8 +543,8 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
     // pieces past the tile (small d) read past the descriptor's end: zeros, not stored
     const uint32_t off = idx < PIECES ? t * qsb + j0 * sizeof(IO) : 0xFFFFFFF0u & (n * qsb + 16u);
     kv[i] = ld16(rk, off, 0);
-    qv[i] = ld16(rq, off, 0);
   }
+  const QRows<IO, D> qrows = load_q_rows<IO, D>(rq, (uint32_t)(16 * wave + (lane & 15)) * qsb, lane >> 4);
   float av = 1.f, bb = 0.f;
   if (wave == 0) {
     const rsrc_t ra = make_rsrc(p.a + cd.row * p.Hv + h, (uint32_t)n * p.Hv * 4);
@@ -507,9 +557,8 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
     const int idx = tid + 256 * i;
     if (idx < PIECES) {
       const int t = idx / PER_ROW, j0 = (idx % PER_ROW) * VEC;
-      const uint4 k4{kv[i][0], kv[i][1], kv[i][2], kv[i][3]}, q4{qv[i][0], qv[i][1], qv[i][2], qv[i][3]};
+      const uint4 k4{kv[i][0], kv[i][1], kv[i][2], kv[i][3]};
       store_row_terms<IO, NTI>(k4, Ks, CT * KP, KP, t, j0);
-      store_row_terms<IO, NTI>(q4, QT, CT * KP, KP, t, j0);
     }
   }
   if (wave == 0) {
@@ -530,10 +579,10 @@ __global__ __launch_bounds__(256) void factorize_kernel(FactorizeArgs<IO> p) {
 
   const int p2_wave = (blockIdx.x + blockIdx.y) & 3;
   switch (wave) {
-    case 0: factorize_wave<IO, D, 0>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
-    case 1: factorize_wave<IO, D, 1>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
-    case 2: factorize_wave<IO, D, 2>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
-    default: factorize_wave<IO, D, 3>(p, n, rec, Ks, QT, As, Ub, p2_wave); break;
+    case 0: factorize_wave<IO, D, 0>(p, n, rec, Ks, qrows, As, Ub, p2_wave); break;
+    case 1: factorize_wave<IO, D, 1>(p, n, rec, Ks, qrows, As, Ub, p2_wave); break;
+    case 2: factorize_wave<IO, D, 2>(p, n, rec, Ks, qrows, As, Ub, p2_wave); break;
+    default: factorize_wave<IO, D, 3>(p, n, rec, Ks, qrows, As, Ub, p2_wave); break;
   }
 }
 

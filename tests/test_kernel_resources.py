@@ -27,3 +27,21 @@ def test_kernels_use_no_private_segment(src, tmp_path):
     assert kernels and len(kernels) == len(sizes)
     bad = [(k, int(n)) for k, n in zip(kernels, sizes) if int(n) > 0]
     assert not bad, bad
+
+
+def test_prefill_prepass_fits_four_workgroups_per_cu(tmp_path):
+    """The pre-pass at d = 128 with bf16 inputs keeps four 4-wave workgroups resident on a
+    compute unit: at most 40 KiB of LDS (160 KiB per CU) and 128 VGPRs (512 per SIMD lane
+    over four waves)."""
+    out = str(tmp_path / "p.s")
+    cmd = ["/opt/rocm/bin/hipcc", "-x", "hip", "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only",
+           "-S", "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form", os.path.join(CSRC, "prefill_kernels.hip"), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = open(out).read()
+    name = "_ZN3gdn16factorize_kernelItLi128EEEvNS_13FactorizeArgsIT_EE"
+    lds = re.search(r"\.amdhsa_kernel " + name + r"\n(.*?)\.end_amdhsa_kernel", text, re.S).group(1)
+    group = int(re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", lds).group(1))
+    vgpr = int(re.search(r"\.set " + name + r"\.num_vgpr, (\d+)", text).group(1))
+    assert group <= 40 * 1024, group
+    assert vgpr <= 128, vgpr
