@@ -326,7 +326,7 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
     }
     const int t = 16 * W + col;
     const float gt = rowvec(As, 0, t);
-    bf16_bits tt[8][NTF];
+    f32x4 vals[2];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sp = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
@@ -334,16 +334,9 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       // the exponent g_t - g_s is <= 0 on the causal side kept by the select
       float dec = __expf(gt - rowvec(As, 0, sp));
       asm volatile("" : "+v"(dec));
-      const float val = (sp <= t && t < n && (e < 4 || two)) ? p.scale * dec * dot : 0.f;
-      split_terms<NTF>(val, tt[e]);
+      vals[e >> 2][e & 3] = (sp <= t && t < n && (e < 4 || two)) ? p.scale * dec * dot : 0.f;
     }
-#pragma unroll
-    for (int i = 0; i < NTF; ++i) {
-      bf16_bits v8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v8[e] = tt[e][i];
-      Pfr[s][i] = pack8(v8);
-    }
+    reg_operand<NTF>(vals[0], vals[1], Pfr[s]);  // terms split two elements at a time
   }
 
   // K^T fragments of state tiles jt = W, W + 4, ... (register scan only): row col of
@@ -431,27 +424,31 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
       mma_terms<NTF, NTF, ORD>(Tb[i], tii, e_op);
       // row 16 W + col of T^T (columns 16 i + 4 grp .. + 3, contiguous in the swizzled
       // order)
-      bf16_bits tt[4][NTF];
       const float bj = rowvec(As, 2, 16 * W + col);
+      {
+        bf16x8 tq[NTF];
+        reg_operand<NTF>(Tb[i], zero4(), tq);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) split_terms<NTF>(Tb[i][r], tt[r]);
-#pragma unroll
-      for (int q = 0; q < NTF; ++q)
-        *reinterpret_cast<uint2*>(Tt + q * CT * TP + xrun<2 * TP>(16 * W + col, swz(16 * i + 4 * grp))) =
-            uint2{(uint32_t)tt[0][q] | ((uint32_t)tt[1][q] << 16), (uint32_t)tt[2][q] | ((uint32_t)tt[3][q] << 16)};
+        for (int q = 0; q < NTF; ++q) {
+          const u32x4 w4 = __builtin_bit_cast(u32x4, tq[q]);
+          *reinterpret_cast<uint2*>(Tt + q * CT * TP + xrun<2 * TP>(16 * W + col, swz(16 * i + 4 * grp))) =
+              uint2{w4[0], w4[1]};
+        }
+      }
       // T''[t][j] = exp(g_n - g_t) T[t][j] b_j: this block's 16 x 16 values, transposed,
       // are half of the record's T'' fragment (i, W / 2) (lane (col, grp): row 16 i + col,
       // kappa elements 4 (W % 2) .. + 3).  A product with the unit operand moves each term
       // exactly from this C layout to the transposed one, and the lane stores it from
       // there.  Blocks i < 2 (W / 2) lie above the diagonal of every fragment.
       if (i >= 2 * (W >> 1)) {
-        bf16_bits t2[4][NTF];
+        f32x4 tv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) split_terms<NTF>((Tb[i][r] * rowvec(As, 3, 16 * i + 4 * grp + r)) * bj, t2[r]);
+        for (int r = 0; r < 4; ++r) tv[r] = (Tb[i][r] * rowvec(As, 3, 16 * i + 4 * grp + r)) * bj;
+        bf16x8 t2[NTF];
+        reg_operand<NTF>(tv, zero4(), t2);  // elements 4 .. 7 zero
 #pragma unroll
         for (int q = 0; q < NTF; ++q) {
-          const bf16_bits v8[8] = {t2[0][q], t2[1][q], t2[2][q], t2[3][q], 0, 0, 0, 0};
-          const f32x4 tr = mfma(pack8(v8), unit, zero4());
+          const f32x4 tr = mfma(t2[q], unit, zero4());
           *reinterpret_cast<uint2*>(rec + Cfg::T_OFF + (frag_combo(i, W >> 1) * NTF + q) * 1024 + lane * 16 +
                                     8 * (W & 1)) = uint2{pack_bf16x2(tr[0], tr[1]), pack_bf16x2(tr[2], tr[3])};
         }
@@ -481,19 +478,15 @@ __device__ __forceinline__ void factorize_wave(const FactorizeArgs<IO>& p, const
         mma_terms<NTF, NTF, ORD>(acc[h2], a, Pfr[sp]);
       }
     }
-    bf16_bits tt[8][NTF];
+    f32x4 vals[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float bj = rowvec(As, 2, 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3));
-      split_terms<NTF>(acc[e >> 2][e & 3] * bj, tt[e]);
-    }
+    for (int e = 0; e < 8; ++e)
+      vals[e >> 2][e & 3] = acc[e >> 2][e & 3] * rowvec(As, 2, 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3));
+    bf16x8 fr[NTF];
+    reg_operand<NTF>(vals[0], vals[1], fr);
 #pragma unroll
-    for (int q = 0; q < NTF; ++q) {
-      bf16_bits v8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v8[e] = tt[e][q];
-      *reinterpret_cast<bf16x8*>(rec + Cfg::P_OFF + (frag_combo(W, s) * NTF + q) * 1024 + lane * 16) = pack8(v8);
-    }
+    for (int q = 0; q < NTF; ++q)
+      *reinterpret_cast<bf16x8*>(rec + Cfg::P_OFF + (frag_combo(W, s) * NTF + q) * 1024 + lane * 16) = fr[q];
   }
 }
 
