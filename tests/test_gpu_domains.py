@@ -1,7 +1,9 @@
 """GPU parity on the paths and input domains the workload distributions never reach.
 
   * strided operands: the conv's packed [q | k | v] output rows read in place by the
-    prefill and by decode_mixed (qk_stride = v_stride = conv channels);
+    prefill and by decode_mixed (qk_stride = v_stride = conv channels), and packed rows
+    at head dims 16..64 in both input dtypes (the register scan and the small-head
+    pre-pass);
   * the conv's decode regime: many one-row sequences with tails in and out;
   * gates at the contract's edges (a = 2^-126, the smallest normal decay; a = 1; b
     exactly 0 or 1), keys far from unit norm (0.25 .. 4, with b |k|^2 <= 2, the range in
@@ -364,3 +366,44 @@ def test_conv_decode_matches_oracle_and_one_row_conv(g, dtype, norm):
     torch.cuda.synchronize()
     assert int(status.item()) == 1 << 8
     assert same_bits(pool, before) and same_bits(y, yb)
+
+
+@pytest.mark.parametrize("d,dtype", [(16, BF), (32, BF), (64, BF), (16, torch.float32), (64, torch.float32)])
+def test_prefill_reads_strided_rows_at_small_heads(g, d, dtype):
+    """q, k and v as column ranges of one packed row buffer whose rows are wider than the
+    heads (NaN in the unused columns), at head dims below 128 and both input dtypes, over
+    ragged varlen chunks with checkpoints: every kernel of the prefill stays inside its
+    heads' columns and follows the row stride."""
+    Hqk, Hv, block = 2, 4, 64
+    lens, starts = [150, 77], [0, 40]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    T = cu[-1]
+    say(f"strided prefill d={d} {dtype}")
+    q, k, v, a, b = gi.qkvab(T, Hqk, Hv, d, dtype, seed=241 + d)
+    qk, vw = Hqk * d, Hv * d
+    C = 2 * qk + vw + 8
+    rows = torch.full((T, C), float("nan"), dtype=dtype)
+    rows[:, :qk] = q.reshape(T, qk)
+    rows[:, qk:2 * qk] = k.reshape(T, qk)
+    rows[:, 2 * qk:2 * qk + vw] = v.reshape(T, vw)
+    rd = rows.cuda()
+    layer = g.Layer(Hqk, Hv, d, dtype, scale=0.5)
+    S1 = gi.states(1, Hv, d, seed=242)[0]
+    n_b = [oracle.count_boundaries(s, L, block) for s, L in zip(starts, lens)]
+    pool = make_pool(g, layer, sum(n_b), block)
+    ids = list(range(sum(n_b)))
+    o = nan_fill_(torch.empty(T, Hv, d, device="cuda"))
+    Sf = torch.empty(2, Hv, d, d, device="cuda")
+    g.chunk_prefill(layer, rd[:, :qk], rd[:, qk:2 * qk], rd[:, 2 * qk:], a.cuda(), b.cuda(), cu, starts,
+                    [("zero", None, Sf[0]), ("slot", S1.cuda(), Sf[1])], o, ckpt=pool, page_ids=ids,
+                    qk_stride=C, v_stride=C)
+    torch.cuda.synchronize()
+    for i, (s0, L) in enumerate(zip(starts, lens)):
+        sl = slice(cu[i], cu[i + 1])
+        o_ref, S_ref, ck_ref = oracle.recurrence(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(a[sl]), f64(b[sl]), 0.5,
+                                                 None if i == 0 else f64(S1), s0, block)
+        assert_close_per(f64(o[sl]), o_ref, TOL[dtype], 1, f"d={d} sequence {i} o")
+        assert_close_per(f64(Sf[i]), S_ref, TOL[dtype], 0, f"d={d} sequence {i} state")
+        for j in range(n_b[i]):
+            pid = sum(n_b[:i]) + j
+            assert_close_per(f64(pool.state_view(pid, layer)), ck_ref[j], TOL[dtype], 0, f"d={d} sequence {i} ckpt {j}")
